@@ -1,0 +1,282 @@
+"""MI355X-native block-quantized weight matvec: Python binding of libqgemv.so.
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name (include/qgemv.h).  Device entry points take torch tensors that
+already live on the GPU (torch is used for device memory and streams only)
+and enqueue the HIP kernel on the current torch stream (or ``stream``); the
+host pack module takes and returns numpy arrays.
+
+Importing this package loads libqgemv.so and raises ImportError if it is not
+built; nothing here computes a matvec on the CPU.
+"""
+
+import ctypes
+
+import numpy as np
+
+from . import _binding as _b
+
+_lib = _b.load()
+
+QG_FMT_FP4_E2M1 = _b.QG_FMT_FP4_E2M1
+QG_FMT_AFFINE_U4 = _b.QG_FMT_AFFINE_U4
+QG_FMT_AFFINE_U8 = _b.QG_FMT_AFFINE_U8
+QG_FMT_FP8_E4M3 = _b.QG_FMT_FP8_E4M3
+qg_plan = _b.qg_plan
+
+__all__ = [
+    "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3",
+    "qg_plan", "qg_plan_query", "qg_status_string", "qg_abi_version", "qg_max_k",
+    "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
+    "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
+    "qg_bytes_fp4", "qg_bytes_affine", "qg_bytes_fp8", "lib",
+]
+
+
+def lib():
+    """The loaded ctypes library (for callers that marshal pointers themselves)."""
+    return _lib
+
+
+class QgError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = int(status)
+        self.name = _b.STATUS_NAMES.get(self.status, "unknown")
+        super().__init__("%s: %s (%s)" % (where, _lib.qg_status_string(self.status).decode(), self.name))
+
+
+def _check(status, where):
+    if status != _b.QG_OK:
+        raise QgError(status, where)
+
+
+def qg_status_string(status):
+    return _lib.qg_status_string(int(status)).decode()
+
+
+def qg_abi_version():
+    return int(_lib.qg_abi_version())
+
+
+def qg_max_k(fmt, batch):
+    return int(_lib.qg_max_k(int(fmt), int(batch)))
+
+
+# ------------------------------------------------------------------ device entry points
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtypes, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.dim() not in ndim:
+        raise ValueError("%s must have %s dimensions, has %d" % (name, ndim, t.dim()))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _x_y(x, y, n):
+    torch = _torch()
+    xp = _dev_ptr(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (1, 2))
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    k = x.shape[-1]
+    yp = _dev_ptr(y, "y", (torch.float32, torch.bfloat16), (1, 2))
+    if y.numel() != batch * n or (y.dim() == 2 and tuple(y.shape) != (batch, n)):
+        raise ValueError("y must be [batch=%d, n=%d], got %s" % (batch, n, tuple(y.shape)))
+    out = _b.QG_OUT_F32 if y.dtype == torch.float32 else _b.QG_OUT_BF16
+    if x.device != y.device:
+        raise ValueError("x and y are on different devices")
+    return xp, yp, batch, k, out
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _plan_ptr(plan):
+    if plan is None:
+        return None
+    if isinstance(plan, dict):
+        plan = qg_plan(**plan)
+    return ctypes.byref(plan)
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts}
+    if len(devs) != 1:
+        raise ValueError("all tensors must be on one device, got %s" % devs)
+
+
+def qgemv_fp4_e2m1(codes, scales, x, y, group_size, plan=None, stream=None):
+    """y[b, n] = sum_k scale[n, k//gs] * E2M1(code[n, k]) * x[b, k].
+
+    codes uint8 [n, k/2] (even column in the low nibble), scales bf16 [n, k/gs],
+    x bf16 [batch, k] (or [k]), y float32 or bf16 [batch, n].
+    """
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.uint8,), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 2 != k or tuple(scales.shape) != (n, k // group_size):
+        raise ValueError("shapes: codes %s, scales %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), k, group_size))
+    _same_device(codes, scales, x, y)
+    st = _lib.qgemv_fp4_e2m1_plan(cp, sp, xp, yp, n, k, int(group_size), batch, out,
+                                  _plan_ptr(plan), _stream(stream, y.device))
+    _check(st, "qgemv_fp4_e2m1")
+    return y
+
+
+def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream):
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] * (32 // bits) != k or tuple(scales.shape) != (n, k // group_size) \
+            or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("shapes: codes %s, scales %s, biases %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), k, group_size))
+    _same_device(codes, scales, biases, x, y)
+    fn = getattr(_lib, name + "_plan")
+    st = fn(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out, _plan_ptr(plan), _stream(stream, y.device))
+    _check(st, name)
+    return y
+
+
+def qgemv_affine_u4(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):
+    """y[b, n] = sum_k (scale[n,g] * q[n,k] + bias[n,g]) * x[b,k], 4-bit u32 low-first codes [n, k/8]."""
+    return _affine("qgemv_affine_u4", 4, codes, scales, biases, x, y, group_size, plan, stream)
+
+
+def qgemv_affine_u8(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):
+    """As qgemv_affine_u4 with 8-bit codes, u32 low-first [n, k/4]."""
+    return _affine("qgemv_affine_u8", 8, codes, scales, biases, x, y, group_size, plan, stream)
+
+
+def qgemv_fp8_e4m3(codes, row_scale, x, y, plan=None, stream=None):
+    """y[b, n] = row_scale[n] * sum_k E4M3(code[n, k]) * x[b, k]; codes uint8 [n, k], row_scale f32 [n]."""
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.uint8,), (2,))
+    rp = _dev_ptr(row_scale, "row_scale", (torch.float32,), (1,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] != k or row_scale.shape[0] != n:
+        raise ValueError("shapes: codes %s, row_scale %s, k=%d" % (tuple(codes.shape), tuple(row_scale.shape), k))
+    _same_device(codes, row_scale, x, y)
+    st = _lib.qgemv_fp8_e4m3_plan(cp, rp, xp, yp, n, k, batch, out, _plan_ptr(plan), _stream(stream, y.device))
+    _check(st, "qgemv_fp8_e4m3")
+    return y
+
+
+def qg_plan_query(fmt, n, k, batch=1):
+    """The launch shape the plain entry point would use on the current device."""
+    p = qg_plan()
+    _check(_lib.qg_plan_query(int(fmt), int(n), int(k), int(batch), ctypes.byref(p)), "qg_plan_query")
+    return {"rows_per_tile": p.rows_per_tile, "waves_per_block": p.waves_per_block, "blocks": p.blocks}
+
+
+# ------------------------------------------------------------------ host pack module
+
+def _host_in(a, dtype, name):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, np.dtype(dtype), a.dtype))
+    return a
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def qg_quantize_fp4_e2m1(w, group_size=32):
+    """float32 [n, k] -> (codes uint8 [n, k/2], scales bf16 bits uint16 [n, k/gs])."""
+    w = _host_in(w, np.float32, "w")
+    n, k = w.shape
+    codes = np.empty((n, k // 2), np.uint8)
+    scales = np.empty((n, max(k // int(group_size), 1)), np.uint16)
+    _check(_lib.qg_quantize_fp4_e2m1(_ptr(w), n, k, int(group_size), _ptr(codes), _ptr(scales)),
+           "qg_quantize_fp4_e2m1")
+    return codes, scales
+
+
+def qg_quantize_affine(w, bits, group_size=64):
+    """float32 [n, k] -> (codes uint32 [n, k*bits/32], scales, biases bf16 bits [n, k/gs])."""
+    w = _host_in(w, np.float32, "w")
+    n, k = w.shape
+    per = 32 // int(bits) if bits in (4, 8) else 1
+    codes = np.empty((n, max(k // per, 1)), np.uint32)
+    scales = np.empty((n, max(k // int(group_size), 1)), np.uint16)
+    biases = np.empty_like(scales)
+    _check(_lib.qg_quantize_affine(_ptr(w), n, k, int(bits), int(group_size), _ptr(codes),
+                                   _ptr(scales), _ptr(biases)), "qg_quantize_affine")
+    return codes, scales, biases
+
+
+def qg_quantize_fp8_e4m3_rowwise(w):
+    """float32 [n, k] -> (codes uint8 [n, k], row_scale float32 [n])."""
+    w = _host_in(w, np.float32, "w")
+    n, k = w.shape
+    codes = np.empty((n, k), np.uint8)
+    rs = np.empty(n, np.float32)
+    _check(_lib.qg_quantize_fp8_e4m3_rowwise(_ptr(w), n, k, _ptr(codes), _ptr(rs)),
+           "qg_quantize_fp8_e4m3_rowwise")
+    return codes, rs
+
+
+def qg_pack_nibbles(codes):
+    c = _host_in(codes, np.uint8, "codes").ravel()
+    out = np.empty(c.size // 2, np.uint8)
+    _check(_lib.qg_pack_nibbles(_ptr(c), c.size, _ptr(out)), "qg_pack_nibbles")
+    return out
+
+
+def qg_unpack_nibbles(packed, count):
+    p = _host_in(packed, np.uint8, "packed").ravel()
+    if p.size * 2 < count:
+        raise ValueError("packed holds %d codes, asked for %d" % (p.size * 2, count))
+    out = np.empty(int(count), np.uint8)
+    _check(_lib.qg_unpack_nibbles(_ptr(p), int(count), _ptr(out)), "qg_unpack_nibbles")
+    return out
+
+
+def qg_pack_u32(codes, bits):
+    c = _host_in(codes, np.uint8, "codes").ravel()
+    out = np.empty(max(c.size * int(bits) // 32, 1), np.uint32)
+    _check(_lib.qg_pack_u32(_ptr(c), c.size, int(bits), _ptr(out)), "qg_pack_u32")
+    return out
+
+
+def qg_unpack_u32(packed, count, bits):
+    p = _host_in(packed, np.uint32, "packed").ravel()
+    if bits in (4, 8) and p.size * (32 // bits) < count:
+        raise ValueError("packed holds %d codes, asked for %d" % (p.size * (32 // bits), count))
+    out = np.empty(int(count), np.uint8)
+    _check(_lib.qg_unpack_u32(_ptr(p), int(count), int(bits), _ptr(out)), "qg_unpack_u32")
+    return out
+
+
+def qg_bytes_fp4(n, k, group_size=32):
+    return int(_lib.qg_bytes_fp4(int(n), int(k), int(group_size)))
+
+
+def qg_bytes_affine(n, k, bits, group_size=64):
+    return int(_lib.qg_bytes_affine(int(n), int(k), int(bits), int(group_size)))
+
+
+def qg_bytes_fp8(n, k):
+    return int(_lib.qg_bytes_fp8(int(n), int(k)))

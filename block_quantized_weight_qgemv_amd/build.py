@@ -1,0 +1,59 @@
+"""Build libqgemv.so in-tree: the HIP kernels + C ABI (hipcc, gfx950) and the
+host pack module (g++, no floating-point contraction).
+
+    python -m block_quantized_weight_qgemv_amd.build
+"""
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libqgemv.so")
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.path.join(ROCM, "bin", "hipcc")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+    # no packed fp32 instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I" + INCLUDE, "-I" + CSRC,
+]
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
+              "-I" + INCLUDE, "-I" + os.path.join(ROCM, "include"), "-D__HIP_PLATFORM_AMD__"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        sys.stderr.write(out + "\n")
+        raise RuntimeError("build step failed: %s" % " ".join(cmd))
+    return out
+
+
+def build(verbose=False):
+    """Compile every source and link libqgemv.so next to this file."""
+    with tempfile.TemporaryDirectory(prefix="qgemv_build_") as tmp:
+        api_o = os.path.join(tmp, "qgemv_api.o")
+        pack_o = os.path.join(tmp, "pack.o")
+        out = _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, "qgemv_api.hip"), "-o", api_o])
+        out += _run(["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "pack.cpp"), "-o", pack_o])
+        tmp_lib = os.path.join(tmp, "libqgemv.so")
+        out += _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", api_o, pack_o,
+                     "-o", tmp_lib, "-lpthread"])
+        shutil.move(tmp_lib, LIB)
+    if verbose and out.strip():
+        print(out)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,340 @@
+// C ABI of the block-quantized weight matvec: argument validation, launch
+// planning and dispatch to the kernel template in qgemv_device.hpp.
+//
+// Validation runs completely before any HIP call, so a bad argument never
+// launches anything and never touches y.  The only state kept across calls is
+// a per-device cache of the compute-unit count and of which kernel instances
+// have had their LDS limit raised; both are filled once, thread-safely.
+
+#include "qgemv.h"
+#include "qgemv_device.hpp"
+
+#include <atomic>
+#include <mutex>
+
+namespace {
+
+using qg::Params;
+
+// Largest dynamic LDS a workgroup may use for the staged activations.  MI355X
+// has 160 KiB of LDS per compute unit; 128 KiB leaves room for a second,
+// smaller workgroup.
+constexpr int64_t kMaxLds = 128 * 1024;
+constexpr int kMaxDevices = 64;
+
+struct FmtInfo {
+    int wpc;        // weights per 16-byte chunk
+    int pieces;     // 16-byte LDS pieces per chunk and batch row
+    bool sums;      // per-chunk activation sums staged
+};
+
+FmtInfo fmt_info(qg_format f) {
+    switch (f) {
+        case QG_FMT_FP4_E2M1: return {qg::FmtFP4::kWpc, qg::FmtFP4::kPieces, qg::FmtFP4::kSums};
+        case QG_FMT_AFFINE_U4: return {qg::FmtAffineU4::kWpc, qg::FmtAffineU4::kPieces, qg::FmtAffineU4::kSums};
+        case QG_FMT_AFFINE_U8: return {qg::FmtAffineU8::kWpc, qg::FmtAffineU8::kPieces, qg::FmtAffineU8::kSums};
+        default: return {qg::FmtFP8::kWpc, qg::FmtFP8::kPieces, qg::FmtFP8::kSums};
+    }
+}
+
+int64_t lds_bytes(qg_format f, int64_t k, int32_t batch) {
+    const FmtInfo fi = fmt_info(f);
+    const int64_t chunks = k / fi.wpc;
+    return int64_t(batch) * fi.pieces * chunks * 16 + (fi.sums ? int64_t(batch) * chunks * 4 : 0);
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qg_status check_common(qg_format f, const void *codes, const void *x, const void *y, int64_t n,
+                       int64_t k, int32_t batch, qg_out_dtype out) {
+    if (!codes || !x || !y) return QG_ERR_NULL_POINTER;
+    if (n < 1 || k < 1) return QG_ERR_BAD_SHAPE;
+    const FmtInfo fi = fmt_info(f);
+    if (k % fi.wpc) return QG_ERR_BAD_SHAPE;
+    if (n > (int64_t(1) << 31) || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    if (out != QG_OUT_F32 && out != QG_OUT_BF16) return QG_ERR_BAD_DTYPE;
+    if (!aligned(codes, 16) || !aligned(x, 16)) return QG_ERR_MISALIGNED;
+    if (!aligned(y, out == QG_OUT_F32 ? 4 : 2)) return QG_ERR_MISALIGNED;
+    if (lds_bytes(f, k, batch) > kMaxLds) return QG_ERR_TOO_LARGE;
+    return QG_OK;
+}
+
+qg_status check_groups(const void *scales, const void *biases, bool need_bias, int64_t k,
+                       int32_t group_size, int wpc) {
+    if (!scales || (need_bias && !biases)) return QG_ERR_NULL_POINTER;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return QG_ERR_BAD_GROUP_SIZE;
+    if (group_size < wpc || k % group_size) return QG_ERR_BAD_GROUP_SIZE;
+    if (!aligned(scales, 2) || (need_bias && !aligned(biases, 2))) return QG_ERR_MISALIGNED;
+    return QG_OK;
+}
+
+int log2i(int v) {
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+
+// ---------------------------------------------------------------- device info
+
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+qg_status device_cus(int *cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_ERR_DEVICE;
+    std::call_once(g_cu_once[dev], [dev] {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+        g_cu_count[dev] = v;
+    });
+    if (g_cu_count[dev] <= 0) return QG_ERR_DEVICE;
+    *cus = g_cu_count[dev];
+    return QG_OK;
+}
+
+// ---------------------------------------------------------------- planning
+
+struct Plan {
+    int rows_per_tile;
+    int waves_per_block;
+    int blocks;
+};
+
+Plan default_plan(qg_format f, int64_t n, int64_t k, int32_t batch, int cus) {
+    const FmtInfo fi = fmt_info(f);
+    const int64_t chunks = k / fi.wpc;
+    const int64_t passes = (chunks + qg::kWave - 1) / qg::kWave;
+    Plan pl;
+    pl.rows_per_tile = passes >= 4 ? 1 : (passes >= 2 ? 2 : 4);
+    (void)batch;
+    pl.waves_per_block = 4;
+    const int64_t waves_per_cu = 16;
+    int64_t blocks = int64_t(cus) * waves_per_cu / pl.waves_per_block;
+    const int64_t max_blocks = (n + pl.waves_per_block - 1) / pl.waves_per_block;
+    if (blocks > max_blocks) blocks = max_blocks;
+    pl.blocks = int(blocks < 1 ? 1 : blocks);
+    return pl;
+}
+
+// ---------------------------------------------------------------- dispatch
+
+template <class Fmt, int R, int B>
+qg_status launch_inst(const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
+    constexpr int D = R == 1 ? 8 : (R == 2 ? 4 : 2);
+    auto kern = qg::qgemv_kernel<Fmt, R, B, D>;
+    static std::once_flag attr_once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(attr_once, [&] {
+        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+    });
+    if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
+    hipLaunchKernelGGL(kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+template <class Fmt, int R>
+qg_status launch_r(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
+    switch (batch) {
+        case 1: return launch_inst<Fmt, R, 1>(p, pl, lds, s);
+        case 2: return launch_inst<Fmt, R, 2>(p, pl, lds, s);
+        case 3: return launch_inst<Fmt, R, 3>(p, pl, lds, s);
+        default: return launch_inst<Fmt, R, 4>(p, pl, lds, s);
+    }
+}
+
+template <class Fmt>
+qg_status launch_fmt(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
+    switch (pl.rows_per_tile) {
+        case 1: return launch_r<Fmt, 1>(p, pl, batch, lds, s);
+        case 2: return launch_r<Fmt, 2>(p, pl, batch, lds, s);
+        default: return launch_r<Fmt, 4>(p, pl, batch, lds, s);
+    }
+}
+
+qg_status check_plan(const qg_plan *plan) {
+    if (!plan) return QG_OK;
+    const int r = plan->rows_per_tile, w = plan->waves_per_block;
+    if (r != 0 && r != 1 && r != 2 && r != 4) return QG_ERR_BAD_SHAPE;
+    if (w < 0 || w > 8) return QG_ERR_BAD_SHAPE;
+    if (plan->blocks < 0) return QG_ERR_BAD_SHAPE;
+    return QG_OK;
+}
+
+qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream) {
+    int cus = 0;
+    qg_status st = device_cus(&cus);
+    if (st != QG_OK) return st;
+    Plan pl = default_plan(f, p.n, p.k, batch, cus);
+    if (override_plan) {
+        if (override_plan->rows_per_tile) pl.rows_per_tile = override_plan->rows_per_tile;
+        if (override_plan->waves_per_block) pl.waves_per_block = override_plan->waves_per_block;
+        if (override_plan->blocks) pl.blocks = override_plan->blocks;
+        else {
+            const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
+            int64_t b = int64_t(cus) * 16 / pl.waves_per_block;
+            pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
+        }
+    }
+    p.total_waves = pl.blocks * pl.waves_per_block;
+    const int64_t lds = lds_bytes(f, p.k, batch);
+    switch (f) {
+        case QG_FMT_FP4_E2M1: return launch_fmt<qg::FmtFP4>(p, pl, batch, lds, stream);
+        case QG_FMT_AFFINE_U4: return launch_fmt<qg::FmtAffineU4>(p, pl, batch, lds, stream);
+        case QG_FMT_AFFINE_U8: return launch_fmt<qg::FmtAffineU8>(p, pl, batch, lds, stream);
+        default: return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, stream);
+    }
+}
+
+Params base_params(qg_format f, const void *codes, const void *x, void *y, int64_t n, int64_t k,
+                   qg_out_dtype out) {
+    const FmtInfo fi = fmt_info(f);
+    Params p{};
+    p.codes = static_cast<const unsigned char *>(codes);
+    p.x = static_cast<const uint16_t *>(x);
+    p.y = y;
+    p.n = n;
+    p.k = int32_t(k);
+    p.chunks = int32_t(k / fi.wpc);
+    p.row_bytes = int64_t(p.chunks) * qg::kChunkBytes;
+    p.passes = (p.chunks + qg::kWave - 1) / qg::kWave;
+    p.out_bf16 = out == QG_OUT_BF16 ? 1 : 0;
+    return p;
+}
+
+qg_status affine_entry(qg_format f, const uint32_t *codes, const uint16_t *scales,
+                       const uint16_t *biases, const uint16_t *x, void *y, int64_t n, int64_t k,
+                       int32_t group_size, int32_t batch, qg_out_dtype out, const qg_plan *plan,
+                       hipStream_t stream) {
+    qg_status st = check_common(f, codes, x, y, n, k, batch, out);
+    if (st != QG_OK) return st;
+    st = check_groups(scales, biases, true, k, group_size, fmt_info(f).wpc);
+    if (st != QG_OK) return st;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(f, codes, x, y, n, k, out);
+    p.scales = scales;
+    p.biases = biases;
+    p.groups = int32_t(k / group_size);
+    p.group_shift = log2i(group_size / fmt_info(f).wpc);
+    return run(f, p, batch, plan, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status qgemv_fp4_e2m1_plan(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                              void *y, int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                              qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream) {
+    qg_status st = check_common(QG_FMT_FP4_E2M1, codes, x, y, n, k, batch, out_dtype);
+    if (st != QG_OK) return st;
+    st = check_groups(scales, nullptr, false, k, group_size, qg::FmtFP4::kWpc);
+    if (st != QG_OK) return st;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(QG_FMT_FP4_E2M1, codes, x, y, n, k, out_dtype);
+    p.scales = scales;
+    p.groups = int32_t(k / group_size);
+    p.group_shift = log2i(group_size / qg::FmtFP4::kWpc);
+    return run(QG_FMT_FP4_E2M1, p, batch, plan, stream);
+}
+
+qg_status qgemv_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y,
+                         int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                         qg_out_dtype out_dtype, hipStream_t stream) {
+    return qgemv_fp4_e2m1_plan(codes, scales, x, y, n, k, group_size, batch, out_dtype, nullptr, stream);
+}
+
+qg_status qgemv_affine_u4_plan(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                               const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                               int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
+                               hipStream_t stream) {
+    return affine_entry(QG_FMT_AFFINE_U4, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, plan, stream);
+}
+
+qg_status qgemv_affine_u4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                          const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                          int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    return affine_entry(QG_FMT_AFFINE_U4, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, nullptr, stream);
+}
+
+qg_status qgemv_affine_u8_plan(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                               const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                               int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
+                               hipStream_t stream) {
+    return affine_entry(QG_FMT_AFFINE_U8, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, plan, stream);
+}
+
+qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                          const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                          int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    return affine_entry(QG_FMT_AFFINE_U8, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, nullptr, stream);
+}
+
+qg_status qgemv_fp8_e4m3_plan(const uint8_t *codes, const float *row_scale, const uint16_t *x,
+                              void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
+                              const qg_plan *plan, hipStream_t stream) {
+    qg_status st = check_common(QG_FMT_FP8_E4M3, codes, x, y, n, k, batch, out_dtype);
+    if (st != QG_OK) return st;
+    if (!row_scale) return QG_ERR_NULL_POINTER;
+    if (!aligned(row_scale, 4)) return QG_ERR_MISALIGNED;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(QG_FMT_FP8_E4M3, codes, x, y, n, k, out_dtype);
+    p.row_scale = row_scale;
+    return run(QG_FMT_FP8_E4M3, p, batch, plan, stream);
+}
+
+qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale, const uint16_t *x, void *y,
+                         int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
+                         hipStream_t stream) {
+    return qgemv_fp8_e4m3_plan(codes, row_scale, x, y, n, k, batch, out_dtype, nullptr, stream);
+}
+
+qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out) {
+    if (!out) return QG_ERR_NULL_POINTER;
+    if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_FP8_E4M3) return QG_ERR_BAD_DTYPE;
+    if (n < 1 || k < 1 || k % fmt_info(format).wpc) return QG_ERR_BAD_SHAPE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    int cus = 0;
+    qg_status st = device_cus(&cus);
+    if (st != QG_OK) return st;
+    Plan pl = default_plan(format, n, k, batch, cus);
+    out->rows_per_tile = pl.rows_per_tile;
+    out->waves_per_block = pl.waves_per_block;
+    out->blocks = pl.blocks;
+    return QG_OK;
+}
+
+const char *qg_status_string(qg_status status) {
+    switch (status) {
+        case QG_OK: return "ok";
+        case QG_ERR_NULL_POINTER: return "a required pointer is null";
+        case QG_ERR_BAD_SHAPE: return "bad shape (n, k, or k not a whole number of 16-byte code chunks)";
+        case QG_ERR_BAD_GROUP_SIZE: return "group_size must be 32, 64 or 128 and divide k";
+        case QG_ERR_MISALIGNED: return "a pointer is not aligned (codes and x: 16 bytes)";
+        case QG_ERR_BAD_BATCH: return "batch must be 1..4";
+        case QG_ERR_BAD_DTYPE: return "unknown output dtype or format";
+        case QG_ERR_BAD_BITS: return "bits must be 4 or 8";
+        case QG_ERR_BAD_VALUE: return "non-finite weight or out-of-range code";
+        case QG_ERR_TOO_LARGE: return "k * batch exceeds the activation staging limit (qg_max_k)";
+        case QG_ERR_DEVICE: return "no usable HIP device";
+        case QG_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int qg_abi_version(void) { return QG_ABI_VERSION; }
+
+int64_t qg_max_k(qg_format format, int32_t batch) {
+    if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_FP8_E4M3) return 0;
+    if (batch < 1 || batch > 4) return 0;
+    const FmtInfo fi = fmt_info(format);
+    const int64_t per_chunk = int64_t(batch) * (fi.pieces * 16 + (fi.sums ? 4 : 0));
+    return (kMaxLds / per_chunk) * fi.wpc;
+}
+
+}  // extern "C"

@@ -1,0 +1,261 @@
+/*
+ * qgemv.h — C ABI of the MI355X block-quantized weight matvec library (libqgemv.so).
+ *
+ * The operation is the decode-step weight matvec
+ *
+ *     y[b, n] = sum_k  W^[n, k] * x[b, k]        b < batch, n < N, k < K
+ *
+ * where W is stored as packed low-bit codes plus per-group (or per-row) scales
+ * and x is a bf16 activation vector or a small batch of them.  This is the
+ * weight stream the "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus
+ * (Part 2)" post identifies as the dominant bucket of a decode token (section
+ * "The starting point", decomposition table: FP4 weight matvecs and the FP8
+ * lm_head), and the "qmm GEMV" of the mlxcel issue "decode is bound by 8-bit
+ * MLP weight bytes" (#683, "Summary").
+ *
+ * Conventions shared by every device entry point
+ *  - Pointers marked DEVICE are device (HBM) pointers; HOST pointers are
+ *    ordinary host memory.  Every matrix is dense row-major with K contiguous.
+ *  - The caller allocates and owns every buffer.  The library never allocates,
+ *    frees or synchronizes; work is enqueued on `stream` and runs
+ *    asynchronously.  `stream` may be 0 (the null stream).
+ *  - Arguments are validated completely before any HIP call.  On an error
+ *    nothing is launched and y is not touched.  Launch failures reported by
+ *    hipGetLastError map to QG_ERR_LAUNCH.  No C++ exception crosses the ABI.
+ *  - Preconditions (else the listed error):
+ *      n >= 1, k >= 1                                  QG_ERR_BAD_SHAPE
+ *      k % group_size == 0, group_size in {32,64,128}  QG_ERR_BAD_GROUP_SIZE
+ *      a code row is a whole number of 16-byte chunks:
+ *        FP4 and u4: k % 32 == 0; u8 and FP8: k % 16 == 0   QG_ERR_BAD_SHAPE
+ *      codes and x 16-byte aligned; scales/biases 2-byte;
+ *        row_scale 4-byte; y 4-byte (f32) or 2-byte (bf16) QG_ERR_MISALIGNED
+ *      1 <= batch <= 4                                 QG_ERR_BAD_BATCH
+ *      out_dtype is QG_OUT_F32 or QG_OUT_BF16          QG_ERR_BAD_DTYPE
+ *      the activation block (k * batch values, staged in LDS) fits the
+ *        staging limit qg_max_k(format, batch)         QG_ERR_TOO_LARGE
+ *      non-null pointers                               QG_ERR_NULL_POINTER
+ *  - Results: fp32 accumulation.  Within 1e-3 relative error of the exact
+ *    product per element (elements whose exact value nearly cancels are judged
+ *    against 2^-12 * sum|w x|).  Run-to-run deterministic (no atomics), and a
+ *    batch row gives the same bits as a batch-1 call with that row.
+ *  - bf16 output is the fp32 result rounded to nearest even.
+ *  - Concurrent calls on different streams are safe; calls that write the
+ *    same y race like any two kernels would.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum qg_status {
+    QG_OK = 0,
+    QG_ERR_NULL_POINTER = 1,
+    QG_ERR_BAD_SHAPE = 2,
+    QG_ERR_BAD_GROUP_SIZE = 3,
+    QG_ERR_MISALIGNED = 4,
+    QG_ERR_BAD_BATCH = 5,
+    QG_ERR_BAD_DTYPE = 6,
+    QG_ERR_BAD_BITS = 7,
+    QG_ERR_BAD_VALUE = 8,     /* a quantizer was given a non-finite weight   */
+    QG_ERR_TOO_LARGE = 9,     /* k * batch beyond the activation staging limit */
+    QG_ERR_DEVICE = 10,       /* no usable HIP device / attribute query failed */
+    QG_ERR_LAUNCH = 11        /* the kernel launch itself failed              */
+} qg_status;
+
+typedef enum qg_out_dtype { QG_OUT_F32 = 0, QG_OUT_BF16 = 1 } qg_out_dtype;
+
+/* Weight formats, used by the query functions. */
+typedef enum qg_format {
+    QG_FMT_FP4_E2M1 = 0,
+    QG_FMT_AFFINE_U4 = 1,
+    QG_FMT_AFFINE_U8 = 2,
+    QG_FMT_FP8_E4M3 = 3
+} qg_format;
+
+/* ------------------------------------------------------------------------
+ * Device entry points
+ * ---------------------------------------------------------------------- */
+
+/*
+ * FP4-E2M1 weights with one bf16 scale per group of `group_size` columns.
+ * Part 2 post, "The assumption that failed the profiler": E2M1 codes (sign in
+ * code bit 3, every magnitude exact in BF16), a per-group scale folded out of
+ * the per-weight math as one multiply-add per group.
+ *
+ *   codes   DEVICE uint8 [n, k/2]: two codes per byte, the code of the even
+ *           column in the low nibble.
+ *   scales  DEVICE bf16 bits [n, k/group_size].
+ *   x       DEVICE bf16 bits [batch, k].
+ *   y       DEVICE [batch, n] float (QG_OUT_F32) or bf16 bits (QG_OUT_BF16).
+ *   W^[n,k] = scale[n, k/group_size] * E2M1(code[n,k]).
+ */
+qg_status qgemv_fp4_e2m1(const uint8_t *codes, const uint16_t *scales,
+                         const uint16_t *x, void *y,
+                         int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                         qg_out_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Min-max affine 4-bit codes, one bf16 scale and one bf16 bias per group.
+ * mlxcel issue #683, "Step 2 result": group-64 affine codes packed into u32
+ * low-first, scales and biases rounded to bf16.
+ *
+ *   codes   DEVICE uint32 [n, k/8]: code j of a word in bits [4j, 4j+4).
+ *   scales, biases  DEVICE bf16 bits [n, k/group_size].
+ *   x, y    as for qgemv_fp4_e2m1.
+ *   W^[n,k] = scale[n,g] * q[n,k] + bias[n,g],  g = k/group_size, computed as
+ *   sum_g scale*sum(q*x) + bias*sum(x) (the bias folded via activation sums).
+ */
+qg_status qgemv_affine_u4(const uint32_t *codes, const uint16_t *scales,
+                          const uint16_t *biases, const uint16_t *x, void *y,
+                          int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                          qg_out_dtype out_dtype, hipStream_t stream);
+
+/*
+ * Min-max affine 8-bit codes (same source and bias fold as qgemv_affine_u4).
+ *   codes   DEVICE uint32 [n, k/4]: code j of a word in bits [8j, 8j+8).
+ */
+qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales,
+                          const uint16_t *biases, const uint16_t *x, void *y,
+                          int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                          qg_out_dtype out_dtype, hipStream_t stream);
+
+/*
+ * FP8-E4M3 (OCP "FN": max 448, S.1111.111 = NaN) weights with one fp32 scale
+ * per row.  Part 2 post, "The assumption that failed the profiler": the FP8
+ * lm_head matvec does one multiply-add per weight byte with no separate
+ * dequantization pass; the row scale is applied once to the row's sum.
+ *
+ *   codes      DEVICE uint8 [n, k].
+ *   row_scale  DEVICE float [n].
+ *   W^[n,k] = row_scale[n] * E4M3(code[n,k]); a NaN code gives a NaN row.
+ */
+qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale,
+                         const uint16_t *x, void *y,
+                         int64_t n, int64_t k, int32_t batch,
+                         qg_out_dtype out_dtype, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Explicit launch shape.  The plain entry points pick a launch shape from the
+ * matrix shape and the device's compute-unit count.  The *_plan variants take
+ * the same arguments plus a qg_plan whose non-zero fields override that
+ * choice (for tuning a deployment's own shapes); plan == NULL is the plain
+ * call.  Results do not depend on the plan except for the summation order of
+ * rows that nearly cancel (every plan meets the same accuracy bound).
+ * ---------------------------------------------------------------------- */
+
+typedef struct qg_plan {
+    int32_t rows_per_tile;    /* rows one wavefront streams together: 1, 2 or 4 */
+    int32_t waves_per_block;  /* wavefronts per workgroup: 1..8                 */
+    int32_t blocks;           /* workgroups in the grid (persistent)            */
+} qg_plan;
+
+/* A plan field outside its range returns QG_ERR_BAD_SHAPE. */
+qg_status qgemv_fp4_e2m1_plan(const uint8_t *codes, const uint16_t *scales,
+                              const uint16_t *x, void *y,
+                              int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                              qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_affine_u4_plan(const uint32_t *codes, const uint16_t *scales,
+                               const uint16_t *biases, const uint16_t *x, void *y,
+                               int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                               qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_affine_u8_plan(const uint32_t *codes, const uint16_t *scales,
+                               const uint16_t *biases, const uint16_t *x, void *y,
+                               int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                               qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_fp8_e4m3_plan(const uint8_t *codes, const float *row_scale,
+                              const uint16_t *x, void *y,
+                              int64_t n, int64_t k, int32_t batch,
+                              qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+
+/* The launch shape the plain entry point would use on the current device
+ * (needs a HIP device for its compute-unit count, else QG_ERR_DEVICE). */
+qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out);
+
+/* ------------------------------------------------------------------------
+ * Queries (host only, no device needed)
+ * ---------------------------------------------------------------------- */
+
+/* Static English description of a status; never NULL. */
+const char *qg_status_string(qg_status status);
+
+/* QG_ABI_VERSION of the loaded library. */
+int qg_abi_version(void);
+
+/* Largest k a device entry point accepts for this format and batch (the
+ * activation block is staged in LDS once per workgroup); 0 for a bad format
+ * or batch. */
+int64_t qg_max_k(qg_format format, int32_t batch);
+
+/* ------------------------------------------------------------------------
+ * Host pack/layout module.  HOST pointers; the caller allocates every output.
+ * These produce the packed layouts the device entry points read.  The
+ * arithmetic is float64 with one rounding per operation (see the quantizer
+ * definitions below); the functions are deterministic and thread-safe.
+ * Every function returns QG_ERR_NULL_POINTER / QG_ERR_BAD_SHAPE /
+ * QG_ERR_BAD_GROUP_SIZE / QG_ERR_BAD_BITS / QG_ERR_BAD_VALUE as applicable and
+ * writes nothing on error.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * FP4-E2M1 group-absmax quantizer.  Per group: s = bf16_rne(absmax / 6);
+ * code = nearest E2M1 value to w / s, ties to the even mantissa bit,
+ * saturating at 6; sign bit set iff w < 0; s == 0 gives code 0.
+ *   w       HOST float [n, k] (finite)
+ *   codes   HOST uint8 [n, k/2] (low nibble = even column)
+ *   scales  HOST bf16 bits [n, k/group_size]
+ */
+qg_status qg_quantize_fp4_e2m1(const float *w, int64_t n, int64_t k, int32_t group_size,
+                               uint8_t *codes, uint16_t *scales);
+
+/*
+ * Min-max affine quantizer (#683 "Step 2 result": scale and bias rounded to
+ * bf16 before q is computed).  Per group: s = bf16_rne((max - min) / (2^bits-1)),
+ * b = bf16_rne(min), q = clamp(rint((w - b) / s), 0, 2^bits - 1) with rint
+ * rounding half to even; s == 0 gives q = 0.
+ *   codes   HOST uint32 [n, k*bits/32], u32 low-first
+ *   scales, biases  HOST bf16 bits [n, k/group_size]
+ */
+qg_status qg_quantize_affine(const float *w, int64_t n, int64_t k, int32_t bits,
+                             int32_t group_size, uint32_t *codes, uint16_t *scales,
+                             uint16_t *biases);
+
+/*
+ * FP8-E4M3 row-absmax quantizer.  s_n = absmax_n / 448 (one binary32
+ * division); code = nearest finite E4M3 to w / s_n (float64 quotient), ties to
+ * even, saturating at 448; sign bit set iff w < 0; s_n == 0 gives code 0.
+ *   codes      HOST uint8 [n, k];  row_scale  HOST float [n]
+ */
+qg_status qg_quantize_fp8_e4m3_rowwise(const float *w, int64_t n, int64_t k,
+                                       uint8_t *codes, float *row_scale);
+
+/* One code per byte (values < 16) <-> two per byte, even index in the low nibble.
+ * count must be even. */
+qg_status qg_pack_nibbles(const uint8_t *one_code_per_byte, int64_t count, uint8_t *packed);
+qg_status qg_unpack_nibbles(const uint8_t *packed, int64_t count, uint8_t *one_code_per_byte);
+
+/* One code per byte (values < 2^bits) <-> u32 low-first words; bits 4 or 8;
+ * count a multiple of 32/bits. */
+qg_status qg_pack_u32(const uint8_t *one_code_per_byte, int64_t count, int32_t bits,
+                      uint32_t *packed);
+qg_status qg_unpack_u32(const uint32_t *packed, int64_t count, int32_t bits,
+                        uint8_t *one_code_per_byte);
+
+/* Bytes of one packed weight matrix (codes + scales [+ biases]), or -1 for
+ * invalid arguments.  These are also the weight part of the algorithmic bytes
+ * a matvec must move. */
+int64_t qg_bytes_fp4(int64_t n, int64_t k, int32_t group_size);
+int64_t qg_bytes_affine(int64_t n, int64_t k, int32_t bits, int32_t group_size);
+int64_t qg_bytes_fp8(int64_t n, int64_t k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

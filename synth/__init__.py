@@ -111,3 +111,24 @@ def sample_rows(n, count, seed=0):
     rng = np.random.default_rng([0, 99, seed, n])
     pick = rng.choice(n, size=min(count, n), replace=False)
     return np.unique(np.concatenate([pick, [0, n - 1]]).astype(np.int64))
+
+
+def uniform_bytes(shape, seed):
+    """Uniform random bytes (every code value of a format, for decode coverage)."""
+    return np.random.default_rng([0, 77, seed]).integers(0, 256, shape, dtype=np.uint8)
+
+
+def uniform_words(shape, seed):
+    """Uniform random uint32 words."""
+    r = np.random.default_rng([0, 78, seed]).integers(0, 2 ** 32, shape, dtype=np.uint64)
+    return r.astype(np.uint32)
+
+
+def uniform_bf16(shape, lo, hi, seed):
+    """bf16 bits of uniform(lo, hi) values."""
+    v = np.random.default_rng([0, 79, seed]).uniform(lo, hi, shape).astype(np.float32)
+    return _bf16_bits(v)
+
+
+def uniform_f32(shape, lo, hi, seed):
+    return np.random.default_rng([0, 80, seed]).uniform(lo, hi, shape).astype(np.float32)

@@ -1,0 +1,134 @@
+"""The C ABI: the library loads, exports every symbol include/*.h declares, and
+rejects invalid arguments with the documented status before touching a
+device (CPU only: no call here reaches a kernel launch).
+
+Every call below passes at least one invalid argument, so the fake (never
+dereferenced) device addresses are safe on a machine with a GPU too.
+"""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import block_quantized_weight_qgemv_amd as q
+from block_quantized_weight_qgemv_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = q.lib()
+
+OK, NULL, SHAPE, GROUP, MIS, BATCH, DTYPE, BITS, VALUE, LARGE = range(10)
+
+A = ctypes.c_void_p(0x100000)        # 16-byte aligned fake addresses
+A2 = ctypes.c_void_p(0x200000)
+A3 = ctypes.c_void_p(0x300000)
+A4 = ctypes.c_void_p(0x400000)
+ODD = ctypes.c_void_p(0x100008)      # 8-byte aligned only
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(q(?:g|gemv)_[A-Za-z0-9_]+)\s*\(",
+                             text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert {"qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3",
+            "qg_quantize_fp4_e2m1", "qg_pack_u32", "qg_bytes_fp8"} <= names
+    for name in sorted(names):
+        assert hasattr(LIB, name), name
+    # and the binding declares a signature for each of them
+    assert names <= set(B.SIGNATURES), names - set(B.SIGNATURES)
+
+
+def test_abi_version_and_status_strings():
+    assert q.qg_abi_version() == 1
+    for s in range(12):
+        assert isinstance(q.qg_status_string(s), str) and q.qg_status_string(s)
+    assert q.qg_status_string(999) == "unknown status"
+
+
+def test_max_k():
+    assert q.qg_max_k(q.QG_FMT_FP4_E2M1, 1) >= 15360
+    assert q.qg_max_k(q.QG_FMT_AFFINE_U8, 1) >= 15360
+    assert q.qg_max_k(q.QG_FMT_FP8_E4M3, 4) >= 3840
+    assert q.qg_max_k(7, 1) == 0 and q.qg_max_k(0, 5) == 0
+    for f in range(4):
+        assert q.qg_max_k(f, 2) < q.qg_max_k(f, 1)
+
+
+def _fp4(codes=A, scales=A2, x=A3, y=A4, n=8, k=64, gs=32, b=1, out=0):
+    return LIB.qgemv_fp4_e2m1(codes, scales, x, y, n, k, gs, b, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"codes": None}, NULL), ({"scales": None}, NULL), ({"x": None}, NULL), ({"y": None}, NULL),
+    ({"n": 0}, SHAPE), ({"k": 0}, SHAPE), ({"k": 48}, SHAPE), ({"n": -3}, SHAPE),
+    ({"gs": 16}, GROUP), ({"gs": 96}, GROUP), ({"k": 96, "gs": 64}, GROUP),
+    ({"codes": ODD}, MIS), ({"x": ODD}, MIS), ({"y": ctypes.c_void_p(0x100002)}, MIS),
+    ({"b": 0}, BATCH), ({"b": 5}, BATCH), ({"out": 2}, DTYPE),
+    ({"k": 1 << 20}, LARGE), ({"k": 40960, "b": 4}, LARGE),
+])
+def test_fp4_validation(kw, status):
+    assert _fp4(**kw) == status
+
+
+def _aff(fn, codes=A, scales=A2, biases=A2, x=A3, y=A4, n=8, k=128, gs=64, b=1, out=0):
+    return fn(codes, scales, biases, x, y, n, k, gs, b, out, None)
+
+
+@pytest.mark.parametrize("name", ["qgemv_affine_u4", "qgemv_affine_u8"])
+@pytest.mark.parametrize("kw,status", [
+    ({"biases": None}, NULL), ({"scales": None}, NULL), ({"codes": None}, NULL),
+    ({"k": 24}, SHAPE), ({"gs": 0}, GROUP), ({"gs": 256}, GROUP),
+    ({"biases": ctypes.c_void_p(0x200001)}, MIS), ({"b": 9}, BATCH), ({"out": -1}, DTYPE),
+    ({"k": 1 << 22}, LARGE),
+])
+def test_affine_validation(name, kw, status):
+    assert _aff(getattr(LIB, name), **kw) == status
+
+
+def test_u8_group_16_rejected_and_u4_needs_k_multiple_of_32():
+    assert _aff(LIB.qgemv_affine_u8, k=128, gs=16) == GROUP
+    assert _aff(LIB.qgemv_affine_u4, k=16 * 3, gs=32) == SHAPE
+
+
+def _fp8(codes=A, rs=A2, x=A3, y=A4, n=8, k=64, b=1, out=0):
+    return LIB.qgemv_fp8_e4m3(codes, rs, x, y, n, k, b, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"rs": None}, NULL), ({"k": 8}, SHAPE), ({"rs": ctypes.c_void_p(0x200002)}, MIS),
+    ({"b": 0}, BATCH), ({"out": 3}, DTYPE), ({"k": 1 << 20, "b": 1}, LARGE),
+])
+def test_fp8_validation(kw, status):
+    assert _fp8(**kw) == status
+
+
+def test_plan_validation():
+    # an out-of-range plan field is rejected before any device call
+    bad = B.qg_plan(3, 0, 0)
+    assert LIB.qgemv_fp4_e2m1_plan(A, A2, A3, A4, 8, 64, 32, 1, 0, ctypes.byref(bad), None) == SHAPE
+    bad = B.qg_plan(0, 9, 0)
+    assert LIB.qgemv_fp8_e4m3_plan(A, A2, A3, A4, 8, 64, 1, 0, ctypes.byref(bad), None) == SHAPE
+    bad = B.qg_plan(0, 0, -1)
+    assert LIB.qgemv_affine_u4_plan(A, A2, A2, A3, A4, 8, 128, 64, 1, 0, ctypes.byref(bad), None) == SHAPE
+
+
+def test_plan_query_needs_a_device():
+    """qg_plan_query never launches; without a GPU it reports QG_ERR_DEVICE."""
+    import torch
+    plan = B.qg_plan()
+    st = q.lib().qg_plan_query(0, 64, 512, 1, ctypes.byref(plan))
+    if torch.cuda.is_available():
+        assert st == OK and plan.blocks >= 1 and plan.rows_per_tile in (1, 2, 4)
+    else:
+        assert st == 10

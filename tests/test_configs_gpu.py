@@ -1,0 +1,107 @@
+"""The full-size workloads on the GPU, in the launch configuration the bench
+times (the plain entry points).
+
+For each matrix the library quantizes the seeded fp32 weights and the GPU
+computes every output.  The oracle independently re-quantizes a seeded sample
+of rows from the same seeded weights (checking the codes bit for bit) and
+computes those outputs in float64; they must meet the parity criterion.  All
+outputs must be finite and a second launch must reproduce them bitwise.
+
+Workloads (weights ~ N(0, 0.02), x ~ N(0, 1) in bf16, batch 1 unless noted):
+  FP4-E2M1 g32: Gemma-4-12B gate_up 30720x3840, qkv 8192x3840,
+                o_proj 3840x4096, fc_down 3840x15360
+  affine g64 4/8-bit: 15360x3840, 3840x15360, 14336x4096, 4096x14336
+  FP8-E4M3 row scale: lm_head 262144x3840, batch 1 and 4
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_qgemv_amd as q
+import synth
+from oracle import gemv as G
+from oracle import quantize as Q
+from tests import parity
+from tests.gpu_util import dev, host_y, log, out_tensor, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SAMPLE = 192
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _launch(fmt, dargs, xd, y, gs):
+    if fmt == "fp4":
+        q.qgemv_fp4_e2m1(dargs[0], dargs[1], xd, y, gs)
+    elif fmt == "u4":
+        q.qgemv_affine_u4(dargs[0], dargs[1], dargs[2], xd, y, gs)
+    elif fmt == "u8":
+        q.qgemv_affine_u8(dargs[0], dargs[1], dargs[2], xd, y, gs)
+    else:
+        q.qgemv_fp8_e4m3(dargs[0], dargs[1], xd, y)
+
+
+def _full_size(fmt, name, batch=1, gs=None):
+    sid, n, k = synth.shape(name)
+    log("full-size %s %s [%d x %d] batch=%d: generating" % (fmt, name, n, k, batch))
+    w = synth.weights(sid, n, k)
+    if fmt == "fp4":
+        arrays = q.qg_quantize_fp4_e2m1(w, gs)
+    elif fmt in ("u4", "u8"):
+        arrays = q.qg_quantize_affine(w, 4 if fmt == "u4" else 8, gs)
+    else:
+        arrays = q.qg_quantize_fp8_e4m3_rowwise(w)
+    del w
+    x = synth.activations(sid, batch, k)
+    dargs = [dev(a) for a in arrays]
+    xd = dev(x)
+    log("full-size %s %s: launching" % (fmt, name))
+    y = out_tensor(batch, n)
+    _launch(fmt, dargs, xd, y, gs)
+    y1 = host_y(y)
+    y2t = out_tensor(batch, n)
+    _launch(fmt, dargs, xd, y2t, gs)
+    y2 = host_y(y2t)
+    del dargs
+    torch.cuda.empty_cache()
+    assert np.isfinite(y1).all()
+    assert np.array_equal(y1, y2), "second launch differs"
+
+    # the oracle side: re-quantize the sampled rows from the seeded weights
+    rows = synth.sample_rows(n, SAMPLE, seed=sid)
+    w_rows = synth.weight_rows(sid, n, k, rows)
+    if fmt == "fp4":
+        ora = Q.quantize_fp4_e2m1(w_rows, gs)
+        y_ref, a_ref = G.gemv_fp4_e2m1(ora[0], ora[1], x, gs)
+    elif fmt in ("u4", "u8"):
+        bits = 4 if fmt == "u4" else 8
+        ora = Q.quantize_affine(w_rows, bits, gs)
+        y_ref, a_ref = G.gemv_affine(ora[0], ora[1], ora[2], x, bits, gs)
+    else:
+        ora = Q.quantize_fp8_e4m3_rowwise(w_rows)
+        y_ref, a_ref = G.gemv_fp8_e4m3(ora[0], ora[1], x)
+    for a_lib, a_ora in zip(arrays, ora):
+        assert np.array_equal(a_lib[rows], a_ora), "library and oracle codes differ"
+    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "%s %s" % (fmt, name))
+    log("full-size %s %s: %r" % (fmt, name, r))
+
+
+@pytest.mark.parametrize("name", ["gate_up", "qkv", "o_proj", "fc_down"])
+def test_fp4_gemma_shapes(name):
+    _full_size("fp4", name, gs=32)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("name", ["mlp_up", "mlp_down", "llama_up", "llama_down"])
+def test_affine_shapes(bits, name):
+    _full_size("u4" if bits == 4 else "u8", name, gs=64)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_fp8_lm_head(batch):
+    _full_size("fp8", "lm_head", batch=batch)

@@ -1,0 +1,357 @@
+"""GPU parity of the HIP path against the oracle, at sizes the oracle finishes
+in seconds: several tiles, partial passes and ragged row tails, every batch
+size, every group size, both output types, explicit launch shapes, and the
+degenerate cases.  Every call goes through the C ABI (the binding only
+marshals arguments).
+
+Bars (the guarded 1e-3 relative criterion is in tests/parity.py):
+  * general inputs: parity with the float64 oracle;
+  * one-hot activations, the code tables and integer-valued cases: bitwise
+    (each output is one exactly rounded product or an exact integer sum);
+  * batch rows, launch shapes and repeated launches: bitwise identical;
+  * bf16 output: bitwise the round-to-nearest-even of the f32 output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_qgemv_amd as q
+import synth
+from oracle import formats as F
+from oracle import gemv as G
+from oracle import quantize as Q
+from tests import parity
+from tests.gpu_util import dev, host_y, log, out_tensor, require_gpu, run
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _quantize(fmt, w, gs=None):
+    """Codes from the library's pack module, checked bit-exact against the oracle's."""
+    if fmt == "fp4":
+        lib, ora = q.qg_quantize_fp4_e2m1(w, gs), Q.quantize_fp4_e2m1(w, gs)
+    elif fmt in ("u4", "u8"):
+        bits = 4 if fmt == "u4" else 8
+        lib, ora = q.qg_quantize_affine(w, bits, gs), Q.quantize_affine(w, bits, gs)
+    else:
+        lib, ora = q.qg_quantize_fp8_e4m3_rowwise(w), Q.quantize_fp8_e4m3_rowwise(w)
+    for a, b in zip(lib, ora):
+        assert np.array_equal(a, b)
+    return ora
+
+
+def _oracle(fmt, arrays, x, gs=None):
+    if fmt == "fp4":
+        return G.gemv_fp4_e2m1(arrays[0], arrays[1], x, gs)
+    if fmt == "u4":
+        return G.gemv_affine(arrays[0], arrays[1], arrays[2], x, 4, gs)
+    if fmt == "u8":
+        return G.gemv_affine(arrays[0], arrays[1], arrays[2], x, 8, gs)
+    return G.gemv_fp8_e4m3(arrays[0], arrays[1], x)
+
+
+def _case(fmt, n, k, gs, batch, seed, plan=None):
+    log("%s n=%d k=%d gs=%s batch=%d seed=%d plan=%s" % (fmt, n, k, gs, batch, seed, plan))
+    w = synth.weights(100 + seed, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x = synth.activations(100 + seed, batch, k)
+    y = run(fmt, arrays, x, n, gs=gs, plan=plan)
+    y_ref, a_ref = _oracle(fmt, arrays, x, gs)
+    parity.assert_parity(y, y_ref, a_ref, "%s n=%d k=%d" % (fmt, n, k))
+    return arrays, x, y
+
+
+# ---------------------------------------------------------------- configs
+
+def test_tiny_fp4_config():
+    """Tiny FP4-E2M1 GEMV: W [256, 512], group 32, bf16 absmax scales, seed 0."""
+    w, x = synth.tiny_fp4_inputs()
+    arrays = _quantize("fp4", w, 32)
+    log("tiny fp4 256x512")
+    y = run("fp4", arrays, x, 256, gs=32)
+    y_ref, a_ref = G.gemv_fp4_e2m1(arrays[0], arrays[1], x, 32)
+    r = parity.assert_parity(y, y_ref, a_ref, "tiny")
+    log("tiny fp4 parity %r" % r)
+
+
+@pytest.mark.parametrize("n,k,gs,batch", [
+    (1, 32, 32, 1), (7, 64, 32, 2), (33, 3840, 32, 1), (100, 512, 128, 3),
+    (65, 4224, 64, 4), (300, 15360, 32, 1), (129, 2048, 32, 4), (5, 8192, 128, 2),
+])
+def test_fp4_shapes(n, k, gs, batch):
+    _case("fp4", n, k, gs, batch, seed=n + k)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("n,k,gs,batch", [
+    (1, 64, 64, 1), (9, 128, 32, 2), (40, 3840, 64, 1), (77, 4096, 64, 3),
+    (31, 15360, 64, 1), (64, 14336, 128, 4), (3, 1088, 64, 2),
+])
+def test_affine_shapes(bits, n, k, gs, batch):
+    _case("u4" if bits == 4 else "u8", n, k, gs, batch, seed=bits * 1000 + n + k)
+
+
+@pytest.mark.parametrize("n,k,batch", [
+    (1, 16, 1), (8, 48, 2), (50, 3840, 4), (257, 1040, 1), (19, 4096, 3), (2, 15360, 1),
+])
+def test_fp8_shapes(n, k, batch):
+    _case("fp8", n, k, None, batch, seed=n * 7 + k)
+
+
+# ---------------------------------------------------------------- code tables
+
+def _one_hot(k, col, batch=1):
+    x = np.zeros((batch, k), np.uint16)
+    x[:, col] = 0x3F80
+    return x
+
+
+def test_fp4_all_codes_bitwise():
+    """Row c holds code c in every position; x one-hot on an even and an odd column."""
+    n, k = 16, 64
+    codes = np.array([[c | (c << 4)] * (k // 2) for c in range(16)], np.uint8)
+    scales = np.full((n, k // 32), 0x3F80, np.uint16)            # scale 1
+    for col in (0, 1, 62, 63):
+        log("fp4 code table col=%d" % col)
+        y = run("fp4", (codes, scales), _one_hot(k, col), n, gs=32)
+        assert np.array_equal(y[0].astype(np.float64), F.E2M1_TABLE), (col, y)
+
+
+def test_fp8_all_codes_bitwise():
+    n, k = 256, 32
+    codes = np.repeat(np.arange(256, dtype=np.uint8)[:, None], k, axis=1)
+    rs = np.ones(n, np.float32)
+    for col in (0, 5, 31):
+        log("fp8 code table col=%d" % col)
+        y = run("fp8", (codes, rs), _one_hot(k, col), n)
+        want = F.E4M3_TABLE
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(y[0]), nan)
+        assert np.array_equal(y[0][~nan].astype(np.float64), want[~nan])
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_affine_all_codes_bitwise(bits):
+    n, k, per = 1 << bits, 128, 32 // bits
+    levels = np.arange(n, dtype=np.uint32)
+    word = np.zeros(n, np.uint32)
+    for j in range(per):
+        word |= levels << (bits * j)
+    codes = np.repeat(word[:, None], k // per, axis=1)
+    scales = np.full((n, 2), 0x3F80, np.uint16)                  # s = 1
+    biases = np.zeros((n, 2), np.uint16)                         # b = 0
+    for col in (0, 1, 2, 3, 5, 7, 127):
+        log("u%d code table col=%d" % (bits, col))
+        y = run("u4" if bits == 4 else "u8", (codes, scales, biases), _one_hot(k, col), n, gs=64)
+        assert np.array_equal(y[0], levels.astype(np.float32)), (col, y[0][:20])
+
+
+# ---------------------------------------------------------------- exact cases
+
+@pytest.mark.parametrize("fmt,gs", [("fp4", 32), ("fp4", 128), ("u4", 64), ("u8", 64), ("fp8", None)])
+def test_one_hot_reads_one_column_bitwise(fmt, gs):
+    n, k = 70, 4096
+    w = synth.weights(7, n, k)
+    arrays = _quantize(fmt, w, gs)
+    if fmt == "fp4":
+        w_hat = G.dequant_fp4_e2m1(arrays[0], arrays[1], k, gs)
+    elif fmt in ("u4", "u8"):
+        w_hat = G.dequant_affine(arrays[0], arrays[1], arrays[2], k, 4 if fmt == "u4" else 8, gs)
+    else:
+        w_hat = G.dequant_fp8_e4m3(arrays[0], arrays[1])
+    for col in (0, 1, 31, 32, 2047, 4095):
+        log("one-hot %s col=%d" % (fmt, col))
+        y = run(fmt, arrays, _one_hot(k, col), n, gs=gs)
+        # one product (plus the bias for affine), rounded once to f32
+        assert np.array_equal(y[0], w_hat[:, col].astype(np.float32)), (fmt, col)
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_affine_integer_case_bitwise(bits):
+    """s = 1, b = 0 and small-integer x: y is an exact integer matvec."""
+    n, k, gs = 96, 3840, 64
+    per = 32 // bits
+    rng = np.random.default_rng(bits)
+    codes = synth.uniform_words((n, k // per), bits)
+    scales = np.full((n, k // gs), 0x3F80, np.uint16)
+    biases = np.zeros((n, k // gs), np.uint16)
+    xi = rng.integers(-4, 5, (2, k))
+    x = torch.from_numpy(xi.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    log("affine integer case bits=%d" % bits)
+    y = run("u4" if bits == 4 else "u8", (codes, scales, biases), x, n, gs=gs)
+    from oracle.layout import unpack_u32
+    qmat = unpack_u32(codes, k, bits).astype(np.int64)
+    want = xi @ qmat.T
+    assert np.abs(want).max() < 2 ** 24
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+# ---------------------------------------------------------------- uniform random codes
+
+@pytest.mark.parametrize("fmt", ["fp4", "u4", "u8", "fp8"])
+def test_uniform_random_codes(fmt):
+    """Every code value (not just those a Gaussian quantizes to) against the oracle."""
+    n, k, gs, batch = 200, 2560, 64, 2
+    if fmt == "fp4":
+        arrays = (synth.uniform_bytes((n, k // 2), 1), synth.uniform_bf16((n, k // gs), 1e-3, 0.1, 1))
+    elif fmt in ("u4", "u8"):
+        per = 8 if fmt == "u4" else 4
+        arrays = (synth.uniform_words((n, k // per), 2), synth.uniform_bf16((n, k // gs), 1e-4, 1e-2, 2),
+                  synth.uniform_bf16((n, k // gs), -0.2, 0.2, 3))
+    else:
+        c = synth.uniform_bytes((n, k), 4)
+        c[(c & 0x7F) == 0x7F] = 0x7E                               # no NaN codes here
+        arrays = (c, synth.uniform_f32(n, 1e-4, 1e-2, 4))
+    x = synth.uniform_bf16((batch, k), -2.0, 2.0, 5)
+    log("uniform codes %s" % fmt)
+    y = run(fmt, arrays, x, n, gs=gs)
+    y_ref, a_ref = _oracle(fmt, arrays, x, gs)
+    parity.assert_parity(y, y_ref, a_ref, fmt)
+
+
+def test_fp8_nan_code_gives_nan_row():
+    n, k = 6, 64
+    codes = np.full((n, k), 0x38, np.uint8)                        # 1.0
+    codes[2, 17] = 0x7F
+    codes[4, 0] = 0xFF
+    x = synth.uniform_bf16((1, k), 0.5, 1.0, 6)
+    log("fp8 nan row")
+    y = run("fp8", (codes, np.ones(n, np.float32)), x, n)
+    assert np.isnan(y[0, 2]) and np.isnan(y[0, 4])
+    assert np.isfinite(y[0, [0, 1, 3, 5]]).all()
+
+
+def test_zero_scale_rows_give_zero():
+    n, k = 9, 256
+    w = synth.weights(8, n, k)
+    w[3] = 0.0
+    arrays = _quantize("fp4", w, 32)
+    log("zero row fp4")
+    y = run("fp4", arrays, synth.activations(8, 1, k), n, gs=32)
+    assert y[0, 3] == 0.0
+
+
+# ---------------------------------------------------------------- bitwise consistency
+
+@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 3840), ("u4", 64, 4096), ("u8", 64, 3840), ("fp8", None, 3840)])
+def test_batch_rows_match_single_calls_bitwise(fmt, gs, k):
+    n = 515
+    w = synth.weights(9, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x4 = synth.activations(9, 4, k)
+    log("batch consistency %s" % fmt)
+    y4 = run(fmt, arrays, x4, n, gs=gs)
+    for b in range(4):
+        y1 = run(fmt, arrays, x4[b:b + 1], n, gs=gs)
+        assert np.array_equal(y1[0], y4[b]), (fmt, b)
+    for bsz in (2, 3):
+        yb = run(fmt, arrays, x4[:bsz], n, gs=gs)
+        assert np.array_equal(yb, y4[:bsz])
+
+
+PLANS = [None, {"rows_per_tile": 1}, {"rows_per_tile": 2}, {"rows_per_tile": 4},
+         {"rows_per_tile": 4, "waves_per_block": 1, "blocks": 3},
+         {"rows_per_tile": 2, "waves_per_block": 8, "blocks": 5},
+         {"rows_per_tile": 1, "waves_per_block": 2, "blocks": 1000},
+         {"waves_per_block": 3, "blocks": 7}]
+
+
+@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 3840), ("u4", 64, 15360), ("u8", 128, 1024), ("fp8", None, 2048)])
+def test_launch_shapes_bitwise_identical(fmt, gs, k):
+    n = 1001
+    w = synth.weights(10, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x = synth.activations(10, 2, k)
+    ys = []
+    for plan in PLANS:
+        log("plan %s %s" % (fmt, plan))
+        ys.append(run(fmt, arrays, x, n, gs=gs, plan=plan))
+    y_ref, a_ref = _oracle(fmt, arrays, x, gs)
+    parity.assert_parity(ys[0], y_ref, a_ref)
+    for y in ys[1:]:
+        assert np.array_equal(y, ys[0])
+
+
+def test_repeated_launches_bitwise_identical():
+    n, k = 4000, 3840
+    w = synth.weights(11, n, k)
+    codes, scales = _quantize("fp4", w, 32)
+    cd, sd = dev(codes), dev(scales)
+    xd = dev(synth.activations(11, 1, k))
+    outs = []
+    for _ in range(3):
+        y = out_tensor(1, n)
+        q.qgemv_fp4_e2m1(cd, sd, xd, y, 32)
+        outs.append(host_y(y))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("fmt,gs", [("fp4", 32), ("u4", 64), ("u8", 64), ("fp8", None)])
+def test_bf16_output_is_rne_of_f32_output(fmt, gs):
+    n, k = 333, 1024
+    w = synth.weights(12, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x = synth.activations(12, 3, k)
+    log("bf16 out %s" % fmt)
+    y32 = run(fmt, arrays, x, n, gs=gs)
+    y16 = run(fmt, arrays, x, n, gs=gs, bf16=True)
+    assert np.array_equal(y16, F.f64_to_bf16_bits(y32.astype(np.float64)))
+
+
+# ---------------------------------------------------------------- poisoning
+
+GUARD = 4096
+
+
+def _guarded(a, fill_byte):
+    """Device buffer with GUARD bytes of `fill_byte` before and after `a`."""
+    raw = np.ascontiguousarray(a).view(np.uint8).ravel()
+    buf = np.full(raw.size + 2 * GUARD, fill_byte, np.uint8)
+    buf[GUARD:GUARD + raw.size] = raw
+    d = torch.from_numpy(buf).to("cuda:0")
+    return d, d[GUARD:GUARD + raw.size]
+
+
+@pytest.mark.parametrize("fmt,gs", [("fp4", 64), ("u4", 64), ("u8", 32), ("fp8", None)])
+def test_poisoned_neighbours_are_never_read_or_written(fmt, gs):
+    """NaN in every byte around the inputs; y pre-filled with NaN and fenced by canaries."""
+    n, k, batch = 123, 3904 if fmt != "fp8" else 3856, 2
+    w = synth.weights(13, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x = synth.activations(13, batch, k)
+    # bf16 NaN is 0x7FC0 -> bytes C0 7F; 0xFF bytes are NaN for bf16 and f32
+    # and the E4M3 NaN code; for packed 4-bit codes 0xFF is a valid code (-6),
+    # which a stray read would still turn into a parity failure
+    dev_arrays = []
+    for a in arrays:
+        full, view = _guarded(a, 0xFF)
+        dt = {np.uint8: torch.uint8, np.uint16: torch.int16, np.uint32: torch.int32,
+              np.float32: torch.float32}[a.dtype.type]
+        dev_arrays.append((full, view.view(dt).view(a.shape)))
+    xfull, xv = _guarded(x, 0xFF)
+    xv = xv.view(torch.int16).view(batch, k)
+    yfull = torch.full(((batch * n * 4) + 2 * GUARD,), 0xAB, dtype=torch.uint8, device="cuda:0")
+    yv = yfull[GUARD:GUARD + batch * n * 4].view(torch.float32).view(batch, n)
+    yv.fill_(float("nan"))
+    log("poison %s" % fmt)
+    views = [v for _, v in dev_arrays]
+    if fmt == "fp4":
+        q.qgemv_fp4_e2m1(views[0], views[1], xv, yv, gs)
+    elif fmt == "u4":
+        q.qgemv_affine_u4(views[0], views[1], views[2], xv, yv, gs)
+    elif fmt == "u8":
+        q.qgemv_affine_u8(views[0], views[1], views[2], xv, yv, gs)
+    else:
+        q.qgemv_fp8_e4m3(views[0], views[1], xv, yv)
+    y = host_y(yv)
+    assert np.isfinite(y).all(), "unwritten or poisoned outputs"
+    yb = yfull.cpu().numpy()
+    assert (yb[:GUARD] == 0xAB).all() and (yb[-GUARD:] == 0xAB).all(), "write outside y"
+    y_ref, a_ref = _oracle(fmt, arrays, x, gs)
+    parity.assert_parity(y, y_ref, a_ref)
