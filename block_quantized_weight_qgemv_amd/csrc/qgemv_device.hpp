@@ -271,7 +271,7 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, false));
 }
 
-// Sum every lane's V partials over the wave.  Step A adds lanes l and l^32
+// Sum every lane's V partials over the wave (V a power of two).  Step A adds lanes l and l^32
 // (when V >= 2 the two halves of the wave keep different halves of the
 // values), step B adds l and l^16 the same way, then a 16-lane row is summed
 // by DPP rotations.  Afterwards the first lane of each 16-lane row holds
@@ -280,6 +280,7 @@ __device__ __forceinline__ float dpp_f(float v) {
 // carried it.  Must run with all 64 lanes active.
 template <int V>
 struct WaveSum {
+    static_assert((V & (V - 1)) == 0, "WaveSum needs a power-of-two count");
     static constexpr bool kSplitA = V >= 2;
     static constexpr int kAfterA = kSplitA ? V / 2 : 1;
     static constexpr bool kSplitB = kAfterA >= 2;
@@ -336,10 +337,17 @@ struct WaveSum {
 
 // ------------------------------------------------------------------ kernel
 
+constexpr int pow2_ceil(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
 template <class Fmt, int R, int B, int D>
 struct Kernel {
     using Aux = typename Fmt::Aux;
     static constexpr int V = R * B;
+    static constexpr int VP = pow2_ceil(V);     // WaveSum halves the count twice
 
     struct Buf {
         uint4 c[R];
@@ -356,7 +364,7 @@ template <class Fmt, int R, int B, int D>
 __global__ void __launch_bounds__(512) qgemv_kernel(const Params p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     using K = Kernel<Fmt, R, B, D>;
-    using Red = WaveSum<K::V>;
+    using Red = WaveSum<K::VP>;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -459,7 +467,7 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const Params p) {
         }
         if (j == passes - 1) {
             // tile complete: wave-reduce the R x B partials and write y
-            float v[K::V];
+            float v[K::VP];
 #pragma unroll
             for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -467,6 +475,8 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const Params p) {
                     v[i * B + b] = acc[i][b];
                     acc[i][b] = 0.0f;
                 }
+#pragma unroll
+            for (int i = K::V; i < K::VP; ++i) v[i] = 0.0f;
             Red::run(v);
             if (Red::writer(lane)) {
 #pragma unroll
@@ -474,7 +484,7 @@ __global__ void __launch_bounds__(512) qgemv_kernel(const Params p) {
                     const int idx = Red::value_index(lane, q);
                     const int i = idx / B, b = idx % B;
                     const int64_t row = row0 + i;
-                    if (row < r_end) {
+                    if (idx < K::V && row < r_end) {
                         float out = v[q];
                         if constexpr (Fmt::kRowScale) out *= p.row_scale[row];
                         if (p.out_bf16)

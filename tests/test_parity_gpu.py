@@ -94,7 +94,25 @@ def test_fp4_shapes(n, k, gs, batch):
     (31, 15360, 64, 1), (64, 14336, 128, 4), (3, 1088, 64, 2),
 ])
 def test_affine_shapes(bits, n, k, gs, batch):
-    _case("u4" if bits == 4 else "u8", n, k, gs, batch, seed=bits * 1000 + n + k)
+    fmt = "u4" if bits == 4 else "u8"
+    fid = q.QG_FMT_AFFINE_U4 if bits == 4 else q.QG_FMT_AFFINE_U8
+    while k > q.qg_max_k(fid, batch):       # u8 stages x as f32: a smaller batch fits
+        batch -= 1
+    _case(fmt, n, k, gs, batch, seed=bits * 1000 + n + k)
+
+
+def test_staging_limit_is_enforced():
+    k = q.qg_max_k(q.QG_FMT_AFFINE_U8, 4) + 32
+    k -= k % 32
+    n = 4
+    codes = dev(np.zeros((n, k // 4), np.uint32))
+    sb = dev(np.zeros((n, k // 32), np.uint16))
+    x = dev(np.zeros((4, k), np.uint16))
+    y = out_tensor(4, n)
+    with pytest.raises(q.QgError) as e:
+        q.qgemv_affine_u8(codes, sb, sb, x, y, 32)
+    assert e.value.name == "QG_ERR_TOO_LARGE"
+    assert torch.isnan(y).all()
 
 
 @pytest.mark.parametrize("n,k,batch", [
