@@ -1,0 +1,391 @@
+#!/usr/bin/env python3
+"""Benchmark of the MI355X block-quantized weight matvec.
+
+Default workload (one JSON line on stdout): the Gemma-4-12B-shaped FP4-E2M1
+gate_up matvec, W [30720, 3840] with group-32 bf16 scales, x bf16, batch 1,
+fp32 output.  One step is one full matvec over one weight matrix; the weights
+rotate over >= 1 GiB of distinct device copies so that every step streams its
+weights from HBM rather than from the 256 MB Infinity Cache, as the distinct
+layers of a decode token do.  Inputs are resident in HBM before timing starts.
+
+  value          algorithmic bytes of the K timed steps / elapsed time (GB/s)
+  ms_per_step    elapsed time / K (HIP events on the launch stream)
+  roofline       the same kernel duration against the 8 TB/s HBM peak;
+                 traffic from rocprofv3 FETCH_SIZE / WRITE_SIZE when known
+  cpu_baseline   the float64 oracle on the host cores, on the same workload
+
+Algorithmic bytes of one FP4 g32 matvec: N*K/2 codes + N*K/32*2 scales +
+B*K*2 activations + B*N*4 outputs (66,485,760 B for gate_up).
+
+Other modes: --sweep times every workload shape (plain entry points) and the
+48-layer FP4 decode step, writing a table to stderr and JSON to --out;
+--calibrate-copy times a plain device copy (the reference kernel for the
+rocprofv3 byte counters); --plan R,W,B overrides the launch shape.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "quantized GEMV HBM GB/s & % of 8 TB/s peak; µs per Gemma-12B-shaped matvec"
+ROT_BYTES = 1 << 30
+# rocprofv3 FETCH_SIZE / WRITE_SIZE per launch of the default workload, scaled
+# by the same counters on a plain copy of known size (see profiles/)
+TRAFFIC = None
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+# ------------------------------------------------------------------ workloads
+
+def algorithmic_bytes(fmt, n, k, batch, gs):
+    import block_quantized_weight_qgemv_amd as q
+    if fmt == "fp4":
+        w = q.qg_bytes_fp4(n, k, gs)
+    elif fmt in ("u4", "u8"):
+        w = q.qg_bytes_affine(n, k, 4 if fmt == "u4" else 8, gs)
+    else:
+        w = q.qg_bytes_fp8(n, k)
+    return w + batch * k * 2 + batch * n * 4
+
+
+def quantize(fmt, w, gs):
+    import block_quantized_weight_qgemv_amd as q
+    if fmt == "fp4":
+        return q.qg_quantize_fp4_e2m1(w, gs)
+    if fmt in ("u4", "u8"):
+        return q.qg_quantize_affine(w, 4 if fmt == "u4" else 8, gs)
+    return q.qg_quantize_fp8_e4m3_rowwise(w)
+
+
+def to_dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    elif a.dtype == np.uint32:
+        a = a.view(np.int32)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+class Workload:
+    """Device-resident copies of one quantized matrix and a launch closure."""
+
+    def __init__(self, fmt, shape_name, batch=1, gs=None, copies=None, plan=None, keep_host=False):
+        import torch
+        import synth
+        import block_quantized_weight_qgemv_amd as q
+        self.q = q
+        self.fmt, self.name, self.batch, self.gs, self.plan = fmt, shape_name, batch, gs, plan
+        sid, n, k = synth.shape(shape_name)
+        self.n, self.k = n, k
+        w = synth.weights(sid, n, k)
+        self.host = quantize(fmt, w, gs)
+        del w
+        self.x_host = synth.activations(sid, batch, k)
+        self.bytes = algorithmic_bytes(fmt, n, k, batch, gs)
+        wbytes = sum(a.nbytes for a in self.host)
+        self.copies = copies or max(1, math.ceil(ROT_BYTES / wbytes))
+        first = [to_dev(a) for a in self.host]
+        self.dev = [first] + [[t.clone() for t in first] for _ in range(self.copies - 1)]
+        if not keep_host:
+            self.host = None
+        self.x = to_dev(self.x_host)
+        self.y = torch.empty((batch, n), dtype=torch.float32, device="cuda:0")
+
+    def launch(self, i):
+        d = self.dev[i % self.copies]
+        q = self.q
+        if self.fmt == "fp4":
+            q.qgemv_fp4_e2m1(d[0], d[1], self.x, self.y, self.gs, plan=self.plan)
+        elif self.fmt == "u4":
+            q.qgemv_affine_u4(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
+        elif self.fmt == "u8":
+            q.qgemv_affine_u8(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
+        else:
+            q.qgemv_fp8_e4m3(d[0], d[1], self.x, self.y, plan=self.plan)
+
+    def label(self):
+        return "%s %s [%dx%d] B=%d" % (self.fmt, self.name, self.n, self.k, self.batch)
+
+
+def time_steps(launch, steps, warmup, mode="graph"):
+    """Run `warmup` untimed steps, then time exactly `steps` steps; returns ms."""
+    import torch
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                launch(warmup + i)
+        g.replay()                       # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        start.record()
+        g.replay()
+        stop.record()
+    else:
+        start.record()
+        for i in range(steps):
+            launch(warmup + i)
+        stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop)
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(wl, target_s=12.0):
+    """The float64 oracle on the host cores over the same packed matrix.
+
+    Row blocks of 2048 rows are spread over one worker thread per usable core
+    (BLAS pinned to one thread per worker); whole matvecs are repeated until
+    about `target_s` seconds have passed.
+    """
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import gemv as G
+
+    cores = min(16, len(os.sched_getaffinity(0)))
+    arrays, x, n, gs = wl.host, wl.x_host, wl.n, wl.gs
+    blocks = [(r, min(n, r + 2048)) for r in range(0, n, 2048)]
+
+    def one(bounds):
+        r0, r1 = bounds
+        if wl.fmt == "fp4":
+            return G.gemv_fp4_e2m1(arrays[0][r0:r1], arrays[1][r0:r1], x, gs)
+        if wl.fmt in ("u4", "u8"):
+            return G.gemv_affine(arrays[0][r0:r1], arrays[1][r0:r1], arrays[2][r0:r1], x,
+                                 4 if wl.fmt == "u4" else 8, gs)
+        return G.gemv_fp8_e4m3(arrays[0][r0:r1], arrays[1][r0:r1], x)
+
+    passes = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(1), ThreadPoolExecutor(cores) as ex:
+        while True:
+            list(ex.map(one, blocks))
+            passes += 1
+            if time.perf_counter() - t0 >= target_s:
+                break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(wl.bytes * passes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": "%d full %dx%d matvecs (same packed weights and x), float64 oracle, "
+                  "%d threads over 2048-row blocks, %.1f s" % (passes, wl.n, wl.k, cores, dt),
+    }
+
+
+# ------------------------------------------------------------------ modes
+
+def parse_plan(s):
+    if not s:
+        return None
+    r, w, b = (int(v) for v in s.split(","))
+    return {"rows_per_tile": r, "waves_per_block": w, "blocks": b}
+
+
+def run_default(args):
+    import torch
+    plan = parse_plan(args.plan)
+    wl = Workload("fp4", "gate_up", batch=1, gs=32, plan=plan, keep_host=not args.no_cpu_baseline)
+    log("bench: %s, %d weight copies (%.2f GB), %d warmup + %d timed steps, mode=%s"
+        % (wl.label(), wl.copies, wl.copies * (wl.bytes / 1e9), args.warmup, args.steps, args.mode))
+    ms = time_steps(wl.launch, args.steps, args.warmup, args.mode)
+    ms_per_step = ms / args.steps
+    gbs = wl.bytes / (ms_per_step * 1e-3) / 1e9
+    log("bench: %.3f ms for %d steps -> %.2f us/step, %.1f GB/s (%.1f%% of 8 TB/s)"
+        % (ms, args.steps, ms_per_step * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS))
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4_e2m1 weights, bf16 x, f32 accumulate",
+        "data": "synthetic (seeded N(0,0.02) weights quantized on the host, N(0,1) bf16 x)",
+        "config": {
+            "workload": "Gemma-4-12B FP4-E2M1 gate_up matvec W[30720x3840] group-32 bf16 scales, batch 1",
+            "n": wl.n, "k": wl.k, "batch": 1, "group_size": 32,
+            "us_per_matvec": round(ms_per_step * 1e3, 3),
+            "algorithmic_bytes_per_step": wl.bytes,
+            "weight_copies_rotated": wl.copies,
+            "launch": args.mode,
+            "plan": wl.q.qg_plan_query(wl.q.QG_FMT_FP4_E2M1, wl.n, wl.k, 1) if plan is None else plan,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": TRAFFIC,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on the host")
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out))
+
+
+SWEEP = [
+    ("fp4", "gate_up", 1, 32), ("fp4", "qkv", 1, 32), ("fp4", "o_proj", 1, 32), ("fp4", "fc_down", 1, 32),
+    ("u4", "mlp_up", 1, 64), ("u4", "mlp_down", 1, 64), ("u4", "llama_up", 1, 64), ("u4", "llama_down", 1, 64),
+    ("u8", "mlp_up", 1, 64), ("u8", "mlp_down", 1, 64), ("u8", "llama_up", 1, 64), ("u8", "llama_down", 1, 64),
+    ("fp8", "lm_head", 1, None), ("fp8", "lm_head", 4, None), ("fp4", "tiny", 1, 32),
+]
+
+
+def run_sweep(args):
+    import torch
+    rows = []
+    only = set(args.only.split(",")) if args.only else None
+    for fmt, name, batch, gs in SWEEP:
+        if only and name not in only and "%s:%s" % (fmt, name) not in only:
+            continue
+        wl = Workload(fmt, name, batch=batch, gs=gs, plan=parse_plan(args.plan))
+        steps = args.steps
+        ms = time_steps(wl.launch, steps, args.warmup, args.mode)
+        us = ms / steps * 1e3
+        gbs = wl.bytes / (us * 1e-6) / 1e9
+        row = {"fmt": fmt, "shape": name, "n": wl.n, "k": wl.k, "batch": batch, "group_size": gs,
+               "bytes": wl.bytes, "copies": wl.copies, "us": round(us, 3), "GBps": round(gbs, 1),
+               "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+        rows.append(row)
+        log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%" % (wl.label(), us, gbs, 100 * gbs / HBM_PEAK_GBS))
+        del wl
+        torch.cuda.empty_cache()
+    if not only or "step48" in only:
+        rows.append(run_decode_step(args))
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+def run_decode_step(args, layers=48):
+    """The FP4 decode step: qkv, o_proj, gate_up, fc_down for 48 distinct layers."""
+    import torch
+    shapes = ["qkv", "o_proj", "gate_up", "fc_down"]
+    wls = [Workload("fp4", s, batch=1, gs=32, copies=layers) for s in shapes]
+    total = sum(w.bytes for w in wls) * layers
+
+    def launch(i):
+        layer = i // len(shapes)
+        wls[i % len(shapes)].launch(layer)
+
+    steps = layers * len(shapes)
+    ms_runs = [time_steps(launch, steps, steps, args.mode) for _ in range(5)]
+    ms = float(np.median(ms_runs))
+    gbs = total / (ms * 1e-3) / 1e9
+    log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  (192 launches, median of 5)"
+        % ("fp4 48-layer decode step", ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS))
+    del wls
+    torch.cuda.empty_cache()
+    return {"fmt": "fp4", "shape": "decode_step_48_layers", "bytes": total, "launches": steps,
+            "us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def run_probe(args):
+    """Achievable HBM read bandwidth: the stream probe over a 2 GiB buffer, and
+    over 64 MiB windows rotating through it (the size of one matvec)."""
+    import torch
+    import block_quantized_weight_qgemv_amd as q
+    total = 2 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda:0").fill_(7)
+    rows = []
+    for window in (total, 64 << 20):
+        nwin = total // window
+        best = {}
+        for pattern in (3, 4, 5):
+            for unroll in (4, 8, 16):
+                for tpb in (256, 512):
+                    for waves_per_cu in (8, 16, 32):
+                        blocks = 256 * waves_per_cu * 64 // tpb
+                        out = torch.empty(blocks * tpb, dtype=torch.int32, device="cuda:0")
+                        views = [buf[i * window:(i + 1) * window] for i in range(nwin)]
+                        launch = lambda i: q.qg_stream_probe(views[i % nwin], pattern, unroll, blocks, tpb, out)
+                        steps = 10 if window == total else 64
+                        ms = time_steps(launch, steps, 2, "graph") / steps
+                        gbs = window / (ms * 1e-3) / 1e9
+                        rows.append({"window": window, "pattern": pattern, "unroll": unroll, "threads": tpb,
+                                     "blocks": blocks, "us": round(ms * 1e3, 2), "GBps": round(gbs, 1)})
+                        if gbs > best.get(pattern, (0,))[0]:
+                            best[pattern] = (gbs, unroll, tpb, blocks, ms * 1e3)
+        for pattern, b in sorted(best.items()):
+            log("probe window=%5d MiB pattern=%d best: %.1f GB/s (%.1f%% of 8 TB/s) %.2f us unroll=%d tpb=%d blocks=%d"
+                % (window >> 20, pattern, b[0], 100 * b[0] / HBM_PEAK_GBS, b[4], b[1], b[2], b[3]))
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+def run_calibrate_copy(args):
+    """A plain device copy of known size, for scaling the rocprofv3 byte counters."""
+    import torch
+    nbytes = 512 << 20
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log("calibrate: copied %d bytes 3 times (each copy reads %d and writes %d bytes)" % (nbytes, nbytes, nbytes))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
+    ap.add_argument("--plan", default="", help="rows_per_tile,waves_per_block,blocks")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--only", default="", help="with --sweep: comma list of shape names or fmt:shape")
+    ap.add_argument("--out", default="")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--probe", action="store_true", help="stream-probe read bandwidth sweep")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py runs on one GPU only: this matvec library has no multi-GPU path "
+                         "(rows would shard across GPUs with no exchange; see DESIGN.md)\n")
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a HIP device\n")
+        return 1
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        run_calibrate_copy(args)
+    elif args.probe:
+        run_probe(args)
+    elif args.sweep:
+        run_sweep(args)
+    else:
+        run_default(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -26,7 +26,7 @@ qg_plan = _b.qg_plan
 
 __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3",
-    "qg_plan", "qg_plan_query", "qg_status_string", "qg_abi_version", "qg_max_k",
+    "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
     "qg_bytes_fp4", "qg_bytes_affine", "qg_bytes_fp8", "lib",
@@ -181,6 +181,21 @@ def qgemv_fp8_e4m3(codes, row_scale, x, y, plan=None, stream=None):
     st = _lib.qgemv_fp8_e4m3_plan(cp, rp, xp, yp, n, k, batch, out, _plan_ptr(plan), _stream(stream, y.device))
     _check(st, "qgemv_fp8_e4m3")
     return y
+
+
+def qg_stream_probe(buf, pattern=1, unroll=8, blocks=1024, threads_per_block=256, out=None, stream=None):
+    """Read every byte of the device tensor `buf` (the HBM read-bandwidth reference)."""
+    torch = _torch()
+    if not (isinstance(buf, torch.Tensor) and buf.is_cuda and buf.is_contiguous()):
+        raise ValueError("buf must be a contiguous device tensor")
+    nbytes = buf.numel() * buf.element_size()
+    if out is None:
+        out = torch.empty(blocks * threads_per_block, dtype=torch.int32, device=buf.device)
+    st = _lib.qg_stream_probe(ctypes.c_void_p(buf.data_ptr()), nbytes, int(pattern), int(unroll),
+                              int(blocks), int(threads_per_block), ctypes.c_void_p(out.data_ptr()),
+                              _stream(stream, buf.device))
+    _check(st, "qg_stream_probe")
+    return out
 
 
 def qg_plan_query(fmt, n, k, batch=1):

@@ -46,6 +46,7 @@ SIGNATURES = {
     "qgemv_fp8_e4m3": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _p]),
     "qgemv_fp8_e4m3_plan": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _p]),
     "qg_plan_query": (_st, [_i32, _i64, _i64, _i32, _p]),
+    "qg_stream_probe": (_st, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "qg_status_string": (ctypes.c_char_p, [_st]),
     "qg_abi_version": (ctypes.c_int, []),
     "qg_max_k": (_i64, [_i32, _i32]),
@@ -65,7 +66,7 @@ SIGNATURES = {
 def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(
-            "libqgemv.so is not built (%s); run `python -m block_quantized_weight_qgemv_amd.build` "
+            "libqgemv.so is not built (%s); run `python block_quantized_weight_qgemv_amd/build.py` "
             "or __graft_entry__.build()" % path)
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():

@@ -1,7 +1,9 @@
 """Build libqgemv.so in-tree: the HIP kernels + C ABI (hipcc, gfx950) and the
 host pack module (g++, no floating-point contraction).
 
-    python -m block_quantized_weight_qgemv_amd.build
+    python block_quantized_weight_qgemv_amd/build.py
+
+(run as a script: importing the package would load the library being built)
 """
 
 import os

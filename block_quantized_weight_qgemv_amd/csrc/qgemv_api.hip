@@ -8,6 +8,7 @@
 
 #include "qgemv.h"
 #include "qgemv_device.hpp"
+#include "stream_probe.hpp"
 
 #include <atomic>
 #include <mutex>
@@ -37,10 +38,12 @@ FmtInfo fmt_info(qg_format f) {
     }
 }
 
+// must equal qg::Kernel<...>::lds_bytes
 int64_t lds_bytes(qg_format f, int64_t k, int32_t batch) {
     const FmtInfo fi = fmt_info(f);
     const int64_t chunks = k / fi.wpc;
-    return int64_t(batch) * fi.pieces * chunks * 16 + (fi.sums ? int64_t(batch) * chunks * 4 : 0);
+    return int64_t(batch) * fi.pieces * chunks * 16 + (fi.sums ? int64_t(batch) * chunks * 4 : 0) +
+           qg::kLdsSink;
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -121,7 +124,7 @@ Plan default_plan(qg_format f, int64_t n, int64_t k, int32_t batch, int cus) {
 
 template <class Fmt, int R, int B>
 qg_status launch_inst(const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
-    constexpr int D = R == 1 ? 8 : (R == 2 ? 4 : 2);
+    constexpr int D = R == 1 ? 8 : 4;
     auto kern = qg::qgemv_kernel<Fmt, R, B, D>;
     static std::once_flag attr_once;
     static hipError_t attr_err = hipSuccess;
@@ -329,12 +332,35 @@ const char *qg_status_string(qg_status status) {
 
 int qg_abi_version(void) { return QG_ABI_VERSION; }
 
+qg_status qg_stream_probe(const void *buf, int64_t bytes, int32_t pattern, int32_t unroll,
+                          int32_t blocks, int32_t threads_per_block, uint32_t *out, hipStream_t stream) {
+    if (!buf || !out) return QG_ERR_NULL_POINTER;
+    if (bytes < 16 || bytes % 16) return QG_ERR_BAD_SHAPE;
+    if (pattern < 0 || pattern > 5) return QG_ERR_BAD_SHAPE;
+    if (pattern % 3 == 2 && unroll < 2) return QG_ERR_BAD_SHAPE;
+    if (blocks < 1 || threads_per_block < 64 || threads_per_block > 1024 || threads_per_block % 64)
+        return QG_ERR_BAD_SHAPE;
+    if (!aligned(buf, 16) || !aligned(out, 4)) return QG_ERR_MISALIGNED;
+    const auto *b = static_cast<const uint4 *>(buf);
+    const int64_t units = bytes / 16;
+    const dim3 g(blocks), t(threads_per_block);
+    switch (unroll) {
+        case 1: hipLaunchKernelGGL(qg::stream_probe_kernel<1>, g, t, 0, stream, b, units, pattern, out); break;
+        case 2: hipLaunchKernelGGL(qg::stream_probe_kernel<2>, g, t, 0, stream, b, units, pattern, out); break;
+        case 4: hipLaunchKernelGGL(qg::stream_probe_kernel<4>, g, t, 0, stream, b, units, pattern, out); break;
+        case 8: hipLaunchKernelGGL(qg::stream_probe_kernel<8>, g, t, 0, stream, b, units, pattern, out); break;
+        case 16: hipLaunchKernelGGL(qg::stream_probe_kernel<16>, g, t, 0, stream, b, units, pattern, out); break;
+        default: return QG_ERR_BAD_SHAPE;
+    }
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
 int64_t qg_max_k(qg_format format, int32_t batch) {
     if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_FP8_E4M3) return 0;
     if (batch < 1 || batch > 4) return 0;
     const FmtInfo fi = fmt_info(format);
     const int64_t per_chunk = int64_t(batch) * (fi.pieces * 16 + (fi.sums ? 4 : 0));
-    return (kMaxLds / per_chunk) * fi.wpc;
+    return ((kMaxLds - qg::kLdsSink) / per_chunk) * fi.wpc;
 }
 
 }  // extern "C"

@@ -194,6 +194,26 @@ int qg_abi_version(void);
 int64_t qg_max_k(qg_format format, int32_t batch);
 
 /* ------------------------------------------------------------------------
+ * Measurement
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Stream probe: reads `bytes` bytes of `buf` with 16-byte coalesced loads per
+ * lane (`unroll` in {1,2,4,8,16} loads in flight per lane) and writes one xor
+ * of what each thread read to out[blocks * threads_per_block] (DEVICE).  It is
+ * the reference for the achievable HBM read bandwidth that the matvec is
+ * compared with: the Part 2 post ("What we'd tell the next person") proves a
+ * streaming kernel's ceiling with a same-run reference kernel.
+ *   pattern 0: grid-stride rounds; 1: each wavefront streams its own
+ *   contiguous range; 2: as 1 with each lane reading two adjacent 16-byte
+ *   units (unroll >= 2); 3, 4, 5: patterns 0, 1, 2 with non-temporal loads.
+ * bytes must be a positive multiple of 16; buf 16-byte aligned.
+ */
+qg_status qg_stream_probe(const void *buf, int64_t bytes, int32_t pattern, int32_t unroll,
+                          int32_t blocks, int32_t threads_per_block, uint32_t *out,
+                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Host pack/layout module.  HOST pointers; the caller allocates every output.
  * These produce the packed layouts the device entry points read.  The
  * arithmetic is float64 with one rounding per operation (see the quantizer
