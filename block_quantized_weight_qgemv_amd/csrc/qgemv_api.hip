@@ -1,5 +1,5 @@
 // C ABI of the block-quantized weight matvec: argument validation, launch
-// planning and dispatch to the kernel template in qgemv_device.hpp.
+// planning and dispatch to the kernel templates in qgemv_kernels.hpp.
 //
 // Validation runs completely before any HIP call, so a bad argument never
 // launches anything and never touches y.  The only state kept across calls is
@@ -7,7 +7,7 @@
 // have had their LDS limit raised; both are filled once, thread-safely.
 
 #include "qgemv.h"
-#include "qgemv_device.hpp"
+#include "qgemv_kernels.hpp"
 #include "stream_probe.hpp"
 
 #include <atomic>
@@ -38,7 +38,7 @@ FmtInfo fmt_info(qg_format f) {
     }
 }
 
-// must equal qg::Kernel<...>::lds_bytes
+// must equal qg::LdsKernel<...>::lds_bytes
 int64_t lds_bytes(qg_format f, int64_t k, int32_t batch) {
     const FmtInfo fi = fmt_info(f);
     const int64_t chunks = k / fi.wpc;
@@ -102,19 +102,37 @@ struct Plan {
     int rows_per_tile;
     int waves_per_block;
     int blocks;
+    bool row_kernel;       // x in registers (short rows) or staged in LDS
+    int passes;            // row kernel: passes per row (1, 2 or 4)
 };
 
-Plan default_plan(qg_format f, int64_t n, int64_t k, int32_t batch, int cus) {
+int passes_of(int64_t chunks) { return int((chunks + qg::kWave - 1) / qg::kWave); }
+
+// The row kernel holds the wave's slice of x in registers (at most 16
+// pieces per lane) and one dword of each group-parameter array per lane (an
+// even number of groups, at most 128, on 4-byte aligned rows).
+bool row_kernel_fits(qg_format f, const Params &p, int32_t batch) {
     const FmtInfo fi = fmt_info(f);
-    const int64_t chunks = k / fi.wpc;
-    const int64_t passes = (chunks + qg::kWave - 1) / qg::kWave;
+    const int j = passes_of(p.chunks);
+    if (j != 1 && j != 2 && j != 4) return false;
+    if (int64_t(batch) * j * fi.pieces > 16) return false;
+    if (f != QG_FMT_FP8_E4M3) {
+        if (p.groups < 2 || p.groups % 2 || p.groups > 128) return false;
+        if (!aligned(p.scales, 4)) return false;
+        if (f != QG_FMT_FP4_E2M1 && !aligned(p.biases, 4)) return false;
+    }
+    return true;
+}
+
+Plan default_plan(qg_format f, const Params &p, int32_t batch, int cus) {
     Plan pl;
-    pl.rows_per_tile = passes >= 4 ? 1 : (passes >= 2 ? 2 : 4);
-    (void)batch;
-    pl.waves_per_block = 4;
-    const int64_t waves_per_cu = 16;
+    pl.row_kernel = row_kernel_fits(f, p, batch);
+    pl.passes = passes_of(p.chunks);
+    pl.rows_per_tile = 2;
+    pl.waves_per_block = 8;
+    const int64_t waves_per_cu = 8;
     int64_t blocks = int64_t(cus) * waves_per_cu / pl.waves_per_block;
-    const int64_t max_blocks = (n + pl.waves_per_block - 1) / pl.waves_per_block;
+    const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
     if (blocks > max_blocks) blocks = max_blocks;
     pl.blocks = int(blocks < 1 ? 1 : blocks);
     return pl;
@@ -122,28 +140,62 @@ Plan default_plan(qg_format f, int64_t n, int64_t k, int32_t batch, int cus) {
 
 // ---------------------------------------------------------------- dispatch
 
-template <class Fmt, int R, int B>
-qg_status launch_inst(const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
-    constexpr int D = R == 1 ? 8 : 4;
-    auto kern = qg::qgemv_kernel<Fmt, R, B, D>;
-    static std::once_flag attr_once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(attr_once, [&] {
-        attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
-    });
-    if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
+template <class Kern>
+qg_status launch(Kern kern, const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
+    if (lds > 64 * 1024) {
+        static std::once_flag attr_once;
+        static hipError_t attr_err = hipSuccess;
+        std::call_once(attr_once, [&] {
+            attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+        });
+        if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
+    }
     hipLaunchKernelGGL(kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+// prefetch depth: about 8 code loads in flight per lane
+constexpr int row_depth(int r, int j) { return 8 / (r * j) > 2 ? 8 / (r * j) : 2; }
+constexpr int lds_depth(int r) { return r == 1 ? 8 : 4; }
+
+template <class Fmt, int R, int B, int J>
+constexpr bool row_instance() {
+    return B * J * Fmt::kPieces <= 16 && !(R == 4 && J == 4);
+}
+
+template <class Fmt, int R, int B>
+qg_status launch_row_j(const Params &p, const Plan &pl, hipStream_t s) {
+    switch (pl.passes) {
+        case 1:
+            if constexpr (row_instance<Fmt, R, B, 1>())
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1), 1>, p, pl, 0, s);
+            break;
+        case 2:
+            if constexpr (row_instance<Fmt, R, B, 2>())
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2), 2>, p, pl, 0, s);
+            break;
+        case 4:
+            if constexpr (row_instance<Fmt, R, B, 4>())
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4), 4>, p, pl, 0, s);
+            break;
+    }
+    return QG_ERR_LAUNCH;     // not reached: the host only picks existing instances
+}
+
+template <class Fmt, int R, int B>
+qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
+    if (pl.row_kernel) return launch_row_j<Fmt, R, B>(p, pl, s);
+    return launch(qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R)>, p, pl, lds, s);
 }
 
 template <class Fmt, int R>
 qg_status launch_r(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
     switch (batch) {
-        case 1: return launch_inst<Fmt, R, 1>(p, pl, lds, s);
-        case 2: return launch_inst<Fmt, R, 2>(p, pl, lds, s);
-        case 3: return launch_inst<Fmt, R, 3>(p, pl, lds, s);
-        default: return launch_inst<Fmt, R, 4>(p, pl, lds, s);
+        case 1: return launch_rb<Fmt, R, 1>(p, pl, lds, s);
+        case 2: return launch_rb<Fmt, R, 2>(p, pl, lds, s);
+        case 3: return launch_rb<Fmt, R, 3>(p, pl, lds, s);
+        default: return launch_rb<Fmt, R, 4>(p, pl, lds, s);
     }
 }
 
@@ -169,19 +221,21 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
-    Plan pl = default_plan(f, p.n, p.k, batch, cus);
+    Plan pl = default_plan(f, p, batch, cus);
     if (override_plan) {
         if (override_plan->rows_per_tile) pl.rows_per_tile = override_plan->rows_per_tile;
         if (override_plan->waves_per_block) pl.waves_per_block = override_plan->waves_per_block;
         if (override_plan->blocks) pl.blocks = override_plan->blocks;
         else {
             const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
-            int64_t b = int64_t(cus) * 16 / pl.waves_per_block;
+            int64_t b = int64_t(cus) * 8 / pl.waves_per_block;
             pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
         }
     }
+    // four passes per row allow at most two rows per tile in the row kernel
+    if (pl.row_kernel && pl.passes == 4 && pl.rows_per_tile > 2) pl.rows_per_tile = 2;
     p.total_waves = pl.blocks * pl.waves_per_block;
-    const int64_t lds = lds_bytes(f, p.k, batch);
+    const int64_t lds = pl.row_kernel ? 0 : lds_bytes(f, p.k, batch);
     switch (f) {
         case QG_FMT_FP4_E2M1: return launch_fmt<qg::FmtFP4>(p, pl, batch, lds, stream);
         case QG_FMT_AFFINE_U4: return launch_fmt<qg::FmtAffineU4>(p, pl, batch, lds, stream);
@@ -305,8 +359,13 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
-    Plan pl = default_plan(format, n, k, batch, cus);
-    out->rows_per_tile = pl.rows_per_tile;
+    // the default group size of the format, aligned parameter arrays
+    Params p = base_params(format, nullptr, nullptr, nullptr, n, k, QG_OUT_F32);
+    const int gs = format == QG_FMT_FP4_E2M1 ? 32 : (format == QG_FMT_FP8_E4M3 ? 0 : 64);
+    p.groups = gs ? int32_t(k / gs) : 0;
+    p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));
+    Plan pl = default_plan(format, p, batch, cus);
+    out->rows_per_tile = (pl.row_kernel && pl.passes == 4 && pl.rows_per_tile > 2) ? 2 : pl.rows_per_tile;
     out->waves_per_block = pl.waves_per_block;
     out->blocks = pl.blocks;
     return QG_OK;

@@ -1,0 +1,216 @@
+// Shared device helpers of the block-quantized weight matvec (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kWave = 64;
+constexpr int kChunkBytes = 16;
+constexpr int kLdsSink = 32;      // LDS bytes after the staged activations
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+struct Params {
+    const unsigned char *codes;     // packed code rows, row_bytes each
+    const uint16_t *scales;         // bf16 [n, groups]   (FP4, affine)
+    const uint16_t *biases;         // bf16 [n, groups]   (affine)
+    const float *row_scale;         // f32 [n]            (FP8)
+    const uint16_t *x;              // bf16 [B, k]
+    void *y;                        // f32 or bf16 [B, n]
+    int64_t n;
+    int64_t row_bytes;              // bytes of one code row (= 16 * chunks)
+    int32_t k;
+    int32_t chunks;                 // 16-byte chunks per code row
+    int32_t passes;                 // ceil(chunks / 64)
+    int32_t groups;                 // scale groups per row
+    int32_t group_shift;            // chunk index >> group_shift = group index
+    int32_t total_waves;            // waves in the grid
+    int32_t out_bf16;               // 0: f32 output, 1: bf16 output
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;     // NaN stays NaN
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float dot2_bf16(bf16x2_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Weight codes and scales are read exactly once: non-temporal loads keep them
+// from displacing the activations and the other rows' lines in the caches
+// (a plain read stream reaches 7.1 TB/s with them, 6.4 TB/s without).
+__device__ __forceinline__ uint4 load_code_chunk(const unsigned char *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t load_param(const uint16_t *p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ uint32_t load_param_pair(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
+}
+
+// Activations are shared by every wave: ordinary cached loads.
+__device__ __forceinline__ uint4 load_x_unit(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Value of lane `src` of v (every lane must be active).
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
+    return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
+}
+
+constexpr int pow2_ceil(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// ------------------------------------------------------------------ launch geometry
+
+// Workgroups are dispatched round-robin over the 8 XCDs; renumbering them so
+// that the workgroups of one XCD own neighbouring rows keeps a row range's
+// neighbours (shared scale lines, the activations) in one L2.
+__device__ __forceinline__ int64_t wave_index() {
+    int lblock = blockIdx.x;
+    if ((gridDim.x & 7) == 0) lblock = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    return int64_t(lblock) * (blockDim.x >> 6) + wave_in_block;
+}
+
+// Rows [begin, end) of this wave: the n rows split into total_waves ranges
+// whose sizes differ by at most one.
+__device__ __forceinline__ void wave_rows(const Params &p, int64_t &begin, int64_t &end) {
+    const int64_t w = wave_index();
+    begin = w * p.n / p.total_waves;
+    end = (w + 1) * p.n / p.total_waves;
+}
+
+// ------------------------------------------------------------------ reduction
+
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), Ctrl, 0xF, 0xF, false));
+}
+
+// Sum every lane's V partials over the wave (V a power of two).  Step A adds
+// lanes l and l^32 (when V >= 2 the two halves of the wave keep different
+// halves of the values), step B adds l and l^16 the same way, then a 16-lane
+// row is summed by DPP rotations.  Afterwards the first lane of each 16-lane
+// row holds kCnt = max(V/4, 1) totals.  The tree of additions a value sees
+// does not depend on V, so a value's bits are the same whatever tile shape or
+// batch carried it.  Must run with all 64 lanes active.
+template <int V>
+struct WaveSum {
+    static_assert((V & (V - 1)) == 0, "WaveSum needs a power-of-two count");
+    static constexpr bool kSplitA = V >= 2;
+    static constexpr int kAfterA = kSplitA ? V / 2 : 1;
+    static constexpr bool kSplitB = kAfterA >= 2;
+    static constexpr int kCnt = kSplitB ? kAfterA / 2 : 1;
+
+    __device__ static __forceinline__ void run(float (&v)[V]) {
+        if constexpr (kSplitA) {
+#pragma unroll
+            for (int i = 0; i < V / 2; ++i) {
+                swap32(v[i], v[i + V / 2]);
+                v[i] = v[i] + v[i + V / 2];
+            }
+        } else {
+            float a = v[0], b = v[0];
+            swap32(a, b);
+            v[0] = a + b;
+        }
+        if constexpr (kSplitB) {
+#pragma unroll
+            for (int i = 0; i < kAfterA / 2; ++i) {
+                swap16(v[i], v[i + kAfterA / 2]);
+                v[i] = v[i] + v[i + kAfterA / 2];
+            }
+        } else {
+            float a = v[0], b = v[0];
+            swap16(a, b);
+            v[0] = a + b;
+        }
+#pragma unroll
+        for (int i = 0; i < kCnt; ++i) {
+            float t = v[i];
+            t = t + dpp_f<0x128>(t);    // row_ror:8
+            t = t + dpp_f<0x124>(t);    // row_ror:4
+            t = t + dpp_f<0x122>(t);    // row_ror:2
+            t = t + dpp_f<0x121>(t);    // row_ror:1
+            v[i] = t;
+        }
+    }
+
+    // Does this lane write totals, and which value index does slot q hold?
+    __device__ static __forceinline__ bool writer(int lane) {
+        if (lane & 15) return false;
+        if (!kSplitA && (lane & 32)) return false;
+        if (!kSplitB && (lane & 16)) return false;
+        return true;
+    }
+    __device__ static __forceinline__ int value_index(int lane, int q) {
+        int idx = q;
+        if constexpr (kSplitB) idx += ((lane >> 4) & 1) * kCnt;
+        if constexpr (kSplitA) idx += ((lane >> 5) & 1) * (kSplitB ? 2 * kCnt : kCnt);
+        return idx;
+    }
+};
+
+// Reduce a tile's R x B accumulators over the wave and write the R rows of y
+// (rows at or past row_end are skipped).  rs(i) is the scale applied to row i
+// (1 unless the format has per-row scales).  Zeroes acc.
+template <int R, int B, class RowScale>
+__device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B], int64_t row0, int64_t row_end,
+                                             int lane, RowScale rs) {
+    constexpr int V = R * B;
+    constexpr int VP = pow2_ceil(V);
+    using Red = WaveSum<VP>;
+    float v[VP];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            v[i * B + b] = acc[i][b];
+            acc[i][b] = 0.0f;
+        }
+#pragma unroll
+    for (int i = V; i < VP; ++i) v[i] = 0.0f;
+    Red::run(v);
+    if (Red::writer(lane)) {
+#pragma unroll
+        for (int q = 0; q < Red::kCnt; ++q) {
+            const int idx = Red::value_index(lane, q);
+            const int i = idx / B, b = idx % B;
+            const int64_t row = row0 + i;
+            if (idx < V && row < row_end) {
+                const float out = v[q] * rs(i);
+                if (p.out_bf16)
+                    reinterpret_cast<uint16_t *>(p.y)[int64_t(b) * p.n + row] =
+                        static_cast<uint16_t>(f32_to_bf16_rne(out));
+                else
+                    reinterpret_cast<float *>(p.y)[int64_t(b) * p.n + row] = out;
+            }
+        }
+    }
+}
+
+}  // namespace qg

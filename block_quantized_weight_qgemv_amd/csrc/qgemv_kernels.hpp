@@ -1,0 +1,345 @@
+// The block-quantized weight matvec kernels for gfx950 (MI355X).
+//
+// Both kernels stream packed weight rows with the same structure:
+//
+//  * Row ranges per wavefront.  Rows [0, n) are split into one contiguous
+//    range per wavefront (sizes differ by at most one row); workgroups are
+//    renumbered so that one XCD's workgroups own neighbouring ranges.  A wave
+//    walks its range R rows (a tile) at a time.
+//  * 16-byte chunks.  Lane l owns chunks l, l+64, l+128, ... of every row
+//    ("pass" j covers chunks 64j .. 64j+63), so every load instruction of a
+//    wave reads 1 KiB of consecutive bytes.
+//  * Prefetch.  The loads of step s+D are issued as soon as step s has been
+//    consumed, so D steps of codes and scales are always in flight.  The loads
+//    are issued unconditionally (clamped to valid addresses) so the compiler's
+//    wait before a step waits for that step's loads only.
+//  * Decode in registers with the gfx950 conversion instructions, a raw dot
+//    per chunk, one multiply-add per chunk for the group scale (plus the bias
+//    times the chunk's activation sum for affine), see qgemv_formats.hpp.
+//  * One wave reduction per tile (permlane swaps and DPP), then y is written.
+//
+// qgemv_row_kernel (rows of at most 4 passes): one step is a whole tile, the
+//    wave's slice of x lives in registers (no LDS, no barrier), and a row's
+//    group parameters arrive as one coalesced dword per lane, handed to the
+//    lane that needs them with ds_bpermute.
+// qgemv_lds_kernel (longer rows): one step is one pass of a tile, x (and its
+//    per-chunk sums) is staged once per workgroup in LDS, and each lane loads
+//    its own group parameter.
+#pragma once
+
+#include "qgemv_common.hpp"
+#include "qgemv_formats.hpp"
+
+namespace qg {
+
+// Consume steps [0, steps) in order from D rotating buffers that the caller
+// has filled with steps 0..D-1.  In the main loop the loads of step s + D go
+// out right after step s is consumed, unconditionally; the last (at most
+// 2D - 1) steps drain without issuing past the end.
+template <int D, class Buf, class Issue, class Consume>
+__device__ __forceinline__ void run_pipeline(Buf (&buf)[D], int steps, Issue &&issue, Consume &&consume) {
+    int s0 = 0;
+    for (; s0 + 2 * D <= steps; s0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(buf[d], s0 + d);
+            issue(buf[d], s0 + d + D);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+        if (s0 + d < steps) consume(buf[d], s0 + d);
+        if (s0 + d + D < steps) issue(buf[d], s0 + d + D);
+    }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (s0 + D + d < steps) consume(buf[d], s0 + D + d);
+}
+
+// ------------------------------------------------------------------ short rows
+
+template <class Fmt, int R, int B, int D, int J>
+struct RowKernel {
+    static constexpr int NA = Fmt::kAuxArrays > 0 ? Fmt::kAuxArrays : 1;
+    struct Buf {
+        uint4 c[R][J];
+        uint32_t a[R][NA];     // this lane's dword of each row's parameter arrays
+        float rs[R];
+    };
+};
+
+template <class Fmt, int R, int B, int D, int J>
+__global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
+    using K = RowKernel<Fmt, R, B, D, J>;
+    using Buf = typename K::Buf;
+    const int lane = threadIdx.x & (kWave - 1);
+    int64_t r_begin, r_end;
+    wave_rows(p, r_begin, r_end);
+    const int tiles = int((r_end - r_begin + R - 1) / R);
+    const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
+    const int C = p.chunks;
+
+    // this lane's activation chunks, one per pass (loaded before the weights)
+    uint4 xraw[B][J][Fmt::kRawUnits];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int c = min(kWave * j + lane, C - 1);
+            const uint16_t *xc = p.x + int64_t(b) * p.k + c * Fmt::kWpc;
+#pragma unroll
+            for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = load_x_unit(xc + 8 * u);
+        }
+
+    // the lane's dword of a row's parameters: elements 2m, 2m+1 (the host
+    // guarantees an even number of groups, at most 128, 4-byte aligned rows)
+    const int aux_off = 2 * min(lane, p.groups / 2 - 1);
+    auto issue = [&](Buf &bf, int t) {
+        const int64_t row0 = r_begin + int64_t(t) * R;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t row = min(row0 + i, row_hi);
+            const unsigned char *rp = p.codes + row * p.row_bytes;      // uniform
+#pragma unroll
+            for (int j = 0; j < J; ++j) bf.c[i][j] = load_code_chunk(rp + uint32_t(min(kWave * j + lane, C - 1)) * kChunkBytes);
+            if constexpr (Fmt::kAuxArrays >= 1) bf.a[i][0] = load_param_pair(p.scales + row * p.groups + aux_off);
+            if constexpr (Fmt::kAuxArrays >= 2) bf.a[i][1] = load_param_pair(p.biases + row * p.groups + aux_off);
+            if constexpr (Fmt::kRowScale) bf.rs[i] = p.row_scale[row];
+        }
+    };
+
+    Buf buf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, tiles - 1)));
+
+    // activation pieces (and chunk sums) in registers
+    uint4 xp[B][J][Fmt::kPieces];
+    float xs[B][J];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+#pragma unroll
+            for (int u = 0; u < Fmt::kRawUnits; ++u) {
+                uint4 pc[Fmt::kPpu];
+                Fmt::unit_pieces(xraw[b][j][u], pc);
+#pragma unroll
+                for (int m = 0; m < Fmt::kPpu; ++m) xp[b][j][u * Fmt::kPpu + m] = pc[m];
+            }
+            xs[b][j] = Fmt::kSums ? chunk_sum(xraw[b][j]) : 0.0f;
+        }
+
+    float acc[R][B];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+
+    auto consume = [&](const Buf &bf, int t) {
+        const int64_t row0 = r_begin + int64_t(t) * R;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            // group parameters of this lane's chunk in every pass
+            float sv[J], bv[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int e = (kWave * j + lane) >> p.group_shift;     // group index in the row
+                const int src = (e >> 1) & (kWave - 1);
+                const bool hi = e & 1;
+                sv[j] = bv[j] = 0.0f;
+                if constexpr (Fmt::kAuxArrays >= 1) {
+                    const uint32_t v = lane_read(bf.a[i][0], src);
+                    sv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                }
+                if constexpr (Fmt::kAuxArrays >= 2) {
+                    const uint32_t v = lane_read(bf.a[i][1], src);
+                    bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                }
+            }
+            if (row0 + i < r_end) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    if (kWave * j + lane < C) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            const float raw = Fmt::dot(bf.c[i][j], xp[b][j], 0.0f);
+                            acc[i][b] = Fmt::fold(acc[i][b], raw, sv[j], bv[j], xs[b][j]);
+                        }
+                    }
+                }
+            }
+        }
+        reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
+            float rs = 1.0f;
+            if constexpr (Fmt::kRowScale) {
+                rs = bf.rs[0];
+#pragma unroll
+                for (int ii = 1; ii < R; ++ii)
+                    if (i == ii) rs = bf.rs[ii];
+            }
+            return rs;
+        });
+    };
+
+    run_pipeline<D>(buf, tiles, issue, consume);
+}
+
+// ------------------------------------------------------------------ long rows
+
+template <class Fmt, int R, int B, int D>
+struct LdsKernel {
+    static constexpr int NA = Fmt::kAuxArrays > 0 ? Fmt::kAuxArrays : 1;
+    struct Buf {
+        uint4 c[R];
+        uint32_t a[R][NA];     // this lane's group parameter of each row
+        float rs[R];
+    };
+    // bytes of dynamic LDS: activation pieces, per-chunk sums, and a 32-byte
+    // sink for the stores of out-of-range staging lanes
+    __host__ __device__ static constexpr int64_t lds_bytes(int chunks) {
+        return int64_t(B) * Fmt::kPieces * chunks * 16 + (Fmt::kSums ? int64_t(B) * chunks * 4 : 0) + kLdsSink;
+    }
+};
+
+template <class Fmt, int R, int B, int D>
+__global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    using Buf = typename LdsKernel<Fmt, R, B, D>::Buf;
+    const int lane = threadIdx.x & (kWave - 1);
+    int64_t r_begin, r_end;
+    wave_rows(p, r_begin, r_end);
+    const int tiles = int((r_end - r_begin + R - 1) / R);
+    const int passes = p.passes;
+    const int steps = tiles * passes;
+    const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
+    const int chunks = p.chunks;
+    const int last_chunk = chunks - 1;
+
+    auto issue = [&](Buf &b, int s) {
+        const int t = s / passes;
+        const int j = s - t * passes;
+        const int c = min(lane + kWave * j, last_chunk);
+        const uint32_t lane_off = uint32_t(c) * kChunkBytes;
+        const int64_t row0 = r_begin + int64_t(t) * R;
+        const int g = c >> p.group_shift;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t row = min(row0 + i, row_hi);
+            b.c[i] = load_code_chunk(p.codes + row * p.row_bytes + lane_off);
+            if constexpr (Fmt::kAuxArrays >= 1) b.a[i][0] = load_param(p.scales + row * p.groups + g);
+            if constexpr (Fmt::kAuxArrays >= 2) b.a[i][1] = load_param(p.biases + row * p.groups + g);
+            if constexpr (Fmt::kRowScale) b.rs[i] = p.row_scale[row];
+        }
+    };
+
+    // ---- activations into LDS, overlapped with the weight prefetch.  Each
+    // thread first loads up to kXU activation units, then the prefetch is
+    // issued, and only then are the units used: the vector-load counter
+    // retires in order, so waiting for them does not wait for the weights.
+    uint4 *xs = reinterpret_cast<uint4 *>(smem);
+    float *xsum = reinterpret_cast<float *>(smem + int64_t(B) * Fmt::kPieces * chunks * 16);
+    unsigned char *sink_base = smem + int64_t(B) * Fmt::kPieces * chunks * 16 +
+                               (Fmt::kSums ? int64_t(B) * chunks * 4 : 0);
+    uint4 *sink = reinterpret_cast<uint4 *>(sink_base);
+    float *sink_f = reinterpret_cast<float *>(sink_base + 16);
+    const int units_per_row = p.k / 8;
+    const int x_units = B * units_per_row;
+    auto x_unit = [&](int u) -> uint4 {
+        const int b = u / units_per_row;
+        return load_x_unit(p.x + int64_t(b) * p.k + (u - b * units_per_row) * 8);
+    };
+    // Every lane runs the same staging code and stores unconditionally (an
+    // out-of-range unit is clamped to the last one and stored to the sink),
+    // so no activation load is sunk into a conditional block below the
+    // prefetch.
+    auto stage_unit = [&](int u_in, const uint4 v) {
+        const bool st = u_in < x_units;
+        const int u = st ? u_in : x_units - 1;
+        const int b = u / units_per_row;
+        const int e = (u - b * units_per_row) * 8;
+        const int c = e / Fmt::kWpc, ru = (e % Fmt::kWpc) / 8;
+        uint4 pc[Fmt::kPpu];
+        Fmt::unit_pieces(v, pc);
+#pragma unroll
+        for (int m = 0; m < Fmt::kPpu; ++m)
+            *(st ? &xs[(b * Fmt::kPieces + ru * Fmt::kPpu + m) * chunks + c] : sink) = pc[m];
+        if constexpr (Fmt::kSums) {
+            float sm = unit_sum(v);
+            // the units of one chunk sit in consecutive lanes (units per row
+            // and the wave width are multiples of the units per chunk); the
+            // tree matches chunk_sum()
+#pragma unroll
+            for (int m = 1; m < Fmt::kRawUnits; m <<= 1) sm += __shfl_xor(sm, m, kWave);
+            *((st && ru == 0) ? &xsum[b * chunks + c] : sink_f) = sm;
+        }
+    };
+    constexpr int kXU = 8;
+    uint4 xr[kXU];
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) xr[i] = x_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
+
+    Buf buf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+
+#pragma unroll
+    for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i]);
+    // activations beyond kXU units per thread; the trip count is the same for
+    // every lane of a wave
+    for (int base = kXU * blockDim.x; base < x_units; base += blockDim.x) {
+        const int u = base + threadIdx.x;
+        stage_unit(u, x_unit(min(u, x_units - 1)));
+    }
+    __syncthreads();
+
+    float acc[R][B];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+
+    auto consume = [&](const Buf &bf, int s) {
+        const int t = s / passes;
+        const int j = s - t * passes;
+        const int c = lane + kWave * j;
+        const int64_t row0 = r_begin + int64_t(t) * R;
+        if (c < chunks) {
+            uint4 xp[B][Fmt::kPieces];
+            float xsv[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+#pragma unroll
+                for (int q = 0; q < Fmt::kPieces; ++q) xp[b][q] = xs[(b * Fmt::kPieces + q) * chunks + c];
+                xsv[b] = Fmt::kSums ? xsum[b * chunks + c] : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                if (row0 + i < r_end) {
+                    const float s_ = Fmt::kAuxArrays >= 1 ? bf16_to_f32(bf.a[i][0]) : 0.0f;
+                    const float b_ = Fmt::kAuxArrays >= 2 ? bf16_to_f32(bf.a[i][LdsKernel<Fmt, R, B, D>::NA - 1]) : 0.0f;
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float raw = Fmt::dot(bf.c[i], xp[b], 0.0f);
+                        acc[i][b] = Fmt::fold(acc[i][b], raw, s_, b_, xsv[b]);
+                    }
+                }
+            }
+        }
+        if (j == passes - 1) {
+            reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
+                float rs = 1.0f;
+                if constexpr (Fmt::kRowScale) {
+                    rs = bf.rs[0];
+#pragma unroll
+                    for (int ii = 1; ii < R; ++ii)
+                        if (i == ii) rs = bf.rs[ii];
+                }
+                return rs;
+            });
+        }
+    };
+
+    run_pipeline<D>(buf, steps, issue, consume);
+}
+
+}  // namespace qg
