@@ -102,34 +102,70 @@ struct Plan {
     int rows_per_tile;
     int waves_per_block;
     int blocks;
-    bool row_kernel;       // x in registers (short rows) or staged in LDS
-    int passes;            // row kernel: passes per row (1, 2 or 4)
+    bool row_kernel;       // x in registers (row kernel) or staged in LDS
+    int passes;            // row kernel: passes per K segment (1, 2 or 4)
 };
 
 int passes_of(int64_t chunks) { return int((chunks + qg::kWave - 1) / qg::kWave); }
 
-// The row kernel holds the wave's slice of x in registers (at most 16
-// pieces per lane) and one dword of each group-parameter array per lane (an
-// even number of groups, at most 128, on 4-byte aligned rows).
-bool row_kernel_fits(qg_format f, const Params &p, int32_t batch) {
+// The row kernel keeps each wave's slice of x in registers: rows are cut into
+// S = 1, 2, 4 or 8 equal K segments of at most two passes (four for FP8,
+// whose activation pieces are half as wide).  S depends only on the format
+// and k, so every batch size and launch shape adds a row's terms in the same
+// order.  A segment's group parameters must be one dword per lane: an even
+// number of groups, at most 128, on a group boundary, on 4-byte aligned rows.
+struct Split {
+    int segs, seg_chunks, seg_groups, passes;
+    bool ok;
+};
+
+Split split_of(qg_format f, const Params &p) {
     const FmtInfo fi = fmt_info(f);
-    const int j = passes_of(p.chunks);
-    if (j != 1 && j != 2 && j != 4) return false;
-    if (int64_t(batch) * j * fi.pieces > 16) return false;
+    Split sp{1, p.chunks, p.groups, 0, false};
+    const int jmax = fi.pieces >= 4 ? 2 : 4;
+    int need = int((p.chunks + 64 * jmax - 1) / (64 * jmax));
+    int segs = 1;
+    while (segs < need) segs <<= 1;
+    if (segs > 8 || p.chunks % segs) return sp;
+    sp.segs = segs;
+    sp.seg_chunks = p.chunks / segs;
+    sp.passes = passes_of(sp.seg_chunks);
+    if (sp.passes != 1 && sp.passes != 2 && sp.passes != 4) return sp;
     if (f != QG_FMT_FP8_E4M3) {
-        if (p.groups < 2 || p.groups % 2 || p.groups > 128) return false;
+        if (p.groups % segs) return sp;
+        sp.seg_groups = p.groups / segs;
+        if ((int64_t(sp.seg_chunks) << 0) % (int64_t(1) << p.group_shift)) return sp;
+        if (sp.seg_groups < 2 || sp.seg_groups % 2 || sp.seg_groups > 128) return sp;
+    } else {
+        sp.seg_groups = 0;
+    }
+    sp.ok = true;
+    return sp;
+}
+
+bool row_kernel_fits(qg_format f, const Params &p, int32_t batch) {
+    if (!p.segs) return false;
+    const FmtInfo fi = fmt_info(f);
+    if (int64_t(batch) * p.passes * fi.pieces > 32) return false;
+    if (f != QG_FMT_FP8_E4M3) {
         if (!aligned(p.scales, 4)) return false;
         if (f != QG_FMT_FP4_E2M1 && !aligned(p.biases, 4)) return false;
     }
     return true;
 }
 
+int64_t row_lds_bytes(const Params &p, int blocks, int32_t batch) {
+    if (p.segs <= 1) return 0;
+    const int64_t rows = (p.n + blocks - 1) / blocks;
+    return rows * p.segs * batch * 4;
+}
+
 Plan default_plan(qg_format f, const Params &p, int32_t batch, int cus) {
     Plan pl;
     pl.row_kernel = row_kernel_fits(f, p, batch);
-    pl.passes = passes_of(p.chunks);
+    pl.passes = p.passes;
     pl.rows_per_tile = 2;
-    pl.waves_per_block = 8;
+    pl.waves_per_block = pl.row_kernel && p.segs > 4 ? p.segs : 4;
     const int64_t waves_per_cu = 8;
     int64_t blocks = int64_t(cus) * waves_per_cu / pl.waves_per_block;
     const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
@@ -159,34 +195,43 @@ qg_status launch(Kern kern, const Params &p, const Plan &pl, int64_t lds, hipStr
 constexpr int row_depth(int r, int j) { return 8 / (r * j) > 2 ? 8 / (r * j) : 2; }
 constexpr int lds_depth(int r) { return r == 1 ? 8 : 4; }
 
+// register budget of the row kernel: at most 32 activation pieces per lane,
+// and fewer rows per tile when they are many
 template <class Fmt, int R, int B, int J>
 constexpr bool row_instance() {
-    return B * J * Fmt::kPieces <= 16 && !(R == 4 && J == 4);
+    return B * J * Fmt::kPieces <= 32 && (B * J * Fmt::kPieces <= 16 || R <= 2) && !(R == 4 && J == 4);
 }
 
 template <class Fmt, int R, int B>
-qg_status launch_row_j(const Params &p, const Plan &pl, hipStream_t s) {
+qg_status launch_row_j(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
     switch (pl.passes) {
         case 1:
             if constexpr (row_instance<Fmt, R, B, 1>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1), 1>, p, pl, 0, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1), 1>, p, pl, lds, s);
             break;
         case 2:
             if constexpr (row_instance<Fmt, R, B, 2>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2), 2>, p, pl, 0, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2), 2>, p, pl, lds, s);
             break;
         case 4:
             if constexpr (row_instance<Fmt, R, B, 4>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4), 4>, p, pl, 0, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4), 4>, p, pl, lds, s);
             break;
     }
-    return QG_ERR_LAUNCH;     // not reached: the host only picks existing instances
+    return QG_ERR_LAUNCH;     // not reached: run() only picks existing instances
 }
 
 template <class Fmt, int R, int B>
 qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
-    if (pl.row_kernel) return launch_row_j<Fmt, R, B>(p, pl, s);
+    if (pl.row_kernel) return launch_row_j<Fmt, R, B>(p, pl, lds, s);
     return launch(qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R)>, p, pl, lds, s);
+}
+
+// Whether a row-kernel instance exists for these (R, B, passes).
+template <class Fmt>
+bool row_instance_exists(int r, int b, int j) {
+    const int pcs = Fmt::kPieces;
+    return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= 2) && !(r == 4 && j == 4);
 }
 
 template <class Fmt, int R>
@@ -217,10 +262,29 @@ qg_status check_plan(const qg_plan *plan) {
     return QG_OK;
 }
 
+bool row_instance_for(qg_format f, int r, int b, int j) {
+    switch (f) {
+        case QG_FMT_FP4_E2M1: return row_instance_exists<qg::FmtFP4>(r, b, j);
+        case QG_FMT_AFFINE_U4: return row_instance_exists<qg::FmtAffineU4>(r, b, j);
+        case QG_FMT_AFFINE_U8: return row_instance_exists<qg::FmtAffineU8>(r, b, j);
+        default: return row_instance_exists<qg::FmtFP8>(r, b, j);
+    }
+}
+
 qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream) {
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
+    const Split sp = split_of(f, p);
+    if (sp.ok) {
+        p.segs = sp.segs;
+        p.seg_chunks = sp.seg_chunks;
+        p.seg_groups = sp.seg_groups;
+        p.passes = sp.passes;
+    } else {
+        p.segs = 0;                               // the row kernel does not apply
+        p.passes = passes_of(p.chunks);
+    }
     Plan pl = default_plan(f, p, batch, cus);
     if (override_plan) {
         if (override_plan->rows_per_tile) pl.rows_per_tile = override_plan->rows_per_tile;
@@ -232,10 +296,26 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
             pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
         }
     }
-    // four passes per row allow at most two rows per tile in the row kernel
-    if (pl.row_kernel && pl.passes == 4 && pl.rows_per_tile > 2) pl.rows_per_tile = 2;
+    int64_t lds = 0;
+    if (pl.row_kernel) {
+        // a workgroup holds whole row groups of `segs` waves
+        if (pl.waves_per_block % p.segs) {
+            pl.waves_per_block = (pl.waves_per_block / p.segs + 1) * p.segs;
+            if (pl.waves_per_block > 8) pl.waves_per_block = p.segs;
+        }
+        // fewer rows per tile where the register budget asks for it
+        while (pl.rows_per_tile > 1 && !row_instance_for(f, pl.rows_per_tile, batch, pl.passes))
+            pl.rows_per_tile /= 2;
+        lds = row_lds_bytes(p, pl.blocks, batch);
+        if (lds > kMaxLds) {
+            pl.blocks = int((p.n * p.segs * batch * 4 + kMaxLds - 1) / kMaxLds);
+            lds = row_lds_bytes(p, pl.blocks, batch);
+        }
+    } else {
+        p.passes = passes_of(p.chunks);           // the LDS kernel walks whole rows
+        lds = lds_bytes(f, p.k, batch);
+    }
     p.total_waves = pl.blocks * pl.waves_per_block;
-    const int64_t lds = pl.row_kernel ? 0 : lds_bytes(f, p.k, batch);
     switch (f) {
         case QG_FMT_FP4_E2M1: return launch_fmt<qg::FmtFP4>(p, pl, batch, lds, stream);
         case QG_FMT_AFFINE_U4: return launch_fmt<qg::FmtAffineU4>(p, pl, batch, lds, stream);
@@ -359,13 +439,20 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
-    // the default group size of the format, aligned parameter arrays
+    // the format's usual group size, aligned parameter arrays
     Params p = base_params(format, nullptr, nullptr, nullptr, n, k, QG_OUT_F32);
     const int gs = format == QG_FMT_FP4_E2M1 ? 32 : (format == QG_FMT_FP8_E4M3 ? 0 : 64);
     p.groups = gs ? int32_t(k / gs) : 0;
+    p.group_shift = gs ? log2i(gs / fmt_info(format).wpc) : 0;
     p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));
+    const Split sp = split_of(format, p);
+    p.segs = sp.ok ? sp.segs : 0;
+    p.passes = sp.ok ? sp.passes : passes_of(p.chunks);
     Plan pl = default_plan(format, p, batch, cus);
-    out->rows_per_tile = (pl.row_kernel && pl.passes == 4 && pl.rows_per_tile > 2) ? 2 : pl.rows_per_tile;
+    if (pl.row_kernel)
+        while (pl.rows_per_tile > 1 && !row_instance_for(format, pl.rows_per_tile, batch, pl.passes))
+            pl.rows_per_tile /= 2;
+    out->rows_per_tile = pl.rows_per_tile;
     out->waves_per_block = pl.waves_per_block;
     out->blocks = pl.blocks;
     return QG_OK;

@@ -29,6 +29,9 @@ struct Params {
     int32_t group_shift;            // chunk index >> group_shift = group index
     int32_t total_waves;            // waves in the grid
     int32_t out_bf16;               // 0: f32 output, 1: bf16 output
+    int32_t segs;                   // row kernel: K segments per row (split-K)
+    int32_t seg_chunks;             // row kernel: chunks per segment
+    int32_t seg_groups;             // row kernel: scale groups per segment
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -77,11 +80,16 @@ constexpr int pow2_ceil(int v) {
 // Workgroups are dispatched round-robin over the 8 XCDs; renumbering them so
 // that the workgroups of one XCD own neighbouring rows keeps a row range's
 // neighbours (shared scale lines, the activations) in one L2.
-__device__ __forceinline__ int64_t wave_index() {
+__device__ __forceinline__ int logical_block() {
     int lblock = blockIdx.x;
     if ((gridDim.x & 7) == 0) lblock = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    const int wave_in_block = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    return int64_t(lblock) * (blockDim.x >> 6) + wave_in_block;
+    return lblock;
+}
+
+__device__ __forceinline__ int wave_in_block() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ int64_t wave_index() {
+    return int64_t(logical_block()) * (blockDim.x >> 6) + wave_in_block();
 }
 
 // Rows [begin, end) of this wave: the n rows split into total_waves ranges
@@ -175,12 +183,10 @@ struct WaveSum {
     }
 };
 
-// Reduce a tile's R x B accumulators over the wave and write the R rows of y
-// (rows at or past row_end are skipped).  rs(i) is the scale applied to row i
-// (1 unless the format has per-row scales).  Zeroes acc.
-template <int R, int B, class RowScale>
-__device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B], int64_t row0, int64_t row_end,
-                                             int lane, RowScale rs) {
+// Reduce a tile's R x B accumulators over the wave; the writer lanes get
+// (row i, batch b, total) through emit(i, b, total).  Zeroes acc.
+template <int R, int B, class Emit>
+__device__ __forceinline__ void reduce_tile(float (&acc)[R][B], int lane, Emit emit) {
     constexpr int V = R * B;
     constexpr int VP = pow2_ceil(V);
     using Red = WaveSum<VP>;
@@ -199,18 +205,28 @@ __device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B]
 #pragma unroll
         for (int q = 0; q < Red::kCnt; ++q) {
             const int idx = Red::value_index(lane, q);
-            const int i = idx / B, b = idx % B;
-            const int64_t row = row0 + i;
-            if (idx < V && row < row_end) {
-                const float out = v[q] * rs(i);
-                if (p.out_bf16)
-                    reinterpret_cast<uint16_t *>(p.y)[int64_t(b) * p.n + row] =
-                        static_cast<uint16_t>(f32_to_bf16_rne(out));
-                else
-                    reinterpret_cast<float *>(p.y)[int64_t(b) * p.n + row] = out;
-            }
+            if (idx < V) emit(idx / B, idx % B, v[q]);
         }
     }
+}
+
+__device__ __forceinline__ void store_y(const Params &p, int b, int64_t row, float out) {
+    if (p.out_bf16)
+        reinterpret_cast<uint16_t *>(p.y)[int64_t(b) * p.n + row] = static_cast<uint16_t>(f32_to_bf16_rne(out));
+    else
+        reinterpret_cast<float *>(p.y)[int64_t(b) * p.n + row] = out;
+}
+
+// Reduce a tile's R x B accumulators over the wave and write the R rows of y
+// (rows at or past row_end are skipped).  rs(i) is the scale applied to row i
+// (1 unless the format has per-row scales).  Zeroes acc.
+template <int R, int B, class RowScale>
+__device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B], int64_t row0, int64_t row_end,
+                                             int lane, RowScale rs) {
+    reduce_tile<R, B>(acc, lane, [&](int i, int b, float total) {
+        const int64_t row = row0 + i;
+        if (row < row_end) store_y(p, b, row, total * rs(i));
+    });
 }
 
 }  // namespace qg

@@ -18,13 +18,15 @@
 //    times the chunk's activation sum for affine), see qgemv_formats.hpp.
 //  * One wave reduction per tile (permlane swaps and DPP), then y is written.
 //
-// qgemv_row_kernel (rows of at most 4 passes): one step is a whole tile, the
-//    wave's slice of x lives in registers (no LDS, no barrier), and a row's
-//    group parameters arrive as one coalesced dword per lane, handed to the
-//    lane that needs them with ds_bpermute.
-// qgemv_lds_kernel (longer rows): one step is one pass of a tile, x (and its
-//    per-chunk sums) is staged once per workgroup in LDS, and each lane loads
-//    its own group parameter.
+// qgemv_row_kernel: one step is a whole tile, the wave's slice of x lives in
+//    registers (no LDS staging, no barrier), and a row's group parameters
+//    arrive as one coalesced dword per lane, handed to the lane that needs
+//    them with ds_bpermute.  Rows longer than a few passes are cut into K
+//    segments streamed by the waves of one workgroup (split-K); the segment
+//    sums meet in LDS once, at the end.
+// qgemv_lds_kernel (any shape the row kernel does not take): one step is one
+//    pass of a tile, x (and its per-chunk sums) is staged once per workgroup
+//    in LDS, and each lane loads its own group parameter.
 #pragma once
 
 #include "qgemv_common.hpp"
@@ -72,12 +74,27 @@ template <class Fmt, int R, int B, int D, int J>
 __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     using K = RowKernel<Fmt, R, B, D, J>;
     using Buf = typename K::Buf;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
-    int64_t r_begin, r_end;
-    wave_rows(p, r_begin, r_end);
+
+    // Rows are split into one contiguous range per workgroup.  A workgroup's
+    // waves form row groups of `segs` waves; the waves of a row group stream
+    // the same rows, each its own segment of the K dimension (split-K), and
+    // their partial sums are added through LDS at the end.
+    const int S = p.segs;
+    const int nb = gridDim.x;
+    const int64_t blk = logical_block();
+    const int64_t b_begin = blk * p.n / nb, b_end = (blk + 1) * p.n / nb;
+    const int w = wave_in_block();
+    const int groups_in_block = (blockDim.x >> 6) / S;
+    const int rg = w / S, seg = w - rg * S;
+    const int64_t b_rows = b_end - b_begin;
+    const int64_t r_begin = b_begin + rg * b_rows / groups_in_block;
+    const int64_t r_end = b_begin + (rg + 1) * b_rows / groups_in_block;
     const int tiles = int((r_end - r_begin + R - 1) / R);
     const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
-    const int C = p.chunks;
+    const int c_lo = seg * p.seg_chunks;
+    const int c_hi = min(p.chunks, c_lo + p.seg_chunks);
 
     // this lane's activation chunks, one per pass (loaded before the weights)
     uint4 xraw[B][J][Fmt::kRawUnits];
@@ -85,15 +102,17 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     for (int b = 0; b < B; ++b)
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int c = min(kWave * j + lane, C - 1);
+            const int c = min(c_lo + kWave * j + lane, c_hi - 1);
             const uint16_t *xc = p.x + int64_t(b) * p.k + c * Fmt::kWpc;
 #pragma unroll
             for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = load_x_unit(xc + 8 * u);
         }
 
-    // the lane's dword of a row's parameters: elements 2m, 2m+1 (the host
-    // guarantees an even number of groups, at most 128, 4-byte aligned rows)
-    const int aux_off = 2 * min(lane, p.groups / 2 - 1);
+    // the lane's dword of a row segment's parameters: elements 2m, 2m+1 of the
+    // segment (the host guarantees an even number of groups per segment, at
+    // most 128, starting on 4-byte boundaries)
+    const int g_lo = seg * p.seg_groups;
+    const int aux_off = g_lo + 2 * min(lane, p.seg_groups / 2 - 1);
     auto issue = [&](Buf &bf, int t) {
         const int64_t row0 = r_begin + int64_t(t) * R;
 #pragma unroll
@@ -101,7 +120,8 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             const int64_t row = min(row0 + i, row_hi);
             const unsigned char *rp = p.codes + row * p.row_bytes;      // uniform
 #pragma unroll
-            for (int j = 0; j < J; ++j) bf.c[i][j] = load_code_chunk(rp + uint32_t(min(kWave * j + lane, C - 1)) * kChunkBytes);
+            for (int j = 0; j < J; ++j)
+                bf.c[i][j] = load_code_chunk(rp + uint32_t(min(c_lo + kWave * j + lane, c_hi - 1)) * kChunkBytes);
             if constexpr (Fmt::kAuxArrays >= 1) bf.a[i][0] = load_param_pair(p.scales + row * p.groups + aux_off);
             if constexpr (Fmt::kAuxArrays >= 2) bf.a[i][1] = load_param_pair(p.biases + row * p.groups + aux_off);
             if constexpr (Fmt::kRowScale) bf.rs[i] = p.row_scale[row];
@@ -135,6 +155,9 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
 
+    // split-K partials of the workgroup's rows: [row - b_begin][seg][b]
+    float *part = reinterpret_cast<float *>(smem);
+
     auto consume = [&](const Buf &bf, int t) {
         const int64_t row0 = r_begin + int64_t(t) * R;
 #pragma unroll
@@ -143,7 +166,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             float sv[J], bv[J];
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int e = (kWave * j + lane) >> p.group_shift;     // group index in the row
+                const int e = ((c_lo + kWave * j + lane) >> p.group_shift) - g_lo;   // group in the segment
                 const int src = (e >> 1) & (kWave - 1);
                 const bool hi = e & 1;
                 sv[j] = bv[j] = 0.0f;
@@ -159,7 +182,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             if (row0 + i < r_end) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
-                    if (kWave * j + lane < C) {
+                    if (c_lo + kWave * j + lane < c_hi) {
 #pragma unroll
                         for (int b = 0; b < B; ++b) {
                             const float raw = Fmt::dot(bf.c[i][j], xp[b][j], 0.0f);
@@ -169,19 +192,40 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
                 }
             }
         }
-        reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
-            float rs = 1.0f;
-            if constexpr (Fmt::kRowScale) {
-                rs = bf.rs[0];
+        if (S == 1) {
+            reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
+                float rs = 1.0f;
+                if constexpr (Fmt::kRowScale) {
+                    rs = bf.rs[0];
 #pragma unroll
-                for (int ii = 1; ii < R; ++ii)
-                    if (i == ii) rs = bf.rs[ii];
-            }
-            return rs;
-        });
+                    for (int ii = 1; ii < R; ++ii)
+                        if (i == ii) rs = bf.rs[ii];
+                }
+                return rs;
+            });
+        } else {
+            reduce_tile<R, B>(acc, lane, [&](int i, int b, float total) {
+                const int64_t row = row0 + i;
+                if (row < r_end) part[((row - b_begin) * S + seg) * B + b] = total;
+            });
+        }
     };
 
     run_pipeline<D>(buf, tiles, issue, consume);
+
+    if (S > 1) {
+        // add the segments of every row in segment order and write y
+        __syncthreads();
+        for (int64_t idx = threadIdx.x; idx < b_rows * B; idx += blockDim.x) {
+            const int64_t r = idx / B;
+            const int b = int(idx - r * B);
+            float sum = part[(r * S) * B + b];
+            for (int sg = 1; sg < S; ++sg) sum += part[(r * S + sg) * B + b];
+            const int64_t row = b_begin + r;
+            if constexpr (Fmt::kRowScale) sum *= p.row_scale[row];
+            store_y(p, b, row, sum);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ long rows

@@ -373,3 +373,66 @@ def test_poisoned_neighbours_are_never_read_or_written(fmt, gs):
     assert (yb[:GUARD] == 0xAB).all() and (yb[-GUARD:] == 0xAB).all(), "write outside y"
     y_ref, a_ref = _oracle(fmt, arrays, x, gs)
     parity.assert_parity(y, y_ref, a_ref)
+
+
+# ---------------------------------------------------------------- kernel paths
+
+@pytest.mark.parametrize("fmt,n,k,gs,batch", [
+    # rows cut into 2, 4 or 8 K segments (split-K inside a workgroup)
+    ("fp4", 129, 15360, 32, 1), ("fp4", 67, 15360, 32, 2), ("fp4", 40, 8192, 64, 4),
+    ("u4", 100, 14336, 64, 1), ("u4", 33, 15360, 64, 3), ("u8", 77, 15360, 64, 1),
+    ("u8", 50, 3840, 64, 2), ("u8", 9, 14336, 64, 1), ("fp8", 70, 15360, None, 4),
+    ("fp8", 300, 8192, None, 1),
+])
+def test_split_k_shapes(fmt, n, k, gs, batch):
+    _case(fmt, n, k, gs, batch, seed=n * 31 + k + batch)
+
+
+@pytest.mark.parametrize("fmt,n,k,gs,batch", [
+    # shapes the register kernel does not take: odd group counts per row or
+    # segment, a chunk count no power-of-two segment count divides
+    ("fp4", 90, 3872, 32, 1), ("u4", 45, 3904, 64, 2), ("u8", 61, 3904, 32, 1),
+    ("fp8", 80, 4112, None, 3),
+])
+def test_lds_kernel_shapes(fmt, n, k, gs, batch):
+    _case(fmt, n, k, gs, batch, seed=n * 17 + k)
+
+
+def test_two_byte_aligned_scales_take_the_lds_kernel():
+    """Scales that are only 2-byte aligned are legal; results must not change."""
+    n, k, gs = 150, 3840, 32
+    w = synth.weights(14, n, k)
+    codes, scales = _quantize("fp4", w, gs)
+    x = synth.activations(14, 2, k)
+    y_ref, a_ref = G.gemv_fp4_e2m1(codes, scales, x, gs)
+    y_aligned = run("fp4", (codes, scales), x, n, gs=gs)
+    buf = torch.zeros(scales.size + 1, dtype=torch.int16, device="cuda:0")
+    buf[1:] = torch.from_numpy(scales.view(np.int16).ravel()).to("cuda:0")
+    s_odd = buf[1:].view(n, k // gs)
+    assert s_odd.data_ptr() % 4 == 2
+    y = out_tensor(2, n)
+    log("fp4 2-byte aligned scales")
+    q.qgemv_fp4_e2m1(dev(codes), s_odd, dev(x), y, gs)
+    y2 = host_y(y)
+    parity.assert_parity(y2, y_ref, a_ref)
+    parity.assert_parity(y_aligned, y_ref, a_ref)
+
+
+@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 15360), ("u8", 64, 15360), ("u4", 64, 14336)])
+def test_split_k_batch_and_bf16(fmt, gs, k):
+    n = 200
+    w = synth.weights(15, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x4 = synth.activations(15, 4, k)
+    fid = {"fp4": q.QG_FMT_FP4_E2M1, "u4": q.QG_FMT_AFFINE_U4, "u8": q.QG_FMT_AFFINE_U8}[fmt]
+    bmax = 4
+    while k > q.qg_max_k(fid, bmax):
+        bmax -= 1
+    log("split-K batch/bf16 %s k=%d batch<=%d" % (fmt, k, bmax))
+    yb = run(fmt, arrays, x4[:bmax], n, gs=gs)
+    for b in range(bmax):
+        assert np.array_equal(run(fmt, arrays, x4[b:b + 1], n, gs=gs)[0], yb[b])
+    y16 = run(fmt, arrays, x4[:bmax], n, gs=gs, bf16=True)
+    assert np.array_equal(y16, F.f64_to_bf16_bits(yb.astype(np.float64)))
+    y_ref, a_ref = _oracle(fmt, arrays, x4[:bmax], gs)
+    parity.assert_parity(yb, y_ref, a_ref)
