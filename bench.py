@@ -35,14 +35,41 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0
 METRIC = "quantized GEMV HBM GB/s & % of 8 TB/s peak; µs per Gemma-12B-shaped matvec"
 ROT_BYTES = 1 << 30
-# rocprofv3 FETCH_SIZE / WRITE_SIZE per launch of the default workload, scaled
-# by the same counters on a plain copy of known size (see profiles/)
-TRAFFIC = None
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "block_quantized_weight_qgemv_amd", "csrc")
+KERNEL_SOURCES = ["qgemv_common.hpp", "qgemv_formats.hpp", "qgemv_kernels.hpp", "qgemv_api.hip"]
+# rocprofv3 FETCH_SIZE / WRITE_SIZE of the default workload, each scaled by
+# what the counter reads for a plain copy of known size; written by
+# --summarize-pmc and only used while the kernel sources are unchanged
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fp4_gate_up_30720x3840_traffic.json")
+COPY_BYTES = 512 << 20
 
 
 def log(msg):
     sys.stderr.write(msg + "\n")
     sys.stderr.flush()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic():
+    """Scaled HBM bytes per launch from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
 
 
 # ------------------------------------------------------------------ workloads
@@ -94,7 +121,7 @@ class Workload:
         self.x_host = synth.activations(sid, batch, k)
         self.bytes = algorithmic_bytes(fmt, n, k, batch, gs)
         wbytes = sum(a.nbytes for a in self.host)
-        self.copies = copies or max(1, math.ceil(ROT_BYTES / wbytes))
+        self.copies = copies or min(4096, max(1, math.ceil(ROT_BYTES / wbytes)))
         first = [to_dev(a) for a in self.host]
         self.dev = [first] + [[t.clone() for t in first] for _ in range(self.copies - 1)]
         if not keep_host:
@@ -239,7 +266,7 @@ def run_default(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
-            "traffic": TRAFFIC,
+            "traffic": stored_traffic(),
         },
         "cpu_baseline": None,
     }
@@ -340,10 +367,85 @@ def run_probe(args):
             json.dump(rows, f, indent=1)
 
 
+def _pmc_median(run_dir, counter, kernel_substr):
+    import csv
+    import glob
+    import statistics
+    vals = []
+    for path in glob.glob(os.path.join(run_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter and kernel_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit("no %s values for kernels matching %r in %s" % (counter, kernel_substr, run_dir))
+    return statistics.median(vals), len(vals)
+
+
+def run_summarize_pmc(args):
+    """FETCH_SIZE and WRITE_SIZE per matvec launch, scaled by the counters of a
+    plain copy of COPY_BYTES (read COPY_BYTES, wrote COPY_BYTES)."""
+    fetch_dir, write_dir, copy_fetch_dir, copy_write_dir = args.summarize_pmc
+    k_fetch, n1 = _pmc_median(fetch_dir, "FETCH_SIZE", "qgemv")
+    k_write, n2 = _pmc_median(write_dir, "WRITE_SIZE", "qgemv")
+    c_fetch, _ = _pmc_median(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
+    c_write, _ = _pmc_median(copy_write_dir, "WRITE_SIZE", "copyBuffer")
+    f_scale = COPY_BYTES / (c_fetch * 1024.0)
+    w_scale = COPY_BYTES / (c_write * 1024.0)
+    fetch_b = k_fetch * 1024.0 * f_scale
+    write_b = k_write * 1024.0 * w_scale
+    out = {
+        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)",
+        "kernel_source_sha256": kernel_source_hash(),
+        "fetch_size_kib_median": k_fetch, "write_size_kib_median": k_write, "dispatches": [n1, n2],
+        "copy_bytes": COPY_BYTES, "copy_fetch_size_kib": c_fetch, "copy_write_size_kib": c_write,
+        "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+        "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
+        "hbm_read_bytes_per_launch": int(round(fetch_b)),
+        "hbm_write_bytes_per_launch": int(round(write_b)),
+        "algorithmic_bytes_per_launch": algorithmic_bytes("fp4", 30720, 3840, 1, 32),
+        "commands": args.commands or "",
+    }
+    with open(args.out or TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    log(json.dumps(out, indent=1))
+
+
+def run_summarize_trace(args):
+    """Short text summary of a rocprofv3 --kernel-trace --stats run."""
+    import csv
+    import glob
+    run_dir = args.summarize_trace
+    lines = ["# rocprofv3 kernel-trace summary", "# command: %s" % (args.commands or "?"), ""]
+    for path in sorted(glob.glob(os.path.join(run_dir, "*kernel_stats.csv"))):
+        rows = list(csv.DictReader(open(path)))
+        lines.append("%-70s %7s %12s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us", "pct"))
+        for r in rows:
+            name = r.get("Name", "")[:70]
+            lines.append("%-70s %7s %12.3f %12.3f %12.3f %12.2f" % (
+                name, r.get("Calls", ""), float(r.get("AverageNs", 0)) / 1e3, float(r.get("MinNs", 0)) / 1e3,
+                float(r.get("MaxNs", 0)) / 1e3, float(r.get("Percentage", 0))))
+    for path in sorted(glob.glob(os.path.join(run_dir, "*kernel_trace.csv"))):
+        import statistics
+        durs = {}
+        for r in csv.DictReader(open(path)):
+            durs.setdefault(r["Kernel_Name"][:70], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines.append("")
+        lines.append("%-70s %7s %10s %10s %10s" % ("kernel (per-dispatch durations)", "n", "median_us", "p10_us", "p90_us"))
+        for k, v in durs.items():
+            v = sorted(v)
+            lines.append("%-70s %7d %10.3f %10.3f %10.3f" % (k, len(v), statistics.median(v),
+                                                          v[len(v) // 10], v[(len(v) * 9) // 10]))
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    sys.stdout.write(text)
+
+
 def run_calibrate_copy(args):
     """A plain device copy of known size, for scaling the rocprofv3 byte counters."""
     import torch
-    nbytes = 512 << 20
+    nbytes = COPY_BYTES
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
     b = torch.empty_like(a)
     for _ in range(3):
@@ -365,7 +467,17 @@ def main(argv=None):
     ap.add_argument("--out", default="")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--probe", action="store_true", help="stream-probe read bandwidth sweep")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
+                    help="fetch, write, copy-fetch and copy-write rocprofv3 --pmc output dirs")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="rocprofv3 --kernel-trace --stats output dir")
+    ap.add_argument("--commands", default="", help="with --summarize-*: the commands that made the data")
     args = ap.parse_args(argv)
+    if args.summarize_pmc:
+        run_summarize_pmc(args)
+        return 0
+    if args.summarize_trace:
+        run_summarize_trace(args)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py runs on one GPU only: this matvec library has no multi-GPU path "
