@@ -64,6 +64,17 @@ __device__ __forceinline__ uint32_t load_param_pair(const uint16_t *p) {
 // Activations are shared by every wave: ordinary cached loads.
 __device__ __forceinline__ uint4 load_x_unit(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// Wait until at most N vector-memory loads of this wave are outstanding.
+// gfx9 encoding of s_waitcnt: vmcnt in bits [3:0] and [15:14], expcnt and
+// lgkmcnt (bits [6:4], [11:8]) left at their maximum, i.e. not waited for.
+// The compiler still places the waits correctness needs; this one only
+// orders issue (what comes after it is issued once the older loads are in).
+template <int N>
+__device__ __forceinline__ void wait_vm_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 // Value of lane `src` of v (every lane must be active).
 __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
     return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));

@@ -128,9 +128,15 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         }
     };
 
+    // Tile 0 goes out right behind the activations, then the wave waits for
+    // the activations alone (loads retire in order) before it issues the rest
+    // of the prefetch: the first burst of weight requests over the whole chip
+    // is one tile per wave, and the activations are not queued behind it.
     Buf buf[D];
+    issue(buf[0], 0);
+    wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, tiles - 1)));
+    for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, tiles - 1)));
 
     // activation pieces (and chunk sums) in registers
     uint4 xp[B][J][Fmt::kPieces];
@@ -322,9 +328,13 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
 #pragma unroll
     for (int i = 0; i < kXU; ++i) xr[i] = x_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
 
+    // step 0 right behind the activations, the rest once they are in (as in
+    // the row kernel)
     Buf buf[D];
+    issue(buf[0], 0);
+    wait_vm_loads<R + R * Fmt::kAuxArrays>();
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+    for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
 
 #pragma unroll
     for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i]);
