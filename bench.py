@@ -284,6 +284,14 @@ SWEEP = [
 ]
 
 
+def timed_steps(launch, mode, target_ms=25.0):
+    """Steps for a timed region of about target_ms: the first launches of a
+    short region run at lower clocks (a 200-launch region of the 30720x3840
+    FP4 matvec times about 8% slower per launch than a 2000-launch one)."""
+    est = time_steps(launch, 20, 5, mode) / 20
+    return int(min(4000, max(50, target_ms / max(est, 1e-4))))
+
+
 def run_sweep(args):
     import torch
     rows = []
@@ -292,8 +300,8 @@ def run_sweep(args):
         if only and name not in only and "%s:%s" % (fmt, name) not in only:
             continue
         wl = Workload(fmt, name, batch=batch, gs=gs, plan=parse_plan(args.plan))
-        steps = args.steps
-        ms = time_steps(wl.launch, steps, args.warmup, args.mode)
+        steps = timed_steps(wl.launch, args.mode)
+        ms = time_steps(wl.launch, steps, max(1, steps // 10), args.mode)
         us = ms / steps * 1e3
         gbs = wl.bytes / (us * 1e-6) / 1e9
         row = {"fmt": fmt, "shape": name, "n": wl.n, "k": wl.k, "batch": batch, "group_size": gs,
@@ -321,11 +329,13 @@ def run_decode_step(args, layers=48):
         layer = i // len(shapes)
         wls[i % len(shapes)].launch(layer)
 
-    steps = layers * len(shapes)
-    ms_runs = [time_steps(launch, steps, steps, args.mode) for _ in range(5)]
+    per_step = layers * len(shapes)
+    reps = 10                     # decode steps per timed region (~15 ms)
+    ms_runs = [time_steps(launch, per_step * reps, per_step * 2, args.mode) / reps for _ in range(3)]
     ms = float(np.median(ms_runs))
+    steps = per_step
     gbs = total / (ms * 1e-3) / 1e9
-    log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  (192 launches, median of 5)"
+    log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  (192 launches per step; 10 steps per region, median of 3)"
         % ("fp4 48-layer decode step", ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS))
     del wls
     torch.cuda.empty_cache()
@@ -410,6 +420,42 @@ def run_summarize_pmc(args):
     log(json.dumps(out, indent=1))
 
 
+BUSY_FILE = os.path.join(ROOT, "profiles", "fp4_gate_up_30720x3840_busy.json")
+BUSY_COUNTERS = ["VALUBusy", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE", "TA_BUSY_avr", "SQ_INSTS_VALU",
+                 "SQ_INSTS_VMEM_RD", "SQ_WAVES", "SQ_WAVE_CYCLES"]
+
+
+def run_summarize_busy(args):
+    """VALU busy against memory-unit (TA) busy for the matvec kernel, from one
+    rocprofv3 --pmc run with BUSY_COUNTERS (medians over dispatches).
+
+    VALUBusy is rocprofv3's derived counter: 100 * sum(SQ_ACTIVE_INST_VALU) /
+    CU_NUM / max(GRBM_GUI_ACTIVE) (SQ_ACTIVE_INST_VALU counts quad-cycles).
+    rocprofv3 reports GRBM_GUI_ACTIVE summed over the 8 XCDs, so one XCD's
+    active cycles are GRBM_GUI_ACTIVE / 8; memory-unit busy is TA_BUSY_avr
+    (busy cycles averaged over the TA instances, one per CU) over that."""
+    run_dir = args.summarize_busy
+    med = {}
+    for c in BUSY_COUNTERS:
+        med[c], n = _pmc_median(run_dir, c, "qgemv")
+    gui_per_xcd = med["GRBM_GUI_ACTIVE"] / 8.0
+    out = {
+        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)",
+        "kernel_source_sha256": kernel_source_hash(),
+        "dispatches": n,
+        "counters_median": med,
+        "valu_busy_pct": round(med["VALUBusy"], 2),
+        "mem_unit_busy_pct": round(100.0 * med["TA_BUSY_avr"] / gui_per_xcd, 2),
+        "gpu_active_cycles_per_xcd": gui_per_xcd,
+        "valu_insts_per_wave": round(med["SQ_INSTS_VALU"] / med["SQ_WAVES"], 1),
+        "vmem_read_insts_per_wave": round(med["SQ_INSTS_VMEM_RD"] / med["SQ_WAVES"], 1),
+        "commands": args.commands or "",
+    }
+    with open(args.out or BUSY_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    log(json.dumps(out, indent=1))
+
+
 def run_summarize_trace(args):
     """Short text summary of a rocprofv3 --kernel-trace --stats run."""
     import csv
@@ -457,8 +503,8 @@ def run_calibrate_copy(args):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--mode", choices=["graph", "stream"], default="graph")
     ap.add_argument("--plan", default="", help="rows_per_tile,waves_per_block,blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -470,6 +516,8 @@ def main(argv=None):
     ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
                     help="fetch, write, copy-fetch and copy-write rocprofv3 --pmc output dirs")
     ap.add_argument("--summarize-trace", metavar="DIR", help="rocprofv3 --kernel-trace --stats output dir")
+    ap.add_argument("--summarize-busy", metavar="DIR",
+                    help="rocprofv3 --pmc output dir holding BUSY_COUNTERS (VALU and memory-unit busy)")
     ap.add_argument("--commands", default="", help="with --summarize-*: the commands that made the data")
     args = ap.parse_args(argv)
     if args.summarize_pmc:
@@ -478,10 +526,13 @@ def main(argv=None):
     if args.summarize_trace:
         run_summarize_trace(args)
         return 0
+    if args.summarize_busy:
+        run_summarize_busy(args)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py runs on one GPU only: this matvec library has no multi-GPU path "
-                         "(rows would shard across GPUs with no exchange; see DESIGN.md)\n")
+                         "(rows would shard across GPUs with no exchange between them)\n")
         return 2
     import torch
     if not torch.cuda.is_available():

@@ -68,6 +68,13 @@ def load(path=LIB_PATH):
         raise ImportError(
             "libqgemv.so is not built (%s); run `python block_quantized_weight_qgemv_amd/build.py` "
             "or __graft_entry__.build()" % path)
+    # PyTorch ships its own copy of the HIP runtime (same soname as ROCm's,
+    # another file).  The library must share the process's one with the
+    # tensors it is handed, so torch is loaded first: the library's
+    # dependency on libamdhip64.so.7 then resolves to the copy already in
+    # the process.  Loading the library first would put two HIP runtimes in
+    # the process, and device pointers of one are unknown to the other.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -21,6 +21,7 @@ using qg::Params;
 // has 160 KiB of LDS per compute unit; 128 KiB leaves room for a second,
 // smaller workgroup.
 constexpr int64_t kMaxLds = 128 * 1024;
+constexpr int64_t kCounterBytes = 32;     // row kernel: up to 8 per-segment tile counters
 constexpr int kMaxDevices = 64;
 
 struct FmtInfo {
@@ -164,8 +165,17 @@ Plan default_plan(qg_format f, const Params &p, int32_t batch, int cus) {
     Plan pl;
     pl.row_kernel = row_kernel_fits(f, p, batch);
     pl.passes = p.passes;
-    pl.rows_per_tile = 2;
-    pl.waves_per_block = pl.row_kernel && p.segs > 4 ? p.segs : 4;
+    if (pl.row_kernel) {
+        // one workgroup of 8 waves per CU: its first four waves stage x for
+        // the four dispatched after them.  One row per tile for FP8: its rows
+        // hold twice the bytes of 4-bit rows of the same k, so a one-row tile
+        // carries as many loads as a two-row 4-bit tile.
+        pl.rows_per_tile = f == QG_FMT_FP8_E4M3 ? 1 : 2;
+        pl.waves_per_block = 8;
+    } else {
+        pl.rows_per_tile = 2;
+        pl.waves_per_block = 4;
+    }
     const int64_t waves_per_cu = 8;
     int64_t blocks = int64_t(cus) * waves_per_cu / pl.waves_per_block;
     const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
@@ -192,14 +202,17 @@ qg_status launch(Kern kern, const Params &p, const Plan &pl, int64_t lds, hipStr
 }
 
 // prefetch depth: about 8 code loads in flight per lane
-constexpr int row_depth(int r, int j) { return 8 / (r * j) > 2 ? 8 / (r * j) : 2; }
+// (two when more than 16 activation pieces already fill the registers)
+constexpr int row_depth(int r, int j, int pieces) { return pieces > 16 ? 2 : (8 / (r * j) > 2 ? 8 / (r * j) : 2); }
 constexpr int lds_depth(int r) { return r == 1 ? 8 : 4; }
 
 // register budget of the row kernel: at most 32 activation pieces per lane,
-// and fewer rows per tile when they are many
+// and fewer rows per tile when they are many (one row for the affine formats,
+// whose chunk sums and biases take further registers); no instance spills
 template <class Fmt, int R, int B, int J>
 constexpr bool row_instance() {
-    return B * J * Fmt::kPieces <= 32 && (B * J * Fmt::kPieces <= 16 || R <= 2) && !(R == 4 && J == 4);
+    return B * J * Fmt::kPieces <= 32 && (B * J * Fmt::kPieces <= 16 || R <= (Fmt::kSums ? 1 : 2)) &&
+           !(R == 4 && J == 4);
 }
 
 template <class Fmt, int R, int B>
@@ -207,15 +220,15 @@ qg_status launch_row_j(const Params &p, const Plan &pl, int64_t lds, hipStream_t
     switch (pl.passes) {
         case 1:
             if constexpr (row_instance<Fmt, R, B, 1>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1), 1>, p, pl, lds, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1, B * 1 * Fmt::kPieces), 1>, p, pl, lds, s);
             break;
         case 2:
             if constexpr (row_instance<Fmt, R, B, 2>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2), 2>, p, pl, lds, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2, B * 2 * Fmt::kPieces), 2>, p, pl, lds, s);
             break;
         case 4:
             if constexpr (row_instance<Fmt, R, B, 4>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4), 4>, p, pl, lds, s);
+                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4, B * 4 * Fmt::kPieces), 4>, p, pl, lds, s);
             break;
     }
     return QG_ERR_LAUNCH;     // not reached: run() only picks existing instances
@@ -231,7 +244,7 @@ qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s)
 template <class Fmt>
 bool row_instance_exists(int r, int b, int j) {
     const int pcs = Fmt::kPieces;
-    return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= 2) && !(r == 4 && j == 4);
+    return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= (Fmt::kSums ? 1 : 2)) && !(r == 4 && j == 4);
 }
 
 template <class Fmt, int R>
@@ -306,10 +319,24 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         // fewer rows per tile where the register budget asks for it
         while (pl.rows_per_tile > 1 && !row_instance_for(f, pl.rows_per_tile, batch, pl.passes))
             pl.rows_per_tile /= 2;
-        lds = row_lds_bytes(p, pl.blocks, batch);
+        // x is shared through LDS when the workgroup has the four staging
+        // waves and x fits their staging registers (k is a multiple of 8, so
+        // x takes a multiple of 16 bytes)
+        p.x_staged = (int64_t(pl.waves_per_block) * qg::kWave >= qg::kStageThreads &&
+                      int64_t(batch) * p.k / 8 <= int64_t(qg::kStageThreads) * qg::kStageUnits &&
+                      qg::row_can_stage(batch, pl.passes, fmt_info(f).pieces)) ? 1 : 0;
+        // LDS: staged x, then (with x staged) the per-segment tile counters,
+        // then the split-K partials
+        const int64_t x_bytes = p.x_staged ? int64_t(batch) * p.k * 2 : 0;
+        p.counter_offset = int32_t(x_bytes);
+        p.part_offset = int32_t(x_bytes + (p.x_staged ? kCounterBytes : 0));
+        lds = p.part_offset + row_lds_bytes(p, pl.blocks, batch);
         if (lds > kMaxLds) {
-            pl.blocks = int((p.n * p.segs * batch * 4 + kMaxLds - 1) / kMaxLds);
-            lds = row_lds_bytes(p, pl.blocks, batch);
+            // more, smaller workgroups until the split-K partials fit
+            const int64_t room = kMaxLds - p.part_offset;
+            pl.blocks = int((p.n * p.segs * batch * 4 + room - 1) / room);
+            while (p.part_offset + row_lds_bytes(p, pl.blocks, batch) > kMaxLds) ++pl.blocks;
+            lds = p.part_offset + row_lds_bytes(p, pl.blocks, batch);
         }
     } else {
         p.passes = passes_of(p.chunks);           // the LDS kernel walks whole rows

@@ -9,6 +9,16 @@ namespace qg {
 constexpr int kWave = 64;
 constexpr int kChunkBytes = 16;
 constexpr int kLdsSink = 32;      // LDS bytes after the staged activations
+constexpr int kStageThreads = 256;   // row kernel: threads (waves 0..3) that stage x
+constexpr int kStageUnits = 8;       // row kernel: at most 8 x units per staging thread
+constexpr int kChunksPerWave = 16;   // row kernel: shared tiles are handed out in about 16 chunks per wave
+
+// Whether a row-kernel instance stages x through LDS: only where the staging
+// registers fit beside the activation pieces (batch x passes x pieces of at
+// most 16 registers of 16 bytes) without spilling.
+__host__ __device__ constexpr bool row_can_stage(int batch, int passes, int pieces) {
+    return batch * passes * pieces <= 16;
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
@@ -32,6 +42,9 @@ struct Params {
     int32_t segs;                   // row kernel: K segments per row (split-K)
     int32_t seg_chunks;             // row kernel: chunks per segment
     int32_t seg_groups;             // row kernel: scale groups per segment
+    int32_t x_staged;               // row kernel: x shared through LDS (>= 4 waves per workgroup)
+    int32_t part_offset;            // row kernel: LDS byte offset of the split-K partials
+    int32_t counter_offset;         // row kernel: LDS byte offset of the per-segment tile counters
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -61,6 +74,28 @@ __device__ __forceinline__ uint32_t load_param_pair(const uint16_t *p) {
     return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p));
 }
 
+// Buffer resources for the row kernel's weight loads: a raw (untyped) buffer
+// of `bytes` bytes at `base`; loads at offsets past its end return zeros
+// without a memory access.  Word 3 is the gfx9 raw-buffer format (32-bit data
+// format, no swizzle, no index stride).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kCacheNonTemporal = 2;      // the nt bit of the buffer-load cache policy
+constexpr uint32_t kOutOfRange = 0x7FFFFFF0u;   // an offset past every resource
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, int(bytes), kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 buffer_code_chunk(rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kCacheNonTemporal);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t buffer_param_pair(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, kCacheNonTemporal);
+}
+
 // Activations are shared by every wave: ordinary cached loads.
 __device__ __forceinline__ uint4 load_x_unit(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 
@@ -78,6 +113,22 @@ __device__ __forceinline__ void wait_vm_loads() {
 // Value of lane `src` of v (every lane must be active).
 __device__ __forceinline__ uint32_t lane_read(uint32_t v, int src) {
     return static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(src << 2, static_cast<int>(v)));
+}
+
+// v[i] for a lane-dependent i, where every v[ii] is the same in all lanes.
+// Each value passes through readfirstlane first: a select between plain loads
+// of a register array would otherwise be folded back into one load with a
+// run-time index, which moves the whole array (and everything stored beside
+// it) to scratch memory.
+template <int N>
+__device__ __forceinline__ float pick_uniform(const float (&v)[N], int i) {
+    float r = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v[0])));
+#pragma unroll
+    for (int ii = 1; ii < N; ++ii) {
+        const float t = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v[ii])));
+        r = (i == ii) ? t : r;
+    }
+    return r;
 }
 
 constexpr int pow2_ceil(int v) {

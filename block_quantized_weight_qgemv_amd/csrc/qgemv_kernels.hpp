@@ -19,7 +19,8 @@
 //  * One wave reduction per tile (permlane swaps and DPP), then y is written.
 //
 // qgemv_row_kernel: one step is a whole tile, the wave's slice of x lives in
-//    registers (no LDS staging, no barrier), and a row's group parameters
+//    registers (shared once through LDS when x is small enough), and a row's
+//    group parameters
 //    arrive as one coalesced dword per lane, handed to the lane that needs
 //    them with ds_bpermute.  Rows longer than a few passes are cut into K
 //    segments streamed by the waves of one workgroup (split-K); the segment
@@ -77,66 +78,177 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
 
-    // Rows are split into one contiguous range per workgroup.  A workgroup's
-    // waves form row groups of `segs` waves; the waves of a row group stream
-    // the same rows, each its own segment of the K dimension (split-K), and
-    // their partial sums are added through LDS at the end.
+    // Rows are split into one contiguous range per workgroup, cut into tiles
+    // of R rows, and the tiles into chunks of C consecutive tiles.  The
+    // workgroup's waves form G = waves / segs waves per K segment (split-K
+    // when segs > 1): the G waves of segment `seg` share the workgroup's
+    // chunks, each streaming that segment of every tile it takes, and a row's
+    // segment sums meet in LDS at the end.  Wave gw of a segment starts with
+    // chunk gw.  With x staged, later chunks come from a per-segment LDS
+    // counter, first come first served (waves dispatched first, or served
+    // faster by the memory system, stream more chunks, so the waves of a
+    // workgroup finish together), and chunks are small: about 16 per wave,
+    // one tile when there are few.  Otherwise (x not staged, or one wave per
+    // segment) each wave has one chunk.
     const int S = p.segs;
     const int nb = gridDim.x;
     const int64_t blk = logical_block();
     const int64_t b_begin = blk * p.n / nb, b_end = (blk + 1) * p.n / nb;
     const int w = wave_in_block();
-    const int groups_in_block = (blockDim.x >> 6) / S;
-    const int rg = w / S, seg = w - rg * S;
+    const int G = (blockDim.x >> 6) / S;
+    const int gw = w / S, seg = w - gw * S;     // wave gw of segment seg
     const int64_t b_rows = b_end - b_begin;
-    const int64_t r_begin = b_begin + rg * b_rows / groups_in_block;
-    const int64_t r_end = b_begin + (rg + 1) * b_rows / groups_in_block;
-    const int tiles = int((r_end - r_begin + R - 1) / R);
-    const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
+    const int T = int((b_rows + R - 1) / R);
     const int c_lo = seg * p.seg_chunks;
     const int c_hi = min(p.chunks, c_lo + p.seg_chunks);
 
-    // this lane's activation chunks, one per pass (loaded before the weights)
+    // ---- activations.  With p.x_staged, waves 0..3 of the workgroup load all
+    // of x with coalesced 16-byte loads and the workgroup shares it through
+    // LDS; otherwise every wave loads its own slice.  The later waves of a
+    // workgroup are dispatched after the weight stream of the whole chip has
+    // started, and their own activation loads would wait behind it (about
+    // 1.5 us at the start of a 30720 x 3840 FP4 matvec); through LDS they get
+    // x as soon as the first four waves have it.
+    constexpr bool kCanStage = row_can_stage(B, J, Fmt::kPieces);
+    const bool staged = kCanStage && p.x_staged != 0;     // uniform
+    const bool shared = staged && G > 1;                  // uniform: tiles handed out through LDS
+    const int C = shared ? max(1, T / (kChunksPerWave * G)) : max(1, (T + G - 1) / G);    // tiles per chunk
+    const int x_units = B * p.k / 8;                      // 16-byte units of x
+    const bool few_units = x_units <= 2 * kStageThreads;  // uniform
+    uint4 xr[kCanStage ? kStageUnits : 1];
     uint4 xraw[B][J][Fmt::kRawUnits];
+    if (!staged) {
 #pragma unroll
-    for (int b = 0; b < B; ++b)
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
-            const int c = min(c_lo + kWave * j + lane, c_hi - 1);
-            const uint16_t *xc = p.x + int64_t(b) * p.k + c * Fmt::kWpc;
+            for (int j = 0; j < J; ++j) {
+                const int c = min(c_lo + kWave * j + lane, c_hi - 1);
+                const uint16_t *xc = p.x + int64_t(b) * p.k + c * Fmt::kWpc;
 #pragma unroll
-            for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = load_x_unit(xc + 8 * u);
+                for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = load_x_unit(xc + 8 * u);
+            }
+    } else if (kCanStage && w < kStageThreads / kWave) {
+        // a fixed number of loads per thread (2 or 8; clamped indices repeat
+        // the last unit), so that the waits stay exact
+        if (few_units) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                xr[i] = load_x_unit(p.x + int64_t(min(int(threadIdx.x) + i * kStageThreads, x_units - 1)) * 8);
+        } else if constexpr (kCanStage) {
+#pragma unroll
+            for (int i = 0; i < kStageUnits; ++i)
+                xr[i] = load_x_unit(p.x + int64_t(min(int(threadIdx.x) + i * kStageThreads, x_units - 1)) * 8);
         }
+    }
 
-    // the lane's dword of a row segment's parameters: elements 2m, 2m+1 of the
-    // segment (the host guarantees an even number of groups per segment, at
-    // most 128, starting on 4-byte boundaries)
+    // The weights of tile t are read through buffer resources that cover the
+    // tile's rows inside the workgroup's range only: rows past it, and whole
+    // tiles past the end, read as zeros without touching memory, while every
+    // issue sends the same loads (so the waits stay exact).  A lane reads its
+    // chunk of every pass, and one dword of each row segment's parameters:
+    // elements 2l, 2l+1 of the segment (the host guarantees an even number of
+    // groups per segment, at most 128, starting on 4-byte boundaries).
     const int g_lo = seg * p.seg_groups;
     const int aux_off = g_lo + 2 * min(lane, p.seg_groups / 2 - 1);
-    auto issue = [&](Buf &bf, int t) {
-        const int64_t row0 = r_begin + int64_t(t) * R;
+    // (lanes past the segment's last chunk read past the resource: no access)
+    auto code_off = [&](int j) {
+        const int c = c_lo + kWave * j + lane;
+        return c < c_hi ? uint32_t(c) * kChunkBytes : kOutOfRange;
+    };
+    auto issue = [&](Buf &bf, int t_in) {
+        // t is the same in every lane; saying so keeps the resources in scalar
+        // registers (a resource the compiler cannot prove uniform is used
+        // through a loop over its distinct values)
+        const int t = __builtin_amdgcn_readfirstlane(t_in);
+        const int64_t row0 = b_begin + int64_t(t) * R;
+        const int64_t valid = t < T ? min(int64_t(R), b_end - row0) : 0;
+        const int64_t rb = valid ? row0 : 0;
+        const rsrc_t rc = make_rsrc(p.codes + rb * p.row_bytes, uint32_t(valid * p.row_bytes));
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const int64_t row = min(row0 + i, row_hi);
-            const unsigned char *rp = p.codes + row * p.row_bytes;      // uniform
+        for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int j = 0; j < J; ++j)
-                bf.c[i][j] = load_code_chunk(rp + uint32_t(min(c_lo + kWave * j + lane, c_hi - 1)) * kChunkBytes);
-            if constexpr (Fmt::kAuxArrays >= 1) bf.a[i][0] = load_param_pair(p.scales + row * p.groups + aux_off);
-            if constexpr (Fmt::kAuxArrays >= 2) bf.a[i][1] = load_param_pair(p.biases + row * p.groups + aux_off);
-            if constexpr (Fmt::kRowScale) bf.rs[i] = p.row_scale[row];
+            for (int j = 0; j < J; ++j) bf.c[i][j] = buffer_code_chunk(rc, uint32_t(i * p.row_bytes) + code_off(j));
+        const uint32_t pbytes = uint32_t(valid * p.groups * 2);
+        if constexpr (Fmt::kAuxArrays >= 1) {
+            const rsrc_t rs = make_rsrc(p.scales + rb * p.groups, pbytes);
+#pragma unroll
+            for (int i = 0; i < R; ++i) bf.a[i][0] = buffer_param_pair(rs, uint32_t(i * p.groups + aux_off) * 2);
+        }
+        if constexpr (Fmt::kAuxArrays >= 2) {
+            const rsrc_t rbias = make_rsrc(p.biases + rb * p.groups, pbytes);
+#pragma unroll
+            for (int i = 0; i < R; ++i) bf.a[i][1] = buffer_param_pair(rbias, uint32_t(i * p.groups + aux_off) * 2);
+        }
+        if constexpr (Fmt::kRowScale) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) bf.rs[i] = p.row_scale[min(row0 + i, p.n - 1)];
         }
     };
 
-    // Tile 0 goes out right behind the activations, then the wave waits for
+    // The wave's first tile goes out right behind the activations, then the wave waits for
     // the activations alone (loads retire in order) before it issues the rest
     // of the prefetch: the first burst of weight requests over the whole chip
     // is one tile per wave, and the activations are not queued behind it.
+    // The wave's tiles in order: `cur` walks the current chunk; when the
+    // chunk is used up the next one is taken, only when its first tile is
+    // needed (so the wave's first tile never touches the counter, which is
+    // set up behind the staging barrier).  Chunks are taken in increasing
+    // order, so a tile at or past T means the wave is done; T itself stands
+    // for "no tile" (an empty issue).
+    // All of it is uniform (scalar) work, and says so through readfirstlane:
+    // a value the compiler takes for divergent here would make the loop exit
+    // divergent, and every load and wait in the loop conservative.
+    unsigned *counter = reinterpret_cast<unsigned *>(smem + p.counter_offset);
+    int chunk = gw, cur = gw * C;
+    auto next_issue = [&]() -> int {
+        const bool at_end = cur < T && cur == (chunk + 1) * C;    // chunk used up
+        int taken = chunk + G;
+        if (shared && at_end) {
+            unsigned v = 0;
+            if (lane == 0) v = __hip_atomic_fetch_add(counter + seg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            taken = int(v);
+        }
+        chunk = __builtin_amdgcn_readfirstlane(at_end ? taken : chunk);
+        cur = at_end ? chunk * C : cur;
+        const int t = min(cur, T);
+        cur = __builtin_amdgcn_readfirstlane(cur < T ? cur + 1 : cur);
+        return __builtin_amdgcn_readfirstlane(t);
+    };
     Buf buf[D];
-    issue(buf[0], 0);
-    wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+    int tl[D];                               // tile in each buffer (uniform)
+    tl[0] = next_issue();
+    issue(buf[0], tl[0]);
+    if (!staged) {
+        wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+    } else {
+        uint4 *xlds = reinterpret_cast<uint4 *>(smem);
+        if (w < kStageThreads / kWave) {
+            if (few_units) {
 #pragma unroll
-    for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, tiles - 1)));
+                for (int i = 0; i < 2; ++i) xlds[min(int(threadIdx.x) + i * kStageThreads, x_units - 1)] = xr[i];
+            } else if constexpr (kCanStage) {
+#pragma unroll
+                for (int i = 0; i < kStageUnits; ++i)
+                    xlds[min(int(threadIdx.x) + i * kStageThreads, x_units - 1)] = xr[i];
+            }
+        }
+        if (shared && int(threadIdx.x) < S) counter[threadIdx.x] = unsigned(G);   // next shared chunk
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int c = min(c_lo + kWave * j + lane, c_hi - 1);
+                const int u0 = (b * p.k + c * Fmt::kWpc) / 8;
+#pragma unroll
+                for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = xlds[u0 + u];
+            }
+    }
+#pragma unroll
+    for (int d = 1; d < D; ++d) {
+        tl[d] = next_issue();
+        issue(buf[d], tl[d]);
+    }
 
     // activation pieces (and chunk sums) in registers
     uint4 xp[B][J][Fmt::kPieces];
@@ -161,11 +273,12 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
         for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
 
-    // split-K partials of the workgroup's rows: [row - b_begin][seg][b]
-    float *part = reinterpret_cast<float *>(smem);
+    // split-K partials of the workgroup's rows: [row - b_begin][seg][b],
+    // behind the staged activations
+    float *part = reinterpret_cast<float *>(smem + p.part_offset);
 
     auto consume = [&](const Buf &bf, int t) {
-        const int64_t row0 = r_begin + int64_t(t) * R;
+        const int64_t row0 = b_begin + int64_t(t) * R;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             // group parameters of this lane's chunk in every pass
@@ -185,7 +298,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
                     bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
                 }
             }
-            if (row0 + i < r_end) {
+            if (row0 + i < b_end) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
                     if (c_lo + kWave * j + lane < c_hi) {
@@ -199,25 +312,36 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             }
         }
         if (S == 1) {
-            reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
-                float rs = 1.0f;
-                if constexpr (Fmt::kRowScale) {
-                    rs = bf.rs[0];
-#pragma unroll
-                    for (int ii = 1; ii < R; ++ii)
-                        if (i == ii) rs = bf.rs[ii];
-                }
-                return rs;
+            reduce_store<R, B>(p, acc, row0, b_end, lane, [&](int i) {
+                if constexpr (Fmt::kRowScale) return pick_uniform(bf.rs, i);
+                return 1.0f;
             });
         } else {
             reduce_tile<R, B>(acc, lane, [&](int i, int b, float total) {
                 const int64_t row = row0 + i;
-                if (row < r_end) part[((row - b_begin) * S + seg) * B + b] = total;
+                if (row < b_end) part[((row - b_begin) * S + seg) * B + b] = total;
             });
         }
     };
 
-    run_pipeline<D>(buf, tiles, issue, consume);
+    // The buffers hold the wave's tiles in order, so the first one past the
+    // end ends its work.  After each tile the buffer is refilled at once (an
+    // empty tile past the end costs no memory traffic).
+    bool more = tl[0] < T;
+    while (more) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            if (tl[d] >= T) {
+                more = false;
+                break;
+            }
+            const int nt = next_issue();
+            consume(buf[d], tl[d]);
+            tl[d] = nt;
+            issue(buf[d], nt);
+        }
+    }
+    wait_vm_loads<0>();
 
     if (S > 1) {
         // add the segments of every row in segment order and write y
@@ -381,14 +505,8 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         }
         if (j == passes - 1) {
             reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
-                float rs = 1.0f;
-                if constexpr (Fmt::kRowScale) {
-                    rs = bf.rs[0];
-#pragma unroll
-                    for (int ii = 1; ii < R; ++ii)
-                        if (i == ii) rs = bf.rs[ii];
-                }
-                return rs;
+                if constexpr (Fmt::kRowScale) return pick_uniform(bf.rs, i);
+                return 1.0f;
             });
         }
     };

@@ -12,8 +12,9 @@ Test infrastructure (see ``oracle/__init__``): no product code may import this.
   magnitudes are exact in BF16.
 * E4M3 (FP8, OCP "FN" variant): sign bit 7, four exponent bits (bias 7), three
   mantissa bits, exponent field 0 subnormal, S.1111.111 is NaN, no infinities,
-  largest finite 448.  The page names only "FP8" for the lm_head matvec; the
-  E4M3 reading is stated in the design doc.
+  largest finite 448.  The page names only "FP8" for the lm_head matvec;
+  this module reads it as OCP E4M3 (FN), the usual weight format of that
+  name.
 
 All decoders return float64 and are exact (every value of these formats is a
 float64).  Encoders round to nearest, ties to even, using exact float64

@@ -10,8 +10,9 @@ All arithmetic is float64 on exact inputs, with one rounding per operation,
 in this order (the C++ pack module has to do the same operations):
 
 FP4-E2M1, group absmax (Part 2 post, "The assumption that failed the
-profiler"; the page gives per-group scales but not their derivation, the
-absmax/6 reading is stated in the design doc):
+profiler"; the page gives per-group scales but not their derivation: this
+module reads them as absmax/6, the scale that maps the group's largest
+magnitude onto E2M1's largest value):
     s  = bf16_rne(absmax_g / 6)
     c  = e2m1_rne(w / s)          (saturating at 6; s == 0 -> every code 0)
 

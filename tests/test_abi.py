@@ -132,3 +132,13 @@ def test_plan_query_needs_a_device():
         assert st == OK and plan.blocks >= 1 and plan.rows_per_tile in (1, 2, 4)
     else:
         assert st == 10
+
+
+def test_one_hip_runtime_in_the_process():
+    """PyTorch ships its own copy of the HIP runtime; the binding loads it before
+    the library, so the process maps exactly one libamdhip64 (a second copy would
+    not know the device pointers of the first)."""
+    import torch  # noqa: F401  (what the GPU tests import after this module)
+    with open("/proc/self/maps") as f:
+        paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    assert len(paths) == 1, paths
