@@ -436,3 +436,42 @@ def test_split_k_batch_and_bf16(fmt, gs, k):
     assert np.array_equal(y16, F.f64_to_bf16_bits(yb.astype(np.float64)))
     y_ref, a_ref = _oracle(fmt, arrays, x4[:bmax], gs)
     parity.assert_parity(yb, y_ref, a_ref)
+
+
+# ---------------------------------------------------------------- tile sharing
+
+# Launch shapes that exercise how a workgroup hands out its tiles: chunks of
+# many tiles with a ragged last chunk, wave counts that are not powers of two,
+# one workgroup for every row, and more workgroups than rows (most get none).
+SHARING_PLANS = [
+    None,
+    {"rows_per_tile": 1, "waves_per_block": 8, "blocks": 4},
+    {"rows_per_tile": 2, "waves_per_block": 5, "blocks": 3},
+    {"rows_per_tile": 4, "waves_per_block": 6, "blocks": 11},
+    {"rows_per_tile": 2, "waves_per_block": 4, "blocks": 1},
+    {"rows_per_tile": 1, "waves_per_block": 8, "blocks": 30000},
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,gs,batch", [
+    ("fp4", 20011, 512, 32, 1),       # x staged, one K segment
+    ("fp8", 20011, 1024, None, 2),
+    ("u4", 3001, 8192, 64, 1),        # two K segments, several waves per segment
+    ("u8", 3001, 4096, 64, 2),
+    ("fp4", 5003, 3840, 32, 3),       # x not staged (registers): one chunk per wave
+])
+def test_shared_tiles_bitwise_across_plans(fmt, n, k, gs, batch):
+    """Each row segment is streamed by exactly one wave, whichever wave takes
+    it: the result meets the oracle and is bitwise the same for every launch
+    shape (the sums do not depend on which wave computed them)."""
+    w = synth.weights(16, n, k)
+    arrays = _quantize(fmt, w, gs)
+    x = synth.activations(16, batch, k)
+    ys = []
+    for plan in SHARING_PLANS:
+        log("shared tiles %s n=%d k=%d batch=%d plan %s" % (fmt, n, k, batch, plan))
+        ys.append(run(fmt, arrays, x, n, gs=gs, plan=plan))
+    y_ref, a_ref = _oracle(fmt, arrays, x, gs)
+    parity.assert_parity(ys[0], y_ref, a_ref, "%s n=%d k=%d" % (fmt, n, k))
+    for plan, y in zip(SHARING_PLANS[1:], ys[1:]):
+        assert np.array_equal(y, ys[0]), plan
