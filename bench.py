@@ -312,7 +312,14 @@ def run_sweep(args):
         del wl
         torch.cuda.empty_cache()
     if not only or "step48" in only:
-        rows.append(run_decode_step(args))
+        step = run_decode_step(args)
+        per_shape = {r["shape"]: r["us"] for r in rows if r["fmt"] == "fp4" and r["batch"] == 1}
+        if all(s in per_shape for s in ("qkv", "o_proj", "gate_up", "fc_down")):
+            # the step beside 48 x the sum of the per-shape times measured alone
+            step["sum_of_shapes_us"] = round(48 * sum(per_shape[s] for s in ("qkv", "o_proj", "gate_up", "fc_down")), 2)
+            log("%-42s %9.2f us  (48 x the four per-shape times above)" % ("fp4 48 x (qkv+o_proj+gate_up+fc_down)",
+                                                                           step["sum_of_shapes_us"]))
+        rows.append(step)
     if args.out:
         with open(args.out, "w") as f:
             json.dump(rows, f, indent=1)

@@ -1,0 +1,74 @@
+"""A decode step captured in a HIP graph: every replay equals the eager launches
+bitwise.
+
+The step is the FP4 layer sequence (qkv, o_proj, gate_up, fc_down shapes,
+scaled down) over three distinct layers, each matvec writing its own output.
+The graph is replayed three times; between replays the outputs are cleared by
+a fill kernel outside the graph and the program does eager work of its own,
+so each replay has to write every output again.  The library records no
+memset or allocation into the graph (Part 2 post, "What's next": a graph
+decode step is one of the two ranked levers; the pages verify graph replay
+bit-identical to direct launch).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_qgemv_amd as q
+import synth
+from tests.gpu_util import dev, log, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [("qkv", 1024, 3840), ("o_proj", 480, 4096), ("gate_up", 3840, 3840), ("fc_down", 480, 15360)]
+LAYERS = 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def test_graph_replay_matches_eager_bitwise():
+    mats = []
+    for li in range(LAYERS):
+        for si, (name, n, k) in enumerate(SHAPES):
+            w = synth.weights(200 + si, n, k, layer=li)
+            codes, scales = q.qg_quantize_fp4_e2m1(w, 32)
+            x = synth.activations(200 + si, 1, k)
+            y = torch.empty((1, n), dtype=torch.float32, device="cuda:0")
+            mats.append((name, dev(codes), dev(scales), dev(x), y))
+
+    def step():
+        for name, c, s, x, y in mats:
+            q.qgemv_fp4_e2m1(c, s, x, y, 32)
+
+    log("graph: eager step")
+    step()
+    torch.cuda.synchronize()
+    eager = [m[4].cpu().numpy().copy() for m in mats]
+    assert all(np.isfinite(e).all() for e in eager)
+
+    log("graph: capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                               # warm the launch path on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    scratch = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(3):
+        for m in mats:
+            m[4].zero_()                     # a fill kernel, outside the graph
+        scratch.mul_(1.0001).add_(0.5)        # eager work between replays
+        torch.cuda.synchronize()
+        log("graph: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for (name, *_, y), e in zip(mats, eager):
+            assert np.array_equal(y.cpu().numpy(), e), (rep, name)
