@@ -146,8 +146,9 @@ qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale,
  * matrix shape and the device's compute-unit count.  The *_plan variants take
  * the same arguments plus a qg_plan whose non-zero fields override that
  * choice (for tuning a deployment's own shapes); plan == NULL is the plain
- * call.  Results do not depend on the plan except for the summation order of
- * rows that nearly cancel (every plan meets the same accuracy bound).
+ * call.  Results are bitwise the same for every plan: a row's terms are
+ * added in an order fixed by the format and k alone, whichever wavefront,
+ * tile shape or grid computes it.
  * ---------------------------------------------------------------------- */
 
 typedef struct qg_plan {
