@@ -26,10 +26,12 @@ Modules
   quantize  the offline quantizers (FP4 absmax, affine min-max, FP8 row absmax).
   gemv      dequantize-then-FP64-dot for each format, plus the conditioning
             mass A = sum |w x| used by the parity criterion.
+  norm      RMSNorm of the activations rounded to bf16, the input of the
+            fused norm-then-matvec variants (Part 2 post, "What's next").
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*``
 against closed forms, library decoders, exact rational brute force or the
 pages' own byte accounting.  Functions with no such pin say "parity unpinned".
 """
 
-from . import formats, layout, quantize, gemv  # noqa: F401
+from . import formats, layout, quantize, gemv, norm  # noqa: F401
