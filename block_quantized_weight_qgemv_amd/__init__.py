@@ -119,6 +119,15 @@ def _same_device(*ts):
         raise ValueError("all tensors must be on one device, got %s" % devs)
 
 
+def _gamma(gamma, k, x):
+    torch = _torch()
+    gp = _dev_ptr(gamma, "gamma", (torch.bfloat16, torch.int16, torch.uint16), (1,))
+    if gamma.shape[0] != k:
+        raise ValueError("gamma must have k=%d values, has %d" % (k, gamma.shape[0]))
+    _same_device(gamma, x)
+    return gp
+
+
 def qgemv_fp4_e2m1(codes, scales, x, y, group_size, plan=None, stream=None):
     """y[b, n] = sum_k scale[n, k//gs] * E2M1(code[n, k]) * x[b, k].
 
@@ -140,7 +149,28 @@ def qgemv_fp4_e2m1(codes, scales, x, y, group_size, plan=None, stream=None):
     return y
 
 
-def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream):
+def qgemv_fp4_e2m1_rmsnorm(codes, scales, x, gamma, eps, y, group_size, plan=None, stream=None):
+    """y = W . RMSNorm(x) in one launch: x~ = bf16(x * gamma / sqrt(mean(x^2) + eps)) per batch row.
+
+    As qgemv_fp4_e2m1, plus gamma bf16 [k] and eps >= 0.
+    """
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.uint8,), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 2 != k or tuple(scales.shape) != (n, k // group_size):
+        raise ValueError("shapes: codes %s, scales %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), k, group_size))
+    gp = _gamma(gamma, k, x)
+    _same_device(codes, scales, x, y)
+    st = _lib.qgemv_fp4_e2m1_rmsnorm(cp, sp, xp, gp, float(eps), yp, n, k, int(group_size), batch, out,
+                                     _plan_ptr(plan), _stream(stream, y.device))
+    _check(st, "qgemv_fp4_e2m1_rmsnorm")
+    return y
+
+
+def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream, gamma=None, eps=0.0):
     torch = _torch()
     cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
     sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
@@ -152,9 +182,16 @@ def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream):
         raise ValueError("shapes: codes %s, scales %s, biases %s, k=%d, group_size=%d"
                          % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), k, group_size))
     _same_device(codes, scales, biases, x, y)
-    fn = getattr(_lib, name + "_plan")
-    st = fn(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out, _plan_ptr(plan), _stream(stream, y.device))
-    _check(st, name)
+    if gamma is None:
+        fn = getattr(_lib, name + "_plan")
+        st = fn(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out, _plan_ptr(plan), _stream(stream, y.device))
+        _check(st, name)
+    else:
+        gp = _gamma(gamma, k, x)
+        fn = getattr(_lib, name + "_rmsnorm")
+        st = fn(cp, sp, bp, xp, gp, float(eps), yp, n, k, int(group_size), batch, out, _plan_ptr(plan),
+                _stream(stream, y.device))
+        _check(st, name + "_rmsnorm")
     return y
 
 
@@ -166,6 +203,34 @@ def qgemv_affine_u4(codes, scales, biases, x, y, group_size=64, plan=None, strea
 def qgemv_affine_u8(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):
     """As qgemv_affine_u4 with 8-bit codes, u32 low-first [n, k/4]."""
     return _affine("qgemv_affine_u8", 8, codes, scales, biases, x, y, group_size, plan, stream)
+
+
+def qg_rmsnorm_bf16(x, gamma, eps, out=None, stream=None):
+    """out = bf16(x * gamma / sqrt(mean(x^2) + eps)) per row, exactly as the fused variants normalize x."""
+    torch = _torch()
+    xp = _dev_ptr(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (1, 2))
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    k = x.shape[-1]
+    gp = _gamma(gamma, k, x)
+    if out is None:
+        out = torch.empty_like(x)
+    op = _dev_ptr(out, "out", (torch.bfloat16, torch.int16, torch.uint16), (1, 2))
+    if out.numel() != batch * k:
+        raise ValueError("out must hold batch * k = %d values" % (batch * k))
+    _same_device(x, out)
+    st = _lib.qg_rmsnorm_bf16(xp, gp, float(eps), op, k, batch, _stream(stream, x.device))
+    _check(st, "qg_rmsnorm_bf16")
+    return out
+
+
+def qgemv_affine_u4_rmsnorm(codes, scales, biases, x, gamma, eps, y, group_size=64, plan=None, stream=None):
+    """y = W . RMSNorm(x) in one launch, 4-bit affine codes (see qgemv_fp4_e2m1_rmsnorm)."""
+    return _affine("qgemv_affine_u4", 4, codes, scales, biases, x, y, group_size, plan, stream, gamma, eps)
+
+
+def qgemv_affine_u8_rmsnorm(codes, scales, biases, x, gamma, eps, y, group_size=64, plan=None, stream=None):
+    """y = W . RMSNorm(x) in one launch, 8-bit affine codes (see qgemv_fp4_e2m1_rmsnorm)."""
+    return _affine("qgemv_affine_u8", 8, codes, scales, biases, x, y, group_size, plan, stream, gamma, eps)
 
 
 def qgemv_fp8_e4m3(codes, row_scale, x, y, plan=None, stream=None):
@@ -180,6 +245,23 @@ def qgemv_fp8_e4m3(codes, row_scale, x, y, plan=None, stream=None):
     _same_device(codes, row_scale, x, y)
     st = _lib.qgemv_fp8_e4m3_plan(cp, rp, xp, yp, n, k, batch, out, _plan_ptr(plan), _stream(stream, y.device))
     _check(st, "qgemv_fp8_e4m3")
+    return y
+
+
+def qgemv_fp8_e4m3_rmsnorm(codes, row_scale, x, gamma, eps, y, plan=None, stream=None):
+    """y = W . RMSNorm(x) in one launch, FP8-E4M3 codes with row scales (see qgemv_fp4_e2m1_rmsnorm)."""
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.uint8,), (2,))
+    rp = _dev_ptr(row_scale, "row_scale", (torch.float32,), (1,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] != k or row_scale.shape[0] != n:
+        raise ValueError("shapes: codes %s, row_scale %s, k=%d" % (tuple(codes.shape), tuple(row_scale.shape), k))
+    gp = _gamma(gamma, k, x)
+    _same_device(codes, row_scale, x, y)
+    st = _lib.qgemv_fp8_e4m3_rmsnorm(cp, rp, xp, gp, float(eps), yp, n, k, batch, out, _plan_ptr(plan),
+                                     _stream(stream, y.device))
+    _check(st, "qgemv_fp8_e4m3_rmsnorm")
     return y
 
 

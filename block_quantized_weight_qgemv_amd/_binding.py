@@ -45,6 +45,13 @@ SIGNATURES = {
     "qgemv_affine_u8_plan": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p, _p]),
     "qgemv_fp8_e4m3": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _p]),
     "qgemv_fp8_e4m3_plan": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "qgemv_fp4_e2m1_rmsnorm": (_st, [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _i32, _p, _p]),
+    "qgemv_affine_u4_rmsnorm": (_st, [_p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _i32,
+                                      _p, _p]),
+    "qgemv_affine_u8_rmsnorm": (_st, [_p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _i32,
+                                      _p, _p]),
+    "qgemv_fp8_e4m3_rmsnorm": (_st, [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "qg_rmsnorm_bf16": (_st, [_p, _p, ctypes.c_float, _p, _i64, _i32, _p]),
     "qg_plan_query": (_st, [_i32, _i64, _i64, _i32, _p]),
     "qg_stream_probe": (_st, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "qg_status_string": (ctypes.c_char_p, [_st]),

@@ -309,6 +309,8 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
             pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
         }
     }
+    // fused RMSNorm: one float per group of 64 activation units per batch row
+    const int64_t norm_bytes = p.norm ? int64_t(batch) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
     int64_t lds = 0;
     if (pl.row_kernel) {
         // a workgroup holds whole row groups of `segs` waves
@@ -322,25 +324,35 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         // x is shared through LDS when the workgroup has the four staging
         // waves and x fits their staging registers (k is a multiple of 8, so
         // x takes a multiple of 16 bytes)
-        p.x_staged = (int64_t(pl.waves_per_block) * qg::kWave >= qg::kStageThreads &&
+        // (the fused norm always takes x through LDS instead)
+        p.x_staged = (!p.norm && int64_t(pl.waves_per_block) * qg::kWave >= qg::kStageThreads &&
                       int64_t(batch) * p.k / 8 <= int64_t(qg::kStageThreads) * qg::kStageUnits &&
                       qg::row_can_stage(batch, pl.passes, fmt_info(f).pieces)) ? 1 : 0;
-        // LDS: staged x, then (with x staged) the per-segment tile counters,
-        // then the split-K partials
-        const int64_t x_bytes = p.x_staged ? int64_t(batch) * p.k * 2 : 0;
-        p.counter_offset = int32_t(x_bytes);
-        p.part_offset = int32_t(x_bytes + (p.x_staged ? kCounterBytes : 0));
+        // LDS: x (staged or normalized), gamma (fused norm), the per-segment
+        // tile counters (x in LDS), the split-K partials, the norm's sums
+        const bool via_lds = p.x_staged || p.norm;
+        const int64_t x_bytes = via_lds ? int64_t(batch) * p.k * 2 : 0;
+        const int64_t g_bytes = p.norm ? int64_t(p.k) * 2 : 0;
+        p.gamma_offset = int32_t(x_bytes);
+        p.counter_offset = int32_t(x_bytes + g_bytes);
+        p.part_offset = int32_t(x_bytes + g_bytes + (via_lds ? kCounterBytes : 0));
+        if (p.part_offset + norm_bytes > kMaxLds) return QG_ERR_TOO_LARGE;
         lds = p.part_offset + row_lds_bytes(p, pl.blocks, batch);
-        if (lds > kMaxLds) {
+        if (lds + norm_bytes > kMaxLds) {
             // more, smaller workgroups until the split-K partials fit
-            const int64_t room = kMaxLds - p.part_offset;
+            const int64_t room = kMaxLds - p.part_offset - norm_bytes;
             pl.blocks = int((p.n * p.segs * batch * 4 + room - 1) / room);
-            while (p.part_offset + row_lds_bytes(p, pl.blocks, batch) > kMaxLds) ++pl.blocks;
+            while (p.part_offset + row_lds_bytes(p, pl.blocks, batch) + norm_bytes > kMaxLds) ++pl.blocks;
             lds = p.part_offset + row_lds_bytes(p, pl.blocks, batch);
         }
+        p.norm_offset = int32_t(lds);
+        lds += norm_bytes;
     } else {
         p.passes = passes_of(p.chunks);           // the LDS kernel walks whole rows
         lds = lds_bytes(f, p.k, batch);
+        p.norm_offset = int32_t(lds);
+        lds += norm_bytes;
+        if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
     }
     p.total_waves = pl.blocks * pl.waves_per_block;
     switch (f) {
@@ -367,21 +379,69 @@ Params base_params(qg_format f, const void *codes, const void *x, void *y, int64
     return p;
 }
 
+// Fused RMSNorm arguments (gamma == nullptr in the plain entry points).
+struct Norm {
+    const uint16_t *gamma;
+    float eps;
+};
+
+qg_status set_norm(Params &p, const Norm *nm) {
+    if (!nm) return QG_OK;
+    if (!nm->gamma) return QG_ERR_NULL_POINTER;
+    if (!aligned(nm->gamma, 16)) return QG_ERR_MISALIGNED;
+    if (!(nm->eps >= 0.0f) || nm->eps > 3.0e38f) return QG_ERR_BAD_VALUE;   // NaN, negative or infinite
+    p.gamma = nm->gamma;
+    p.eps = nm->eps;
+    p.norm = 1;
+    return QG_OK;
+}
+
+qg_status fp4_entry(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y, int64_t n,
+                    int64_t k, int32_t group_size, int32_t batch, qg_out_dtype out, const qg_plan *plan,
+                    const Norm *nm, hipStream_t stream) {
+    qg_status st = check_common(QG_FMT_FP4_E2M1, codes, x, y, n, k, batch, out);
+    if (st != QG_OK) return st;
+    st = check_groups(scales, nullptr, false, k, group_size, qg::FmtFP4::kWpc);
+    if (st != QG_OK) return st;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(QG_FMT_FP4_E2M1, codes, x, y, n, k, out);
+    if ((st = set_norm(p, nm)) != QG_OK) return st;
+    p.scales = scales;
+    p.groups = int32_t(k / group_size);
+    p.group_shift = log2i(group_size / qg::FmtFP4::kWpc);
+    return run(QG_FMT_FP4_E2M1, p, batch, plan, stream);
+}
+
 qg_status affine_entry(qg_format f, const uint32_t *codes, const uint16_t *scales,
                        const uint16_t *biases, const uint16_t *x, void *y, int64_t n, int64_t k,
                        int32_t group_size, int32_t batch, qg_out_dtype out, const qg_plan *plan,
-                       hipStream_t stream) {
+                       const Norm *nm, hipStream_t stream) {
     qg_status st = check_common(f, codes, x, y, n, k, batch, out);
     if (st != QG_OK) return st;
     st = check_groups(scales, biases, true, k, group_size, fmt_info(f).wpc);
     if (st != QG_OK) return st;
     if ((st = check_plan(plan)) != QG_OK) return st;
     Params p = base_params(f, codes, x, y, n, k, out);
+    if ((st = set_norm(p, nm)) != QG_OK) return st;
     p.scales = scales;
     p.biases = biases;
     p.groups = int32_t(k / group_size);
     p.group_shift = log2i(group_size / fmt_info(f).wpc);
     return run(f, p, batch, plan, stream);
+}
+
+qg_status fp8_entry(const uint8_t *codes, const float *row_scale, const uint16_t *x, void *y, int64_t n,
+                    int64_t k, int32_t batch, qg_out_dtype out, const qg_plan *plan, const Norm *nm,
+                    hipStream_t stream) {
+    qg_status st = check_common(QG_FMT_FP8_E4M3, codes, x, y, n, k, batch, out);
+    if (st != QG_OK) return st;
+    if (!row_scale) return QG_ERR_NULL_POINTER;
+    if (!aligned(row_scale, 4)) return QG_ERR_MISALIGNED;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(QG_FMT_FP8_E4M3, codes, x, y, n, k, out);
+    if ((st = set_norm(p, nm)) != QG_OK) return st;
+    p.row_scale = row_scale;
+    return run(QG_FMT_FP8_E4M3, p, batch, plan, stream);
 }
 
 }  // namespace
@@ -391,22 +451,21 @@ extern "C" {
 qg_status qgemv_fp4_e2m1_plan(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
                               void *y, int64_t n, int64_t k, int32_t group_size, int32_t batch,
                               qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream) {
-    qg_status st = check_common(QG_FMT_FP4_E2M1, codes, x, y, n, k, batch, out_dtype);
-    if (st != QG_OK) return st;
-    st = check_groups(scales, nullptr, false, k, group_size, qg::FmtFP4::kWpc);
-    if (st != QG_OK) return st;
-    if ((st = check_plan(plan)) != QG_OK) return st;
-    Params p = base_params(QG_FMT_FP4_E2M1, codes, x, y, n, k, out_dtype);
-    p.scales = scales;
-    p.groups = int32_t(k / group_size);
-    p.group_shift = log2i(group_size / qg::FmtFP4::kWpc);
-    return run(QG_FMT_FP4_E2M1, p, batch, plan, stream);
+    return fp4_entry(codes, scales, x, y, n, k, group_size, batch, out_dtype, plan, nullptr, stream);
 }
 
 qg_status qgemv_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y,
                          int64_t n, int64_t k, int32_t group_size, int32_t batch,
                          qg_out_dtype out_dtype, hipStream_t stream) {
-    return qgemv_fp4_e2m1_plan(codes, scales, x, y, n, k, group_size, batch, out_dtype, nullptr, stream);
+    return fp4_entry(codes, scales, x, y, n, k, group_size, batch, out_dtype, nullptr, nullptr, stream);
+}
+
+qg_status qgemv_fp4_e2m1_rmsnorm(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                                 const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k,
+                                 int32_t group_size, int32_t batch, qg_out_dtype out_dtype,
+                                 const qg_plan *plan, hipStream_t stream) {
+    const Norm nm{gamma, eps};
+    return fp4_entry(codes, scales, x, y, n, k, group_size, batch, out_dtype, plan, &nm, stream);
 }
 
 qg_status qgemv_affine_u4_plan(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
@@ -414,14 +473,23 @@ qg_status qgemv_affine_u4_plan(const uint32_t *codes, const uint16_t *scales, co
                                int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
                                hipStream_t stream) {
     return affine_entry(QG_FMT_AFFINE_U4, codes, scales, biases, x, y, n, k, group_size, batch,
-                        out_dtype, plan, stream);
+                        out_dtype, plan, nullptr, stream);
 }
 
 qg_status qgemv_affine_u4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                           const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
                           int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     return affine_entry(QG_FMT_AFFINE_U4, codes, scales, biases, x, y, n, k, group_size, batch,
-                        out_dtype, nullptr, stream);
+                        out_dtype, nullptr, nullptr, stream);
+}
+
+qg_status qgemv_affine_u4_rmsnorm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                  const uint16_t *x, const uint16_t *gamma, float eps, void *y,
+                                  int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                                  qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream) {
+    const Norm nm{gamma, eps};
+    return affine_entry(QG_FMT_AFFINE_U4, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, plan, &nm, stream);
 }
 
 qg_status qgemv_affine_u8_plan(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
@@ -429,33 +497,67 @@ qg_status qgemv_affine_u8_plan(const uint32_t *codes, const uint16_t *scales, co
                                int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
                                hipStream_t stream) {
     return affine_entry(QG_FMT_AFFINE_U8, codes, scales, biases, x, y, n, k, group_size, batch,
-                        out_dtype, plan, stream);
+                        out_dtype, plan, nullptr, stream);
 }
 
 qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                           const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
                           int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     return affine_entry(QG_FMT_AFFINE_U8, codes, scales, biases, x, y, n, k, group_size, batch,
-                        out_dtype, nullptr, stream);
+                        out_dtype, nullptr, nullptr, stream);
+}
+
+qg_status qgemv_affine_u8_rmsnorm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                  const uint16_t *x, const uint16_t *gamma, float eps, void *y,
+                                  int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                                  qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream) {
+    const Norm nm{gamma, eps};
+    return affine_entry(QG_FMT_AFFINE_U8, codes, scales, biases, x, y, n, k, group_size, batch,
+                        out_dtype, plan, &nm, stream);
 }
 
 qg_status qgemv_fp8_e4m3_plan(const uint8_t *codes, const float *row_scale, const uint16_t *x,
                               void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
                               const qg_plan *plan, hipStream_t stream) {
-    qg_status st = check_common(QG_FMT_FP8_E4M3, codes, x, y, n, k, batch, out_dtype);
-    if (st != QG_OK) return st;
-    if (!row_scale) return QG_ERR_NULL_POINTER;
-    if (!aligned(row_scale, 4)) return QG_ERR_MISALIGNED;
-    if ((st = check_plan(plan)) != QG_OK) return st;
-    Params p = base_params(QG_FMT_FP8_E4M3, codes, x, y, n, k, out_dtype);
-    p.row_scale = row_scale;
-    return run(QG_FMT_FP8_E4M3, p, batch, plan, stream);
+    return fp8_entry(codes, row_scale, x, y, n, k, batch, out_dtype, plan, nullptr, stream);
 }
 
 qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale, const uint16_t *x, void *y,
                          int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
                          hipStream_t stream) {
-    return qgemv_fp8_e4m3_plan(codes, row_scale, x, y, n, k, batch, out_dtype, nullptr, stream);
+    return fp8_entry(codes, row_scale, x, y, n, k, batch, out_dtype, nullptr, nullptr, stream);
+}
+
+qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, const uint16_t *x,
+                                 const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k,
+                                 int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
+                                 hipStream_t stream) {
+    const Norm nm{gamma, eps};
+    return fp8_entry(codes, row_scale, x, y, n, k, batch, out_dtype, plan, &nm, stream);
+}
+
+qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *out, int64_t k,
+                          int32_t batch, hipStream_t stream) {
+    if (!x || !gamma || !out) return QG_ERR_NULL_POINTER;
+    if (k < 8 || k % 8 || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(out, 16)) return QG_ERR_MISALIGNED;
+    Params p{};
+    p.x = x;
+    p.k = int32_t(k);
+    const Norm nm{gamma, eps};
+    qg_status st = set_norm(p, &nm);
+    if (st != QG_OK) return st;
+    const int64_t lds = int64_t(batch) * ((k / 8 + qg::kWave - 1) / qg::kWave) * 4;
+    if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
+    const dim3 grid(1), block(256);
+    switch (batch) {
+        case 1: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<1>, grid, block, size_t(lds), stream, p, out); break;
+        case 2: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<2>, grid, block, size_t(lds), stream, p, out); break;
+        case 3: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<3>, grid, block, size_t(lds), stream, p, out); break;
+        default: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<4>, grid, block, size_t(lds), stream, p, out); break;
+    }
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out) {
@@ -495,7 +597,7 @@ const char *qg_status_string(qg_status status) {
         case QG_ERR_BAD_BATCH: return "batch must be 1..4";
         case QG_ERR_BAD_DTYPE: return "unknown output dtype or format";
         case QG_ERR_BAD_BITS: return "bits must be 4 or 8";
-        case QG_ERR_BAD_VALUE: return "non-finite weight or out-of-range code";
+        case QG_ERR_BAD_VALUE: return "non-finite weight, out-of-range code, or eps negative or not finite";
         case QG_ERR_TOO_LARGE: return "k * batch exceeds the activation staging limit (qg_max_k)";
         case QG_ERR_DEVICE: return "no usable HIP device";
         case QG_ERR_LAUNCH: return "kernel launch failed";

@@ -45,6 +45,11 @@ struct Params {
     int32_t x_staged;               // row kernel: x shared through LDS (>= 4 waves per workgroup)
     int32_t part_offset;            // row kernel: LDS byte offset of the split-K partials
     int32_t counter_offset;         // row kernel: LDS byte offset of the per-segment tile counters
+    const uint16_t *gamma;          // bf16 [k]: fused RMSNorm weights (norm != 0)
+    float eps;                      // fused RMSNorm epsilon
+    int32_t norm;                   // 1: x is RMS-normalized inside the kernel
+    int32_t norm_offset;            // LDS byte offset of the norm's group sums
+    int32_t gamma_offset;           // row kernel: LDS byte offset of gamma (fused norm)
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
@@ -137,6 +142,33 @@ constexpr int pow2_ceil(int v) {
     return p;
 }
 
+// ------------------------------------------------------------------ fused RMSNorm
+
+// Sum of the squares of the 8 bf16 values of a 16-byte unit, in a fixed order.
+__device__ __forceinline__ float unit_sumsq(const uint4 v) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = bf16_to_f32(w[i] & 0xFFFFu), b = bf16_to_f32(w[i] >> 16);
+        s = fmaf(a, a, s);
+        s = fmaf(b, b, s);
+    }
+    return s;
+}
+
+// bf16_rne(x * r * g) for a pair of bf16 values (x, g in the low and high halves)
+__device__ __forceinline__ uint32_t norm_pair(uint32_t xw, uint32_t gw, float r) {
+    const float lo = (bf16_to_f32(xw & 0xFFFFu) * r) * bf16_to_f32(gw & 0xFFFFu);
+    const float hi = (bf16_to_f32(xw >> 16) * r) * bf16_to_f32(gw >> 16);
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// The normalized activation unit: what a separate RMSNorm would hand over.
+__device__ __forceinline__ uint4 norm_unit(const uint4 x, const uint4 g, float r) {
+    return make_uint4(norm_pair(x.x, g.x, r), norm_pair(x.y, g.y, r), norm_pair(x.z, g.z, r), norm_pair(x.w, g.w, r));
+}
+
 // ------------------------------------------------------------------ launch geometry
 
 // Workgroups are dispatched round-robin over the 8 XCDs; renumbering them so
@@ -160,6 +192,53 @@ __device__ __forceinline__ void wave_rows(const Params &p, int64_t &begin, int64
     const int64_t w = wave_index();
     begin = w * p.n / p.total_waves;
     end = (w + 1) * p.n / p.total_waves;
+}
+
+// RMSNorm factors r[b] = 1 / sqrt(mean_k x[b,k]^2 + eps) for the fused
+// variants, computed by the whole workgroup (every thread must call it).  Row
+// b's 16-byte units are cut into groups of 64 consecutive units; a wave sums a
+// group over its lanes with a fixed butterfly and lane 0 keeps the sum in LDS
+// (gsum); after a barrier every thread adds a row's group sums in group order.
+// So r[b] depends on x[b] and k alone: not on the launch shape, the kernel or
+// the batch size.  Loads go out four groups at a time.  With xdst (and gdst)
+// given, the raw units of x (and of gamma, [k/8]) are copied to LDS on the way.
+template <int B>
+__device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = blockDim.x >> 6;
+    const int w = wave_in_block();
+    const int upr = p.k / 8;                       // 16-byte units per row
+    const int gpr = (upr + kWave - 1) / kWave;     // groups per row
+    const int ng = B * gpr;
+    for (int g0 = w; g0 < ng; g0 += 4 * W) {
+        uint4 v[4], gv[4];
+        int uu[4], bb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gi = min(g0 + i * W, ng - 1);
+            bb[i] = gi / gpr;
+            uu[i] = (gi - bb[i] * gpr) * kWave + lane;
+            v[i] = load_x_unit(p.x + (int64_t(bb[i]) * upr + min(uu[i], upr - 1)) * 8);
+            if (gdst) gv[i] = load_x_unit(p.gamma + int64_t(min(uu[i], upr - 1)) * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool real = g0 + i * W < ng && uu[i] < upr;
+            float sq = real ? unit_sumsq(v[i]) : 0.0f;
+#pragma unroll
+            for (int off = kWave / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
+            if (lane == 0 && g0 + i * W < ng) gsum[g0 + i * W] = sq;
+            if (xdst && real) xdst[bb[i] * upr + uu[i]] = v[i];
+            if (gdst && real && bb[i] == 0) gdst[uu[i]] = gv[i];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float t = 0.0f;
+        for (int g = 0; g < gpr; ++g) t += gsum[b * gpr + g];
+        r[b] = 1.0f / sqrtf(t / float(p.k) + p.eps);
+    }
 }
 
 // ------------------------------------------------------------------ reduction

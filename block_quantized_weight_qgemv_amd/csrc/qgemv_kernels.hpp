@@ -84,11 +84,11 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // when segs > 1): the G waves of segment `seg` share the workgroup's
     // chunks, each streaming that segment of every tile it takes, and a row's
     // segment sums meet in LDS at the end.  Wave gw of a segment starts with
-    // chunk gw.  With x staged, later chunks come from a per-segment LDS
+    // chunk gw.  With x in LDS, later chunks come from a per-segment LDS
     // counter, first come first served (waves dispatched first, or served
     // faster by the memory system, stream more chunks, so the waves of a
     // workgroup finish together), and chunks are small: about 16 per wave,
-    // one tile when there are few.  Otherwise (x not staged, or one wave per
+    // one tile when there are few.  Otherwise (x not in LDS, or one wave per
     // segment) each wave has one chunk.
     const int S = p.segs;
     const int nb = gridDim.x;
@@ -102,22 +102,40 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     const int c_lo = seg * p.seg_chunks;
     const int c_hi = min(p.chunks, c_lo + p.seg_chunks);
 
-    // ---- activations.  With p.x_staged, waves 0..3 of the workgroup load all
-    // of x with coalesced 16-byte loads and the workgroup shares it through
-    // LDS; otherwise every wave loads its own slice.  The later waves of a
-    // workgroup are dispatched after the weight stream of the whole chip has
-    // started, and their own activation loads would wait behind it (about
-    // 1.5 us at the start of a 30720 x 3840 FP4 matvec); through LDS they get
-    // x as soon as the first four waves have it.
+    // ---- activations.  Three ways in, each ending with the wave's slice of x
+    // in registers:
+    //  * staged (p.x_staged): waves 0..3 of the workgroup load all of x with
+    //    coalesced 16-byte loads and the workgroup shares it through LDS.  The
+    //    later waves of a workgroup are dispatched after the weight stream of
+    //    the whole chip has started, and their own activation loads would wait
+    //    behind it (about 1.5 us at the start of a 30720 x 3840 FP4 matvec);
+    //    through LDS they get x as soon as the first four waves have it.
+    //  * fused RMSNorm (p.norm): the workgroup first computes every batch
+    //    row's norm factor, copying raw x and gamma to LDS on the way; once
+    //    the wave's first weight step is out, x is normalized in LDS in place
+    //    and read from there as in the staged case.
+    //  * otherwise every wave loads its own slice.
+    float rn[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) rn[b] = 1.0f;
+    const bool norm = p.norm != 0;                        // uniform
+    uint4 *xlds = reinterpret_cast<uint4 *>(smem);
+    uint4 *glds = reinterpret_cast<uint4 *>(smem + p.gamma_offset);
+    if (norm) block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds);
+    const int upr = p.k / 8;                              // 16-byte units per row of x
+
     constexpr bool kCanStage = row_can_stage(B, J, Fmt::kPieces);
-    const bool staged = kCanStage && p.x_staged != 0;     // uniform
-    const bool shared = staged && G > 1;                  // uniform: tiles handed out through LDS
+    const bool staged = !norm && kCanStage && p.x_staged != 0;    // uniform
+    const bool via_lds = staged || norm;                  // uniform: x reaches the waves through LDS
+    const bool shared = via_lds && G > 1;                 // uniform: tiles handed out through LDS
     const int C = shared ? max(1, T / (kChunksPerWave * G)) : max(1, (T + G - 1) / G);    // tiles per chunk
     const int x_units = B * p.k / 8;                      // 16-byte units of x
     const bool few_units = x_units <= 2 * kStageThreads;  // uniform
     uint4 xr[kCanStage ? kStageUnits : 1];
     uint4 xraw[B][J][Fmt::kRawUnits];
-    if (!staged) {
+    // the staging threads' units (clamped indices repeat the last unit)
+    auto stage_unit_index = [&](int i) { return min(int(threadIdx.x) + i * kStageThreads, x_units - 1); };
+    if (!via_lds) {
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -127,17 +145,15 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
                 for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = load_x_unit(xc + 8 * u);
             }
-    } else if (kCanStage && w < kStageThreads / kWave) {
-        // a fixed number of loads per thread (2 or 8; clamped indices repeat
-        // the last unit), so that the waits stay exact
+    } else if (staged && kCanStage && w < kStageThreads / kWave) {
+        // a fixed number of loads per thread (2 or 8), so that the waits stay
+        // exact
         if (few_units) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                xr[i] = load_x_unit(p.x + int64_t(min(int(threadIdx.x) + i * kStageThreads, x_units - 1)) * 8);
+            for (int i = 0; i < 2; ++i) xr[i] = load_x_unit(p.x + int64_t(stage_unit_index(i)) * 8);
         } else if constexpr (kCanStage) {
 #pragma unroll
-            for (int i = 0; i < kStageUnits; ++i)
-                xr[i] = load_x_unit(p.x + int64_t(min(int(threadIdx.x) + i * kStageThreads, x_units - 1)) * 8);
+            for (int i = 0; i < kStageUnits; ++i) xr[i] = load_x_unit(p.x + int64_t(stage_unit_index(i)) * 8);
         }
     }
 
@@ -185,10 +201,6 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         }
     };
 
-    // The wave's first tile goes out right behind the activations, then the wave waits for
-    // the activations alone (loads retire in order) before it issues the rest
-    // of the prefetch: the first burst of weight requests over the whole chip
-    // is one tile per wave, and the activations are not queued behind it.
     // The wave's tiles in order: `cur` walks the current chunk; when the
     // chunk is used up the next one is taken, only when its first tile is
     // needed (so the wave's first tile never touches the counter, which is
@@ -214,22 +226,32 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         cur = __builtin_amdgcn_readfirstlane(cur < T ? cur + 1 : cur);
         return __builtin_amdgcn_readfirstlane(t);
     };
+    // The wave's first tile goes out right behind the activations, then the
+    // wave waits for the activations alone (loads retire in order) before it
+    // issues the rest of the prefetch: the first burst of weight requests over
+    // the whole chip is one tile per wave, and the activations are not queued
+    // behind it.
     Buf buf[D];
     int tl[D];                               // tile in each buffer (uniform)
     tl[0] = next_issue();
     issue(buf[0], tl[0]);
-    if (!staged) {
+    if (!via_lds) {
         wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
     } else {
-        uint4 *xlds = reinterpret_cast<uint4 *>(smem);
-        if (w < kStageThreads / kWave) {
+        if (norm) {
+            // normalize x in LDS in place (no global loads: the waits of the
+            // weight loads already in flight are not disturbed)
+            for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
+                const int b = u / upr;
+                xlds[u] = norm_unit(xlds[u], glds[u - b * upr], pick_uniform(rn, b));
+            }
+        } else if (w < kStageThreads / kWave) {
             if (few_units) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i) xlds[min(int(threadIdx.x) + i * kStageThreads, x_units - 1)] = xr[i];
+                for (int i = 0; i < 2; ++i) xlds[stage_unit_index(i)] = xr[i];
             } else if constexpr (kCanStage) {
 #pragma unroll
-                for (int i = 0; i < kStageUnits; ++i)
-                    xlds[min(int(threadIdx.x) + i * kStageThreads, x_units - 1)] = xr[i];
+                for (int i = 0; i < kStageUnits; ++i) xlds[stage_unit_index(i)] = xr[i];
             }
         }
         if (shared && int(threadIdx.x) < S) counter[threadIdx.x] = unsigned(G);   // next shared chunk
@@ -326,21 +348,21 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 
     // The buffers hold the wave's tiles in order, so the first one past the
     // end ends its work.  After each tile the buffer is refilled at once (an
-    // empty tile past the end costs no memory traffic).
-    bool more = tl[0] < T;
-    while (more) {
+    // empty tile past the end costs no memory traffic).  The loop is left by
+    // a jump: every way back to its head then passes all D refills, which is
+    // what lets the compiler's waits before a tile count exactly the loads
+    // of the other buffers.
+    for (;;) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            if (tl[d] >= T) {
-                more = false;
-                break;
-            }
+            if (tl[d] >= T) goto done;
             const int nt = next_issue();
             consume(buf[d], tl[d]);
             tl[d] = nt;
             issue(buf[d], nt);
         }
     }
+done:
     wait_vm_loads<0>();
 
     if (S > 1) {
@@ -380,6 +402,12 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     using Buf = typename LdsKernel<Fmt, R, B, D>::Buf;
     const int lane = threadIdx.x & (kWave - 1);
+    // fused RMSNorm: every batch row's factor, before any weight load
+    float rn[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) rn[b] = 1.0f;
+    const bool norm = p.norm != 0;                        // uniform
+    if (norm) block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, nullptr, nullptr);
     int64_t r_begin, r_end;
     wave_rows(p, r_begin, r_end);
     const int tiles = int((r_end - r_begin + R - 1) / R);
@@ -422,16 +450,20 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         const int b = u / units_per_row;
         return load_x_unit(p.x + int64_t(b) * p.k + (u - b * units_per_row) * 8);
     };
+    auto gamma_unit = [&](int u) -> uint4 {
+        return load_x_unit(p.gamma + (u - (u / units_per_row) * units_per_row) * 8);
+    };
     // Every lane runs the same staging code and stores unconditionally (an
     // out-of-range unit is clamped to the last one and stored to the sink),
     // so no activation load is sunk into a conditional block below the
     // prefetch.
-    auto stage_unit = [&](int u_in, const uint4 v) {
+    auto stage_unit = [&](int u_in, const uint4 v_raw, const uint4 g) {
         const bool st = u_in < x_units;
         const int u = st ? u_in : x_units - 1;
         const int b = u / units_per_row;
         const int e = (u - b * units_per_row) * 8;
         const int c = e / Fmt::kWpc, ru = (e % Fmt::kWpc) / 8;
+        const uint4 v = norm ? norm_unit(v_raw, g, pick_uniform(rn, b)) : v_raw;
         uint4 pc[Fmt::kPpu];
         Fmt::unit_pieces(v, pc);
 #pragma unroll
@@ -448,9 +480,16 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         }
     };
     constexpr int kXU = 8;
-    uint4 xr[kXU];
+    uint4 xr[kXU], gr[kXU];
 #pragma unroll
     for (int i = 0; i < kXU; ++i) xr[i] = x_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
+    if (norm) {
+#pragma unroll
+        for (int i = 0; i < kXU; ++i) gr[i] = gamma_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
+    } else {
+#pragma unroll
+        for (int i = 0; i < kXU; ++i) gr[i] = make_uint4(0, 0, 0, 0);
+    }
 
     // step 0 right behind the activations, the rest once they are in (as in
     // the row kernel)
@@ -461,12 +500,12 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
 
 #pragma unroll
-    for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i]);
+    for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i], gr[i]);
     // activations beyond kXU units per thread; the trip count is the same for
     // every lane of a wave
     for (int base = kXU * blockDim.x; base < x_units; base += blockDim.x) {
-        const int u = base + threadIdx.x;
-        stage_unit(u, x_unit(min(u, x_units - 1)));
+        const int u = min(base + int(threadIdx.x), x_units - 1);
+        stage_unit(base + threadIdx.x, x_unit(u), norm ? gamma_unit(u) : make_uint4(0, 0, 0, 0));
     }
     __syncthreads();
 
@@ -512,6 +551,25 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     };
 
     run_pipeline<D>(buf, steps, issue, consume);
+}
+
+// ------------------------------------------------------------------ standalone norm
+
+// The fused variants' RMSNorm on its own: out[b, k] = bf16_rne(x * r[b] *
+// gamma), with r[b] summed exactly as the fused matvec sums it (block_rms).
+// One workgroup does the whole [B, k] block.
+template <int B>
+__global__ void __launch_bounds__(256) qg_rmsnorm_kernel(const Params p, uint16_t *out) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    float rn[B];
+    block_rms<B>(p, reinterpret_cast<float *>(smem), rn, nullptr, nullptr);
+    const int upr = p.k / 8;
+    for (int u = threadIdx.x; u < B * upr; u += blockDim.x) {
+        const int b = u / upr;
+        const uint4 xv = load_x_unit(p.x + int64_t(u) * 8);
+        const uint4 gv = load_x_unit(p.gamma + int64_t(u - b * upr) * 8);
+        *reinterpret_cast<uint4 *>(out + int64_t(u) * 8) = norm_unit(xv, gv, pick_uniform(rn, b));
+    }
 }
 
 }  // namespace qg

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 1
+#define QG_ABI_VERSION 2
 
 typedef enum qg_status {
     QG_OK = 0,
@@ -63,7 +63,8 @@ typedef enum qg_status {
     QG_ERR_BAD_BATCH = 5,
     QG_ERR_BAD_DTYPE = 6,
     QG_ERR_BAD_BITS = 7,
-    QG_ERR_BAD_VALUE = 8,     /* a quantizer was given a non-finite weight   */
+    QG_ERR_BAD_VALUE = 8,     /* a quantizer was given a non-finite weight,
+                                 or a fused norm a negative / non-finite eps */
     QG_ERR_TOO_LARGE = 9,     /* k * batch beyond the activation staging limit */
     QG_ERR_DEVICE = 10,       /* no usable HIP device / attribute query failed */
     QG_ERR_LAUNCH = 11        /* the kernel launch itself failed              */
@@ -185,6 +186,61 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
 
 /* Static English description of a status; never NULL. */
 const char *qg_status_string(qg_status status);
+
+/* ------------------------------------------------------------------------
+ * Fused RMSNorm variants: y = W . RMSNorm(x), in one launch.
+ *
+ * "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus (Part 2)",
+ * section "What's next", ranks RMSNorm fusion into the decode step's matvecs
+ * among the next levers (the norm takes hundreds of launches per token).  The
+ * page does not print the norm; these calls take the standard one, row by row:
+ *
+ *     r[b]    = 1 / sqrt( (1/k) * sum_k x[b,k]^2 + eps )          (fp32)
+ *     x~[b,k] = bf16_rne( (x[b,k] * r[b]) * gamma[k] )             (fp32 products)
+ *
+ * and compute the matvec of x~, exactly what the plain entry point returns
+ * for an x~ computed by a separate norm (up to that norm's own rounding of
+ * r[b]).  Models that scale by (1 + gamma) pass that vector as gamma.
+ *
+ *   gamma  bf16 [k] (DEVICE), 16-byte aligned     else QG_ERR_NULL_POINTER /
+ *                                                  QG_ERR_MISALIGNED
+ *   eps    >= 0 and finite                        else QG_ERR_BAD_VALUE
+ *   plan   as in the *_plan variants (NULL: the default launch)
+ *   x and gamma are held in LDS together: (batch + 1) * k * 2 bytes must fit
+ *   the same 128 KiB as the staging limit, else QG_ERR_TOO_LARGE
+ *
+ * Everything else (arguments, layouts, errors, accuracy, determinism, batch
+ * consistency) is as in the plain calls.  r[b] is summed in an order fixed by
+ * k, so the result is also bitwise the same for every plan and batch size.
+ * x itself is not modified.
+ * ---------------------------------------------------------------------- */
+
+qg_status qgemv_fp4_e2m1_rmsnorm(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                                 const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k,
+                                 int32_t group_size, int32_t batch, qg_out_dtype out_dtype,
+                                 const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_affine_u4_rmsnorm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                  const uint16_t *x, const uint16_t *gamma, float eps, void *y,
+                                  int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                                  qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_affine_u8_rmsnorm(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                  const uint16_t *x, const uint16_t *gamma, float eps, void *y,
+                                  int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                                  qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, const uint16_t *x,
+                                 const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k,
+                                 int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
+                                 hipStream_t stream);
+
+/* The fused variants' RMSNorm on its own: out[b, k] = x~[b, k] as defined
+ * above, with r[b] summed exactly as the fused matvec sums it, so the plain
+ * entry point fed `out` returns bitwise what the fused variant returns.  For
+ * consumers that need the normalized activations themselves.
+ *   x, out   bf16 [batch, k] (DEVICE), gamma bf16 [k] (DEVICE), all 16-byte
+ *            aligned; 8 <= k, k % 8 == 0; 1 <= batch <= 4; eps as above.
+ * One workgroup, asynchronous on `stream`. */
+qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *out, int64_t k,
+                          int32_t batch, hipStream_t stream);
 
 /* QG_ABI_VERSION of the loaded library. */
 int qg_abi_version(void);

@@ -25,12 +25,17 @@ def rms_factor(x_bits, eps):
     return 1.0 / np.sqrt(np.mean(x * x, axis=1) + float(eps))
 
 
-def rmsnorm_bf16(x_bits, gamma_bits, eps):
-    """bf16 bits [B, K] of x~ = bf16_rne(x * r * gamma)."""
+def rmsnorm_f64(x_bits, gamma_bits, eps):
+    """x * r * gamma in float64 [B, K], before the rounding to bf16."""
     x_bits = np.atleast_2d(np.asarray(x_bits, dtype=np.uint16))
     x = bf16_bits_to_f64(x_bits)
     g = bf16_bits_to_f64(np.asarray(gamma_bits, dtype=np.uint16))
     if g.shape != (x.shape[1],):
         raise ValueError("gamma has shape %s, K=%d" % (g.shape, x.shape[1]))
     r = rms_factor(x_bits, eps)
-    return f64_to_bf16_bits(x * r[:, None] * g[None, :])
+    return x * r[:, None] * g[None, :]
+
+
+def rmsnorm_bf16(x_bits, gamma_bits, eps):
+    """bf16 bits [B, K] of x~ = bf16_rne(x * r * gamma)."""
+    return f64_to_bf16_bits(rmsnorm_f64(x_bits, gamma_bits, eps))

@@ -50,7 +50,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert q.qg_abi_version() == 1
+    assert q.qg_abi_version() == 2
     for s in range(12):
         assert isinstance(q.qg_status_string(s), str) and q.qg_status_string(s)
     assert q.qg_status_string(999) == "unknown status"
