@@ -37,7 +37,8 @@ METRIC = "quantized GEMV HBM GB/s & % of 8 TB/s peak; µs per Gemma-12B-shaped m
 ROT_BYTES = 1 << 30
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "block_quantized_weight_qgemv_amd", "csrc")
-KERNEL_SOURCES = ["qgemv_common.hpp", "qgemv_formats.hpp", "qgemv_kernels.hpp", "qgemv_api.hip"]
+KERNEL_SOURCES = ["qgemv_common.hpp", "qgemv_formats.hpp", "qgemv_kernels.hpp", "qgemv_launch.hpp", "qgemv_api.hip",
+                  "qgemv_fp4.hip"]
 # rocprofv3 FETCH_SIZE / WRITE_SIZE of the default workload, each scaled by
 # what the counter reads for a plain copy of known size; written by
 # --summarize-pmc and only used while the kernel sources are unchanged
@@ -326,28 +327,70 @@ def run_sweep(args):
 
 
 def run_decode_step(args, layers=48):
-    """The FP4 decode step: qkv, o_proj, gate_up, fc_down for 48 distinct layers."""
+    """The FP4 decode step: qkv, o_proj, gate_up, fc_down for 48 distinct layers.
+
+    Also the step with an RMSNorm before qkv and before gate_up (the two norms
+    of a pre-norm decoder layer), once fused into those matvecs and once as
+    separate norm launches (the same norm arithmetic) ahead of plain matvecs."""
     import torch
+    import block_quantized_weight_qgemv_amd as q
     shapes = ["qkv", "o_proj", "gate_up", "fc_down"]
     wls = [Workload("fp4", s, batch=1, gs=32, copies=layers) for s in shapes]
     total = sum(w.bytes for w in wls) * layers
+    per_step = layers * len(shapes)
+    reps = 10                     # decode steps per timed region (~15 ms)
+
+    def timed(launch, n_launch):
+        ms_runs = [time_steps(launch, per_step * reps, per_step * 2, args.mode) / reps for _ in range(3)]
+        ms = float(np.median(ms_runs))
+        gbs = total / (ms * 1e-3) / 1e9
+        return ms, gbs
 
     def launch(i):
         layer = i // len(shapes)
         wls[i % len(shapes)].launch(layer)
 
-    per_step = layers * len(shapes)
-    reps = 10                     # decode steps per timed region (~15 ms)
-    ms_runs = [time_steps(launch, per_step * reps, per_step * 2, args.mode) / reps for _ in range(3)]
-    ms = float(np.median(ms_runs))
-    steps = per_step
-    gbs = total / (ms * 1e-3) / 1e9
+    ms, gbs = timed(launch, per_step)
     log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  (192 launches per step; 10 steps per region, median of 3)"
         % ("fp4 48-layer decode step", ms * 1e3, gbs, 100 * gbs / HBM_PEAK_GBS))
+    row = {"fmt": "fp4", "shape": "decode_step_48_layers", "bytes": total, "launches": per_step,
+           "us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+
+    # with the two RMSNorms per layer
+    normed = {0: 3840, 2: 3840}           # shape index -> k (qkv and gate_up read the normed stream)
+    rng = np.random.default_rng(7)
+    gammas = {si: torch.from_numpy(rng.uniform(0.5, 1.5, k).astype(np.float32)).to("cuda:0").to(torch.bfloat16)
+              for si, k in normed.items()}
+    xn = {si: torch.empty_like(wls[si].x) for si in normed}
+
+    def launch_fused(i):
+        layer, si = i // len(shapes), i % len(shapes)
+        w = wls[si]
+        if si in normed:
+            d = w.dev[layer % w.copies]
+            q.qgemv_fp4_e2m1_rmsnorm(d[0], d[1], w.x, gammas[si], 1e-6, w.y, 32)
+        else:
+            w.launch(layer)
+
+    def launch_separate(i):
+        layer, si = i // len(shapes), i % len(shapes)
+        w = wls[si]
+        if si in normed:
+            d = w.dev[layer % w.copies]
+            q.qg_rmsnorm_bf16(w.x, gammas[si], 1e-6, xn[si])
+            q.qgemv_fp4_e2m1(d[0], d[1], xn[si], w.y, 32)
+        else:
+            w.launch(layer)
+
+    for name, fn, n_launch, key in (("fused", launch_fused, per_step, "norm_fused_us"),
+                                    ("separate", launch_separate, per_step + 2 * layers, "norm_separate_us")):
+        ms_n, gbs_n = timed(fn, n_launch)
+        row[key] = round(ms_n * 1e3, 2)
+        log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  (%d launches per step)"
+            % ("fp4 48-layer step + 96 RMSNorms, %s" % name, ms_n * 1e3, gbs_n, 100 * gbs_n / HBM_PEAK_GBS, n_launch))
     del wls
     torch.cuda.empty_cache()
-    return {"fmt": "fp4", "shape": "decode_step_48_layers", "bytes": total, "launches": steps,
-            "us": round(ms * 1e3, 2), "GBps": round(gbs, 1), "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4)}
+    return row
 
 
 def run_probe(args):

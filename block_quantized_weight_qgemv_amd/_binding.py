@@ -9,6 +9,10 @@ import os
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
+# QG_ABI_VERSION of include/qgemv.h that these declarations follow; a
+# library that reports another version is refused at load.
+ABI_VERSION = 2
+
 QG_OK = 0
 QG_OUT_F32 = 0
 QG_OUT_BF16 = 1
@@ -87,4 +91,7 @@ def load(path=LIB_PATH):
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.qg_abi_version() != ABI_VERSION:
+        raise ImportError("%s reports ABI version %d, the binding declares %d: rebuild the library"
+                          % (path, lib.qg_abi_version(), ABI_VERSION))
     return lib

@@ -41,16 +41,34 @@ def _run(cmd):
     return out
 
 
+HIP_SOURCES = ["qgemv_api.hip", "qgemv_fp4.hip", "qgemv_affine_u4.hip", "qgemv_affine_u8.hip", "qgemv_fp8.hip"]
+
+
 def build(verbose=False):
-    """Compile every source and link libqgemv.so next to this file."""
+    """Compile every source (in parallel: each format's kernel instances are a
+    file of their own) and link libqgemv.so next to this file."""
     with tempfile.TemporaryDirectory(prefix="qgemv_build_") as tmp:
-        api_o = os.path.join(tmp, "qgemv_api.o")
+        jobs = []
+        for src in HIP_SOURCES:
+            obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
+            jobs.append((obj, [HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]))
         pack_o = os.path.join(tmp, "pack.o")
-        out = _run([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, "qgemv_api.hip"), "-o", api_o])
-        out += _run(["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "pack.cpp"), "-o", pack_o])
+        jobs.append((pack_o, ["g++"] + HOST_FLAGS + ["-c", os.path.join(CSRC, "pack.cpp"), "-o", pack_o]))
+        procs = [(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+                 for _, cmd in jobs]
+        out, failed = "", []
+        for cmd, pr in procs:
+            text = pr.communicate()[0]
+            text = "\n".join(l for l in text.splitlines() if "packed-fp32-ops" not in l)
+            out += text
+            if pr.returncode != 0:
+                sys.stderr.write(text + "\n")
+                failed.append(" ".join(cmd))
+        if failed:
+            raise RuntimeError("build step failed: %s" % failed[0])
         tmp_lib = os.path.join(tmp, "libqgemv.so")
-        out += _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", api_o, pack_o,
-                     "-o", tmp_lib, "-lpthread"])
+        out += _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC"] + [o for o, _ in jobs] +
+                    ["-o", tmp_lib, "-lpthread"])
         shutil.move(tmp_lib, LIB)
     if verbose and out.strip():
         print(out)

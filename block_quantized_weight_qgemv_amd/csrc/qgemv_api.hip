@@ -1,5 +1,6 @@
 // C ABI of the block-quantized weight matvec: argument validation, launch
-// planning and dispatch to the kernel templates in qgemv_kernels.hpp.
+// planning and dispatch to the per-format launchers (qgemv_launch.hpp; the
+// kernel instances of each format are compiled in a file of their own).
 //
 // Validation runs completely before any HIP call, so a bad argument never
 // launches anything and never touches y.  The only state kept across calls is
@@ -7,6 +8,7 @@
 // have had their LDS limit raised; both are filled once, thread-safely.
 
 #include "qgemv.h"
+#include "qgemv_launch.hpp"
 #include "qgemv_kernels.hpp"
 #include "stream_probe.hpp"
 
@@ -16,11 +18,9 @@
 namespace {
 
 using qg::Params;
+using qgl::kMaxLds;
+using qgl::Plan;
 
-// Largest dynamic LDS a workgroup may use for the staged activations.  MI355X
-// has 160 KiB of LDS per compute unit; 128 KiB leaves room for a second,
-// smaller workgroup.
-constexpr int64_t kMaxLds = 128 * 1024;
 constexpr int64_t kCounterBytes = 32;     // row kernel: up to 8 per-segment tile counters
 constexpr int kMaxDevices = 64;
 
@@ -99,14 +99,6 @@ qg_status device_cus(int *cus) {
 
 // ---------------------------------------------------------------- planning
 
-struct Plan {
-    int rows_per_tile;
-    int waves_per_block;
-    int blocks;
-    bool row_kernel;       // x in registers (row kernel) or staged in LDS
-    int passes;            // row kernel: passes per K segment (1, 2 or 4)
-};
-
 int passes_of(int64_t chunks) { return int((chunks + qg::kWave - 1) / qg::kWave); }
 
 // The row kernel keeps each wave's slice of x in registers: rows are cut into
@@ -184,86 +176,11 @@ Plan default_plan(qg_format f, const Params &p, int32_t batch, int cus) {
     return pl;
 }
 
-// ---------------------------------------------------------------- dispatch
-
-template <class Kern>
-qg_status launch(Kern kern, const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
-    if (lds > 64 * 1024) {
-        static std::once_flag attr_once;
-        static hipError_t attr_err = hipSuccess;
-        std::call_once(attr_once, [&] {
-            attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
-        });
-        if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
-    }
-    hipLaunchKernelGGL(kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
-}
-
-// prefetch depth: about 8 code loads in flight per lane
-// (two when more than 16 activation pieces already fill the registers)
-constexpr int row_depth(int r, int j, int pieces) { return pieces > 16 ? 2 : (8 / (r * j) > 2 ? 8 / (r * j) : 2); }
-constexpr int lds_depth(int r) { return r == 1 ? 8 : 4; }
-
-// register budget of the row kernel: at most 32 activation pieces per lane,
-// and fewer rows per tile when they are many (one row for the affine formats,
-// whose chunk sums and biases take further registers); no instance spills
-template <class Fmt, int R, int B, int J>
-constexpr bool row_instance() {
-    return B * J * Fmt::kPieces <= 32 && (B * J * Fmt::kPieces <= 16 || R <= (Fmt::kSums ? 1 : 2)) &&
-           !(R == 4 && J == 4);
-}
-
-template <class Fmt, int R, int B>
-qg_status launch_row_j(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
-    switch (pl.passes) {
-        case 1:
-            if constexpr (row_instance<Fmt, R, B, 1>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1, B * 1 * Fmt::kPieces), 1>, p, pl, lds, s);
-            break;
-        case 2:
-            if constexpr (row_instance<Fmt, R, B, 2>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2, B * 2 * Fmt::kPieces), 2>, p, pl, lds, s);
-            break;
-        case 4:
-            if constexpr (row_instance<Fmt, R, B, 4>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4, B * 4 * Fmt::kPieces), 4>, p, pl, lds, s);
-            break;
-    }
-    return QG_ERR_LAUNCH;     // not reached: run() only picks existing instances
-}
-
-template <class Fmt, int R, int B>
-qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
-    if (pl.row_kernel) return launch_row_j<Fmt, R, B>(p, pl, lds, s);
-    return launch(qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R)>, p, pl, lds, s);
-}
-
 // Whether a row-kernel instance exists for these (R, B, passes).
 template <class Fmt>
 bool row_instance_exists(int r, int b, int j) {
     const int pcs = Fmt::kPieces;
     return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= (Fmt::kSums ? 1 : 2)) && !(r == 4 && j == 4);
-}
-
-template <class Fmt, int R>
-qg_status launch_r(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
-    switch (batch) {
-        case 1: return launch_rb<Fmt, R, 1>(p, pl, lds, s);
-        case 2: return launch_rb<Fmt, R, 2>(p, pl, lds, s);
-        case 3: return launch_rb<Fmt, R, 3>(p, pl, lds, s);
-        default: return launch_rb<Fmt, R, 4>(p, pl, lds, s);
-    }
-}
-
-template <class Fmt>
-qg_status launch_fmt(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
-    switch (pl.rows_per_tile) {
-        case 1: return launch_r<Fmt, 1>(p, pl, batch, lds, s);
-        case 2: return launch_r<Fmt, 2>(p, pl, batch, lds, s);
-        default: return launch_r<Fmt, 4>(p, pl, batch, lds, s);
-    }
 }
 
 qg_status check_plan(const qg_plan *plan) {
@@ -356,10 +273,10 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
     }
     p.total_waves = pl.blocks * pl.waves_per_block;
     switch (f) {
-        case QG_FMT_FP4_E2M1: return launch_fmt<qg::FmtFP4>(p, pl, batch, lds, stream);
-        case QG_FMT_AFFINE_U4: return launch_fmt<qg::FmtAffineU4>(p, pl, batch, lds, stream);
-        case QG_FMT_AFFINE_U8: return launch_fmt<qg::FmtAffineU8>(p, pl, batch, lds, stream);
-        default: return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, stream);
+        case QG_FMT_FP4_E2M1: return qgl::launch_fp4(p, pl, batch, lds, stream);
+        case QG_FMT_AFFINE_U4: return qgl::launch_affine_u4(p, pl, batch, lds, stream);
+        case QG_FMT_AFFINE_U8: return qgl::launch_affine_u8(p, pl, batch, lds, stream);
+        default: return qgl::launch_fp8(p, pl, batch, lds, stream);
     }
 }
 

@@ -200,19 +200,23 @@ __device__ __forceinline__ void wave_rows(const Params &p, int64_t &begin, int64
 // group over its lanes with a fixed butterfly and lane 0 keeps the sum in LDS
 // (gsum); after a barrier every thread adds a row's group sums in group order.
 // So r[b] depends on x[b] and k alone: not on the launch shape, the kernel or
-// the batch size.  Loads go out four groups at a time.  With xdst (and gdst)
-// given, the raw units of x (and of gamma, [k/8]) are copied to LDS on the way.
-template <int B>
-__device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst) {
+// the batch size.  Loads go out four groups per wave at a time; `between` is
+// called once by every wave right after its first four loads are issued (the
+// caller can send its own loads behind them and wait for these alone).  With
+// xdst (and gdst) given, the raw units of x (and of gamma, [k/8]) are copied
+// to LDS on the way.
+template <int B, class Between>
+__device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst,
+                                          Between &&between) {
     const int lane = threadIdx.x & (kWave - 1);
     const int W = blockDim.x >> 6;
     const int w = wave_in_block();
     const int upr = p.k / 8;                       // 16-byte units per row
     const int gpr = (upr + kWave - 1) / kWave;     // groups per row
     const int ng = B * gpr;
-    for (int g0 = w; g0 < ng; g0 += 4 * W) {
-        uint4 v[4], gv[4];
-        int uu[4], bb[4];
+    uint4 v[4], gv[4];
+    int uu[4], bb[4];
+    auto load_round = [&](int g0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int gi = min(g0 + i * W, ng - 1);
@@ -221,6 +225,8 @@ __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&
             v[i] = load_x_unit(p.x + (int64_t(bb[i]) * upr + min(uu[i], upr - 1)) * 8);
             if (gdst) gv[i] = load_x_unit(p.gamma + int64_t(min(uu[i], upr - 1)) * 8);
         }
+    };
+    auto sum_round = [&](int g0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool real = g0 + i * W < ng && uu[i] < upr;
@@ -231,6 +237,13 @@ __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&
             if (xdst && real) xdst[bb[i] * upr + uu[i]] = v[i];
             if (gdst && real && bb[i] == 0) gdst[uu[i]] = gv[i];
         }
+    };
+    load_round(w);                 // every wave, even one with no group (clamped loads)
+    between();
+    sum_round(w);
+    for (int g0 = w + 4 * W; g0 < ng; g0 += 4 * W) {
+        load_round(g0);
+        sum_round(g0);
     }
     __syncthreads();
 #pragma unroll

@@ -30,6 +30,9 @@
 //    in LDS, and each lane loads its own group parameter.
 #pragma once
 
+#include <type_traits>
+#include <utility>
+
 #include "qgemv_common.hpp"
 #include "qgemv_formats.hpp"
 
@@ -61,6 +64,13 @@ __device__ __forceinline__ void run_pipeline(Buf (&buf)[D], int steps, Issue &&i
 
 // ------------------------------------------------------------------ short rows
 
+// step(integral_constant<int, d>) for d = 0, 1, ... in order, stopping at
+// the first that returns false; true when every step ran.
+template <class Step, int... d>
+__device__ __forceinline__ bool steps_in_order(Step &step, std::integer_sequence<int, d...>) {
+    return (step(std::integral_constant<int, d>{}) && ...);
+}
+
 template <class Fmt, int R, int B, int D, int J>
 struct RowKernel {
     static constexpr int NA = Fmt::kAuxArrays > 0 ? Fmt::kAuxArrays : 1;
@@ -71,7 +81,7 @@ struct RowKernel {
     };
 };
 
-template <class Fmt, int R, int B, int D, int J>
+template <class Fmt, int R, int B, int D, int J, bool kNorm>
 __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     using K = RowKernel<Fmt, R, B, D, J>;
     using Buf = typename K::Buf;
@@ -110,18 +120,18 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     //    the whole chip has started, and their own activation loads would wait
     //    behind it (about 1.5 us at the start of a 30720 x 3840 FP4 matvec);
     //    through LDS they get x as soon as the first four waves have it.
-    //  * fused RMSNorm (p.norm): the workgroup first computes every batch
-    //    row's norm factor, copying raw x and gamma to LDS on the way; once
-    //    the wave's first weight step is out, x is normalized in LDS in place
-    //    and read from there as in the staged case.
+    //  * fused RMSNorm (p.norm): the workgroup computes every batch row's
+    //    norm factor, copying raw x and gamma to LDS on the way (its loads go
+    //    out ahead of the wave's first weight step, as x's do in the other
+    //    cases); after a barrier the workgroup normalizes x in LDS in place
+    //    and, after another, every wave reads its slice as in the staged case.
     //  * otherwise every wave loads its own slice.
     float rn[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) rn[b] = 1.0f;
-    const bool norm = p.norm != 0;                        // uniform
+    constexpr bool norm = kNorm;                          // a separate instance: no cost to the plain call
     uint4 *xlds = reinterpret_cast<uint4 *>(smem);
     uint4 *glds = reinterpret_cast<uint4 *>(smem + p.gamma_offset);
-    if (norm) block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds);
     const int upr = p.k / 8;                              // 16-byte units per row of x
 
     constexpr bool kCanStage = row_can_stage(B, J, Fmt::kPieces);
@@ -171,7 +181,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         const int c = c_lo + kWave * j + lane;
         return c < c_hi ? uint32_t(c) * kChunkBytes : kOutOfRange;
     };
-    auto issue = [&](Buf &bf, int t_in) {
+    auto issue = [&](Buf &bf, int t_in) __attribute__((always_inline)) {
         // t is the same in every lane; saying so keeps the resources in scalar
         // registers (a resource the compiler cannot prove uniform is used
         // through a loop over its distinct values)
@@ -212,7 +222,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // divergent, and every load and wait in the loop conservative.
     unsigned *counter = reinterpret_cast<unsigned *>(smem + p.counter_offset);
     int chunk = gw, cur = gw * C;
-    auto next_issue = [&]() -> int {
+    auto next_issue = [&]() __attribute__((always_inline)) -> int {
         const bool at_end = cur < T && cur == (chunk + 1) * C;    // chunk used up
         int taken = chunk + G;
         if (shared && at_end) {
@@ -234,27 +244,17 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     Buf buf[D];
     int tl[D];                               // tile in each buffer (uniform)
     tl[0] = next_issue();
-    issue(buf[0], tl[0]);
-    if (!via_lds) {
-        wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
-    } else {
-        if (norm) {
-            // normalize x in LDS in place (no global loads: the waits of the
-            // weight loads already in flight are not disturbed)
-            for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
-                const int b = u / upr;
-                xlds[u] = norm_unit(xlds[u], glds[u - b * upr], pick_uniform(rn, b));
-            }
-        } else if (w < kStageThreads / kWave) {
-            if (few_units) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) xlds[stage_unit_index(i)] = xr[i];
-            } else if constexpr (kCanStage) {
-#pragma unroll
-                for (int i = 0; i < kStageUnits; ++i) xlds[stage_unit_index(i)] = xr[i];
-            }
-        }
+    if constexpr (norm) {
         if (shared && int(threadIdx.x) < S) counter[threadIdx.x] = unsigned(G);   // next shared chunk
+        block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds, [&] {
+            issue(buf[0], tl[0]);
+            wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+        });
+        // normalize x in LDS in place, the work spread over the workgroup
+        for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
+            const int b = u / upr;
+            xlds[u] = norm_unit(xlds[u], glds[u - b * upr], pick_uniform(rn, b));
+        }
         __syncthreads();
 #pragma unroll
         for (int b = 0; b < B; ++b)
@@ -265,6 +265,34 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
                 for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = xlds[u0 + u];
             }
+    } else {
+        // one issue ahead of both ways (a copy in each costs the plain
+        // instances code and speed)
+        issue(buf[0], tl[0]);
+        if (!via_lds) {
+            wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+        } else {
+            if (w < kStageThreads / kWave) {
+                if (few_units) {
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) xlds[stage_unit_index(i)] = xr[i];
+                } else if constexpr (kCanStage) {
+#pragma unroll
+                    for (int i = 0; i < kStageUnits; ++i) xlds[stage_unit_index(i)] = xr[i];
+                }
+            }
+            if (shared && int(threadIdx.x) < S) counter[threadIdx.x] = unsigned(G);   // next shared chunk
+            __syncthreads();
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    const int c = min(c_lo + kWave * j + lane, c_hi - 1);
+                    const int u0 = (b * p.k + c * Fmt::kWpc) / 8;
+#pragma unroll
+                    for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = xlds[u0 + u];
+                }
+        }
     }
 #pragma unroll
     for (int d = 1; d < D; ++d) {
@@ -299,7 +327,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // behind the staged activations
     float *part = reinterpret_cast<float *>(smem + p.part_offset);
 
-    auto consume = [&](const Buf &bf, int t) {
+    auto consume = [&](const Buf &bf, int t) __attribute__((always_inline)) {
         const int64_t row0 = b_begin + int64_t(t) * R;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -348,21 +376,22 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 
     // The buffers hold the wave's tiles in order, so the first one past the
     // end ends its work.  After each tile the buffer is refilled at once (an
-    // empty tile past the end costs no memory traffic).  The loop is left by
-    // a jump: every way back to its head then passes all D refills, which is
-    // what lets the compiler's waits before a tile count exactly the loads
-    // of the other buffers.
-    for (;;) {
-#pragma unroll
-        for (int d = 0; d < D; ++d) {
-            if (tl[d] >= T) goto done;
-            const int nt = next_issue();
-            consume(buf[d], tl[d]);
-            tl[d] = nt;
-            issue(buf[d], nt);
-        }
+    // empty tile past the end costs no memory traffic).  One pass of the loop
+    // is the D steps written out (a fold over d); the first step that finds
+    // no tile leaves the loop, so every way back to its head passes all D
+    // refills, which is what lets the compiler's waits before a tile count
+    // exactly the loads of the other buffers.
+    auto step = [&](auto dc) __attribute__((always_inline)) {
+        constexpr int d = decltype(dc)::value;
+        if (tl[d] >= T) return false;
+        const int nt = next_issue();
+        consume(buf[d], tl[d]);
+        tl[d] = nt;
+        issue(buf[d], nt);
+        return true;
+    };
+    while (steps_in_order(step, std::make_integer_sequence<int, D>{})) {
     }
-done:
     wait_vm_loads<0>();
 
     if (S > 1) {
@@ -397,7 +426,7 @@ struct LdsKernel {
     }
 };
 
-template <class Fmt, int R, int B, int D>
+template <class Fmt, int R, int B, int D, bool kNorm>
 __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     using Buf = typename LdsKernel<Fmt, R, B, D>::Buf;
@@ -406,8 +435,8 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     float rn[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) rn[b] = 1.0f;
-    const bool norm = p.norm != 0;                        // uniform
-    if (norm) block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, nullptr, nullptr);
+    constexpr bool norm = kNorm;
+    if constexpr (norm) block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, nullptr, nullptr, [] {});
     int64_t r_begin, r_end;
     wave_rows(p, r_begin, r_end);
     const int tiles = int((r_end - r_begin + R - 1) / R);
@@ -562,7 +591,7 @@ template <int B>
 __global__ void __launch_bounds__(256) qg_rmsnorm_kernel(const Params p, uint16_t *out) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     float rn[B];
-    block_rms<B>(p, reinterpret_cast<float *>(smem), rn, nullptr, nullptr);
+    block_rms<B>(p, reinterpret_cast<float *>(smem), rn, nullptr, nullptr, [] {});
     const int upr = p.k / 8;
     for (int u = threadIdx.x; u < B * upr; u += blockDim.x) {
         const int b = u / upr;

@@ -50,7 +50,10 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version_and_status_strings():
-    assert q.qg_abi_version() == 2
+    header = open(os.path.join(ROOT, "include", "qgemv.h")).read()
+    declared = int(re.search(r"#define\s+QG_ABI_VERSION\s+(\d+)", header).group(1))
+    # the header, the binding's declarations and the loaded library agree
+    assert q.qg_abi_version() == declared == B.ABI_VERSION
     for s in range(12):
         assert isinstance(q.qg_status_string(s), str) and q.qg_status_string(s)
     assert q.qg_status_string(999) == "unknown status"
