@@ -465,15 +465,14 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
     const Norm nm{gamma, eps};
     qg_status st = set_norm(p, &nm);
     if (st != QG_OK) return st;
-    const int64_t lds = int64_t(batch) * ((k / 8 + qg::kWave - 1) / qg::kWave) * 4;
-    if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
-    const dim3 grid(1), block(256);
-    switch (batch) {
-        case 1: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<1>, grid, block, size_t(lds), stream, p, out); break;
-        case 2: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<2>, grid, block, size_t(lds), stream, p, out); break;
-        case 3: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<3>, grid, block, size_t(lds), stream, p, out); break;
-        default: hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<4>, grid, block, size_t(lds), stream, p, out); break;
-    }
+    // one workgroup per batch row; x and gamma stay in LDS when they fit in
+    // 64 KiB with the group sums
+    const int64_t sums = qg::rmsnorm_sums_bytes(k);
+    if (sums > 64 * 1024) return QG_ERR_TOO_LARGE;      // k > 2^23
+    if (sums + 4 * k <= 64 * 1024)
+        hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<true>, dim3(batch), dim3(256), size_t(sums + 4 * k), stream, p, out);
+    else
+        hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<false>, dim3(batch), dim3(256), size_t(sums), stream, p, out);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 

@@ -194,66 +194,6 @@ __device__ __forceinline__ void wave_rows(const Params &p, int64_t &begin, int64
     end = (w + 1) * p.n / p.total_waves;
 }
 
-// RMSNorm factors r[b] = 1 / sqrt(mean_k x[b,k]^2 + eps) for the fused
-// variants, computed by the whole workgroup (every thread must call it).  Row
-// b's 16-byte units are cut into groups of 64 consecutive units; a wave sums a
-// group over its lanes with a fixed butterfly and lane 0 keeps the sum in LDS
-// (gsum); after a barrier every thread adds a row's group sums in group order.
-// So r[b] depends on x[b] and k alone: not on the launch shape, the kernel or
-// the batch size.  Loads go out four groups per wave at a time; `between` is
-// called once by every wave right after its first four loads are issued (the
-// caller can send its own loads behind them and wait for these alone).  With
-// xdst (and gdst) given, the raw units of x (and of gamma, [k/8]) are copied
-// to LDS on the way.
-template <int B, class Between>
-__device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst,
-                                          Between &&between) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int W = blockDim.x >> 6;
-    const int w = wave_in_block();
-    const int upr = p.k / 8;                       // 16-byte units per row
-    const int gpr = (upr + kWave - 1) / kWave;     // groups per row
-    const int ng = B * gpr;
-    uint4 v[4], gv[4];
-    int uu[4], bb[4];
-    auto load_round = [&](int g0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int gi = min(g0 + i * W, ng - 1);
-            bb[i] = gi / gpr;
-            uu[i] = (gi - bb[i] * gpr) * kWave + lane;
-            v[i] = load_x_unit(p.x + (int64_t(bb[i]) * upr + min(uu[i], upr - 1)) * 8);
-            if (gdst) gv[i] = load_x_unit(p.gamma + int64_t(min(uu[i], upr - 1)) * 8);
-        }
-    };
-    auto sum_round = [&](int g0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool real = g0 + i * W < ng && uu[i] < upr;
-            float sq = real ? unit_sumsq(v[i]) : 0.0f;
-#pragma unroll
-            for (int off = kWave / 2; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, kWave);
-            if (lane == 0 && g0 + i * W < ng) gsum[g0 + i * W] = sq;
-            if (xdst && real) xdst[bb[i] * upr + uu[i]] = v[i];
-            if (gdst && real && bb[i] == 0) gdst[uu[i]] = gv[i];
-        }
-    };
-    load_round(w);                 // every wave, even one with no group (clamped loads)
-    between();
-    sum_round(w);
-    for (int g0 = w + 4 * W; g0 < ng; g0 += 4 * W) {
-        load_round(g0);
-        sum_round(g0);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float t = 0.0f;
-        for (int g = 0; g < gpr; ++g) t += gsum[b * gpr + g];
-        r[b] = 1.0f / sqrtf(t / float(p.k) + p.eps);
-    }
-}
-
 // ------------------------------------------------------------------ reduction
 
 __device__ __forceinline__ void swap32(float &a, float &b) {
@@ -336,6 +276,86 @@ struct WaveSum {
         return idx;
     }
 };
+
+// i / per for i < B * per, by comparisons (B <= 4: no integer division)
+template <int B>
+__device__ __forceinline__ int row_of(int i, int per) {
+    int b = 0;
+#pragma unroll
+    for (int r = 1; r < B; ++r) b += i >= r * per ? 1 : 0;
+    return b;
+}
+
+// RMSNorm factors r[b] = 1 / sqrt(mean_k x[b,k]^2 + eps) for the fused
+// variants, computed by the whole workgroup (every thread must call it).  Row
+// b's 16-byte units are cut into groups of 64 consecutive units; a wave sums a
+// group's squares over its lanes (WaveSum, whose tree does not depend on how
+// many groups it carries) and keeps the sum in LDS (gsum); after a barrier
+// every thread adds a row's group sums in group order.  So r[b] depends on
+// x[b] and k alone: not on the launch shape, the kernel or the batch size.
+// Only the workgroup's first four waves load (four groups per wave at a time):
+// the waves dispatched after them would find their loads queued behind the
+// weight stream of the whole chip.  `between` is called once by every wave,
+// by the loading waves right after their first loads are issued (the caller
+// can send its own loads behind them and wait for these alone).  With xdst
+// (and gdst) given, the raw units of x (and of gamma, [k/8]) are copied to LDS
+// on the way.
+template <int B, class Between>
+__device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst,
+                                          Between &&between) {
+    using Red = WaveSum<4>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int W = min(int(blockDim.x >> 6), kStageThreads / kWave);    // loading waves
+    const int w = wave_in_block();
+    const bool loader = w < W;                     // uniform
+    const int upr = p.k / 8;                       // 16-byte units per row
+    const int gpr = (upr + kWave - 1) / kWave;     // groups per row
+    const int ng = B * gpr;
+    uint4 v[4], gv[4];
+    int uu[4], bb[4];
+    auto load_round = [&](int g0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int g = g0 + i * W;
+            const int gi = min(g, ng - 1);
+            bb[i] = row_of<B>(gi, gpr);
+            uu[i] = (gi - bb[i] * gpr) * kWave + lane;
+            v[i] = load_x_unit(p.x + (int64_t(bb[i]) * upr + min(uu[i], upr - 1)) * 8);
+            if (gdst && g < gpr) gv[i] = load_x_unit(p.gamma + int64_t(min(uu[i], upr - 1)) * 8);
+        }
+    };
+    auto sum_round = [&](int g0) {
+        float sq[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool real = g0 + i * W < ng && uu[i] < upr;
+            sq[i] = real ? unit_sumsq(v[i]) : 0.0f;
+            if (xdst && real) xdst[bb[i] * upr + uu[i]] = v[i];
+            if (gdst && real && g0 + i * W < gpr) gdst[uu[i]] = gv[i];
+        }
+        Red::run(sq);
+        if (Red::writer(lane)) {
+            const int g = g0 + Red::value_index(lane, 0) * W;
+            if (g < ng) gsum[g] = sq[0];
+        }
+    };
+    if (loader) load_round(w);
+    between();
+    if (loader) {
+        sum_round(w);
+        for (int g0 = w + 4 * W; g0 < ng; g0 += 4 * W) {
+            load_round(g0);
+            sum_round(g0);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float t = 0.0f;
+        for (int g = 0; g < gpr; ++g) t += gsum[b * gpr + g];
+        r[b] = 1.0f / sqrtf(t / float(p.k) + p.eps);
+    }
+}
 
 // Reduce a tile's R x B accumulators over the wave; the writer lanes get
 // (row i, batch b, total) through emit(i, b, total).  Zeroes acc.

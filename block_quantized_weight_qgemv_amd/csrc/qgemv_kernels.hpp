@@ -30,9 +30,6 @@
 //    in LDS, and each lane loads its own group parameter.
 #pragma once
 
-#include <type_traits>
-#include <utility>
-
 #include "qgemv_common.hpp"
 #include "qgemv_formats.hpp"
 
@@ -63,13 +60,6 @@ __device__ __forceinline__ void run_pipeline(Buf (&buf)[D], int steps, Issue &&i
 }
 
 // ------------------------------------------------------------------ short rows
-
-// step(integral_constant<int, d>) for d = 0, 1, ... in order, stopping at
-// the first that returns false; true when every step ran.
-template <class Step, int... d>
-__device__ __forceinline__ bool steps_in_order(Step &step, std::integer_sequence<int, d...>) {
-    return (step(std::integral_constant<int, d>{}) && ...);
-}
 
 template <class Fmt, int R, int B, int D, int J>
 struct RowKernel {
@@ -135,6 +125,8 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     const int upr = p.k / 8;                              // 16-byte units per row of x
 
     constexpr bool kCanStage = row_can_stage(B, J, Fmt::kPieces);
+    // vector-memory loads one tile issues (codes, parameter pairs, row scales)
+    constexpr int kTileLoads = R * J + R * Fmt::kAuxArrays + (Fmt::kRowScale ? R : 0);
     const bool staged = !norm && kCanStage && p.x_staged != 0;    // uniform
     const bool via_lds = staged || norm;                  // uniform: x reaches the waves through LDS
     const bool shared = via_lds && G > 1;                 // uniform: tiles handed out through LDS
@@ -248,11 +240,18 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         if (shared && int(threadIdx.x) < S) counter[threadIdx.x] = unsigned(G);   // next shared chunk
         block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds, [&] {
             issue(buf[0], tl[0]);
-            wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+            wait_vm_loads<kTileLoads>();
         });
-        // normalize x in LDS in place, the work spread over the workgroup
+        // the rest of the prefetch goes out now (the barrier in block_rms has
+        // made the tile counters visible), so the weight stream runs while x
+        // is normalized in LDS in place, the work spread over the workgroup
+#pragma unroll
+        for (int d = 1; d < D; ++d) {
+            tl[d] = next_issue();
+            issue(buf[d], tl[d]);
+        }
         for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
-            const int b = u / upr;
+            const int b = row_of<B>(u, upr);
             xlds[u] = norm_unit(xlds[u], glds[u - b * upr], pick_uniform(rn, b));
         }
         __syncthreads();
@@ -270,7 +269,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         // instances code and speed)
         issue(buf[0], tl[0]);
         if (!via_lds) {
-            wait_vm_loads<R * J + R * Fmt::kAuxArrays>();
+            wait_vm_loads<kTileLoads>();
         } else {
             if (w < kStageThreads / kWave) {
                 if (few_units) {
@@ -294,10 +293,12 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
                 }
         }
     }
+    if constexpr (!norm) {
 #pragma unroll
-    for (int d = 1; d < D; ++d) {
-        tl[d] = next_issue();
-        issue(buf[d], tl[d]);
+        for (int d = 1; d < D; ++d) {
+            tl[d] = next_issue();
+            issue(buf[d], tl[d]);
+        }
     }
 
     // activation pieces (and chunk sums) in registers
@@ -374,24 +375,29 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         }
     };
 
-    // The buffers hold the wave's tiles in order, so the first one past the
-    // end ends its work.  After each tile the buffer is refilled at once (an
-    // empty tile past the end costs no memory traffic).  One pass of the loop
-    // is the D steps written out (a fold over d); the first step that finds
-    // no tile leaves the loop, so every way back to its head passes all D
-    // refills, which is what lets the compiler's waits before a tile count
-    // exactly the loads of the other buffers.
-    auto step = [&](auto dc) __attribute__((always_inline)) {
-        constexpr int d = decltype(dc)::value;
-        if (tl[d] >= T) return false;
-        const int nt = next_issue();
-        consume(buf[d], tl[d]);
-        tl[d] = nt;
-        issue(buf[d], nt);
-        return true;
-    };
-    while (steps_in_order(step, std::make_integer_sequence<int, D>{})) {
+    // The buffers hold the wave's tiles in increasing order (T, "no tile",
+    // once the wave's work is out), so when the last buffer holds a tile they
+    // all do.  The loop runs while that is so: each step consumes a buffer
+    // and refills it at once (a refill past the end is empty and costs no
+    // memory traffic), and the loop's only exit is its test at the top.
+    // Every way back to the head then passes all D refills, which is what
+    // lets the compiler's wait before each step count exactly the loads of
+    // the other buffers (with exits inside the body, some instances kept an
+    // edge from a middle step to the head and waited for the whole prefetch
+    // at every first step).  What the last refills brought is consumed after
+    // the loop, in order.
+    while (tl[D - 1] < T) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int nt = next_issue();
+            consume(buf[d], tl[d]);
+            tl[d] = nt;
+            issue(buf[d], nt);
+        }
     }
+#pragma unroll
+    for (int d = 0; d < D - 1; ++d)
+        if (tl[d] < T) consume(buf[d], tl[d]);
     wait_vm_loads<0>();
 
     if (S > 1) {
@@ -524,7 +530,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     // the row kernel)
     Buf buf[D];
     issue(buf[0], 0);
-    wait_vm_loads<R + R * Fmt::kAuxArrays>();
+    wait_vm_loads<R + R * Fmt::kAuxArrays + (Fmt::kRowScale ? R : 0)>();
 #pragma unroll
     for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
 
@@ -586,18 +592,25 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
 
 // The fused variants' RMSNorm on its own: out[b, k] = bf16_rne(x * r[b] *
 // gamma), with r[b] summed exactly as the fused matvec sums it (block_rms).
-// One workgroup does the whole [B, k] block.
-template <int B>
-__global__ void __launch_bounds__(256) qg_rmsnorm_kernel(const Params p, uint16_t *out) {
+// Workgroup b does batch row b.  LDS holds the row's group sums and, with
+// kKeep (when they fit), the row's x and gamma as they were first read, so
+// that each is read from memory once.
+inline constexpr int64_t rmsnorm_sums_bytes(int64_t k) { return ((k / 8 + kWave - 1) / kWave * 4 + 15) / 16 * 16; }
+
+template <bool kKeep>
+__global__ void __launch_bounds__(256) qg_rmsnorm_kernel(Params p, uint16_t *out) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    float rn[B];
-    block_rms<B>(p, reinterpret_cast<float *>(smem), rn, nullptr, nullptr, [] {});
     const int upr = p.k / 8;
-    for (int u = threadIdx.x; u < B * upr; u += blockDim.x) {
-        const int b = u / upr;
-        const uint4 xv = load_x_unit(p.x + int64_t(u) * 8);
-        const uint4 gv = load_x_unit(p.gamma + int64_t(u - b * upr) * 8);
-        *reinterpret_cast<uint4 *>(out + int64_t(u) * 8) = norm_unit(xv, gv, pick_uniform(rn, b));
+    p.x += int64_t(blockIdx.x) * p.k;
+    out += int64_t(blockIdx.x) * p.k;
+    uint4 *xs = reinterpret_cast<uint4 *>(smem + rmsnorm_sums_bytes(p.k));
+    uint4 *gs = xs + upr;
+    float rn[1];
+    block_rms<1>(p, reinterpret_cast<float *>(smem), rn, kKeep ? xs : nullptr, kKeep ? gs : nullptr, [] {});
+    for (int u = threadIdx.x; u < upr; u += blockDim.x) {
+        const uint4 xv = kKeep ? xs[u] : load_x_unit(p.x + int64_t(u) * 8);
+        const uint4 gv = kKeep ? gs[u] : load_x_unit(p.gamma + int64_t(u) * 8);
+        *reinterpret_cast<uint4 *>(out + int64_t(u) * 8) = norm_unit(xv, gv, rn[0]);
     }
 }
 

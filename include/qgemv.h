@@ -238,7 +238,10 @@ qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, c
  * consumers that need the normalized activations themselves.
  *   x, out   bf16 [batch, k] (DEVICE), gamma bf16 [k] (DEVICE), all 16-byte
  *            aligned; 8 <= k, k % 8 == 0; 1 <= batch <= 4; eps as above.
- * One workgroup, asynchronous on `stream`. */
+ *   out may be x (normalized in place); otherwise the two must not overlap.
+ *   k above 2^23 returns QG_ERR_TOO_LARGE (the group sums of a row must fit
+ *   in 64 KiB of LDS).
+ * One workgroup per batch row, asynchronous on `stream`. */
 qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *out, int64_t k,
                           int32_t batch, hipStream_t stream);
 

@@ -145,3 +145,12 @@ def test_one_hip_runtime_in_the_process():
     with open("/proc/self/maps") as f:
         paths = {line.split()[-1] for line in f if "libamdhip64" in line}
     assert len(paths) == 1, paths
+
+def test_standalone_norm_limits():
+    fn = LIB.qg_rmsnorm_bf16
+    assert fn(A, A2, 1e-5, A3, (1 << 23) + 8, 1, None) == LARGE     # the row's group sums exceed 64 KiB
+    assert fn(A, A2, 1e-5, A3, 12, 1, None) == SHAPE                # k % 8
+    assert fn(A, A2, 1e-5, A3, 64, 5, None) == BATCH
+    assert fn(A, ODD, 1e-5, A3, 64, 1, None) == MIS
+    assert fn(A, A2, -1.0, A3, 64, 1, None) == VALUE
+    assert fn(None, A2, 1e-5, A3, 64, 1, None) == NULL

@@ -153,6 +153,41 @@ def test_fused_norm_parity(fmt, n, k, gs, batch):
         parity.assert_parity(y, y_ref, a_ref, "%s fused norm n=%d k=%d" % (fmt, n, k))
 
 
+@pytest.mark.parametrize("k", [8, 3840, 8200, 16384, 20480])
+def test_standalone_norm_kept_and_reread_rows(k):
+    """Rows whose x and gamma fit in LDS beside the sums (k up to 16352) are
+    read once; longer rows are read again to normalize.  Both: the oracle's
+    bits except at ambiguous elements, each batch row as it is alone, and the
+    same in place (out = x).  k = 8 is one unit; 8200 ends in a ragged group."""
+    log("standalone norm k=%d" % k)
+    x = synth.activations(400 + k % 89, 3, k)
+    gamma = _gamma(k, k)
+    eps = 1e-6
+    xg = host_bits(q.qg_rmsnorm_bf16(dev(x), dev(gamma), eps))
+    xn = N.rmsnorm_bf16(x, gamma, eps)
+    amb, other = _ambiguous(x, gamma, eps)
+    diff = xg != xn
+    assert np.all(amb[diff]) and np.array_equal(xg[diff], other[diff]), \
+        "%d non-ambiguous mismatches" % int(np.sum(diff & ~amb))
+    for b in range(3):
+        assert np.array_equal(host_bits(q.qg_rmsnorm_bf16(dev(x[b:b + 1]), dev(gamma), eps))[0], xg[b]), b
+    xd = dev(x)
+    q.qg_rmsnorm_bf16(xd, dev(gamma), eps, xd)
+    assert np.array_equal(host_bits(xd), xg)
+
+
+def test_fused_norm_equals_plain_on_a_reread_row():
+    """k = 20480: the standalone norm reads x twice, the fused one keeps it in
+    LDS; the two still agree bit for bit."""
+    n, k, gs = 700, 20480, 32
+    arrays = _quantize("fp4", synth.weights(36, n, k), gs)
+    x = synth.activations(36, 1, k)
+    gamma = _gamma(k, 9)
+    y = run_norm("fp4", arrays, x, gamma, 1e-6, n, gs)
+    xg = host_bits(q.qg_rmsnorm_bf16(dev(x), dev(gamma), 1e-6))
+    assert np.array_equal(y, run("fp4", arrays, xg, n, gs=gs))
+
+
 PLANS = [None, {"rows_per_tile": 1}, {"rows_per_tile": 4, "waves_per_block": 1, "blocks": 3},
          {"rows_per_tile": 2, "waves_per_block": 5, "blocks": 7}, {"waves_per_block": 2, "blocks": 1000}]
 
