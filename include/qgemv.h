@@ -191,7 +191,7 @@ const char *qg_status_string(qg_status status);
  * Fused RMSNorm variants: y = W . RMSNorm(x), in one launch.
  *
  * "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus (Part 2)",
- * section "What's next", ranks RMSNorm fusion into the decode step's matvecs
+ * section "Where it landed", ranks RMSNorm fusion into the decode step's matvecs
  * among the next levers (the norm takes hundreds of launches per token).  The
  * page does not print the norm; these calls take the standard one, row by row:
  *

@@ -27,7 +27,7 @@ Modules
   gemv      dequantize-then-FP64-dot for each format, plus the conditioning
             mass A = sum |w x| used by the parity criterion.
   norm      RMSNorm of the activations rounded to bf16, the input of the
-            fused norm-then-matvec variants (Part 2 post, "What's next").
+            fused norm-then-matvec variants (Part 2 post, "Where it landed").
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*``
 against closed forms, library decoders, exact rational brute force or the

@@ -1,7 +1,7 @@
 """RMSNorm of the activations, as the fused matvec variants consume it.  Test
 infrastructure.
 
-The Part 2 post ("What's next") ranks RMSNorm fusion into the decode step's
+The Part 2 post ("Where it landed") ranks RMSNorm fusion into the decode step's
 matvecs among the next levers; it does not print the norm itself.  This module
 takes the standard RMSNorm, row by row, and hands the matvec what a separate
 norm kernel would: the normalized activation rounded to bf16,

@@ -6,7 +6,7 @@ scaled down) over three distinct layers, each matvec writing its own output.
 The graph is replayed three times; between replays the outputs are cleared by
 a fill kernel outside the graph and the program does eager work of its own,
 so each replay has to write every output again.  The library records no
-memset or allocation into the graph (Part 2 post, "What's next": a graph
+memset or allocation into the graph (Part 2 post, "Where it landed": a graph
 decode step is one of the two ranked levers; the pages verify graph replay
 bit-identical to direct launch).
 """
@@ -72,3 +72,66 @@ def test_graph_replay_matches_eager_bitwise():
         torch.cuda.synchronize()
         for (name, *_, y), e in zip(mats, eager):
             assert np.array_equal(y.cpu().numpy(), e), (rep, name)
+
+
+def test_graph_replay_with_norms_matches_eager_bitwise():
+    """The pre-norm decode step (an RMSNorm before qkv and before gate_up) in
+    one graph, twice: with the norm fused into those matvecs, and with
+    separate norm launches writing the normalized x that plain matvecs read.
+    Every replay equals the eager launches bitwise, and the fused outputs
+    equal the separate ones."""
+    rng = np.random.default_rng(11)
+    normed = {"qkv", "gate_up"}
+    mats = []
+    for li in range(LAYERS):
+        for si, (name, n, k) in enumerate(SHAPES):
+            w = synth.weights(210 + si, n, k, layer=li)
+            codes, scales = q.qg_quantize_fp4_e2m1(w, 32)
+            x = dev(synth.activations(210 + si + 7 * li, 1, k))
+            g16 = torch.from_numpy(rng.uniform(0.5, 1.5, k).astype(np.float32)).to("cuda:0").to(torch.bfloat16)
+            y_f = torch.empty((1, n), dtype=torch.float32, device="cuda:0")
+            y_s = torch.empty((1, n), dtype=torch.float32, device="cuda:0")
+            mats.append((name, dev(codes), dev(scales), x, g16, torch.empty_like(x), y_f, y_s))
+
+    def step():
+        for name, c, s, x, g, xn, y_f, y_s in mats:
+            if name in normed:
+                q.qgemv_fp4_e2m1_rmsnorm(c, s, x, g, 1e-6, y_f, 32)
+                q.qg_rmsnorm_bf16(x, g, 1e-6, xn)
+                q.qgemv_fp4_e2m1(c, s, xn, y_s, 32)
+            else:
+                q.qgemv_fp4_e2m1(c, s, x, y_f, 32)
+                q.qgemv_fp4_e2m1(c, s, x, y_s, 32)
+
+    log("graph+norm: eager step")
+    step()
+    torch.cuda.synchronize()
+    eager = [(m[6].cpu().numpy().copy(), m[7].cpu().numpy().copy()) for m in mats]
+    for (name, *_), (f, s) in zip(mats, eager):
+        assert np.isfinite(f).all() and np.array_equal(f, s), name
+
+    log("graph+norm: capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    scratch = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(3):
+        for m in mats:
+            m[5].zero_()
+            m[6].zero_()
+            m[7].zero_()
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        log("graph+norm: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for (name, *_, y_f, y_s), (f, s) in zip(mats, eager):
+            assert np.array_equal(y_f.cpu().numpy(), f), (rep, name, "fused")
+            assert np.array_equal(y_s.cpu().numpy(), s), (rep, name, "separate")
