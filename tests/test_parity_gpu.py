@@ -101,6 +101,36 @@ def test_affine_shapes(bits, n, k, gs, batch):
     _case(fmt, n, k, gs, batch, seed=bits * 1000 + n + k)
 
 
+FMT_IDS = {"fp4": q.QG_FMT_FP4_E2M1, "u4": q.QG_FMT_AFFINE_U4, "u8": q.QG_FMT_AFFINE_U8, "fp8": q.QG_FMT_FP8_E4M3}
+WPC = {"fp4": 32, "u4": 32, "u8": 16, "fp8": 16}      # weights per 16-byte chunk
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("fmt,gs", [("fp4", 32), ("u4", 64), ("u8", 64), ("fp8", None)])
+def test_largest_k_each_format(fmt, gs, batch):
+    """The largest k the library takes for the format and batch (qg_max_k,
+    rounded down to whole groups) meets the parity bar on a ragged row count;
+    the next admissible k is refused with QG_ERR_TOO_LARGE."""
+    step = max(gs or 1, WPC[fmt])
+    k = q.qg_max_k(FMT_IDS[fmt], batch)
+    k -= k % step
+    _case(fmt, 70, k, gs, batch, seed=7 * batch + k % 97)
+    k2 = k + step
+    n = 3
+    if fmt == "fp4":
+        arrays = (np.zeros((n, k2 // 2), np.uint8), np.zeros((n, k2 // gs), np.uint16))
+    elif fmt == "fp8":
+        arrays = (np.zeros((n, k2), np.uint8), np.ones(n, np.float32))
+    else:
+        per = 8 if fmt == "u4" else 4
+        arrays = (np.zeros((n, k2 // per), np.uint32), np.zeros((n, k2 // gs), np.uint16),
+                  np.zeros((n, k2 // gs), np.uint16))
+    log("%s k=%d batch=%d refused" % (fmt, k2, batch))
+    with pytest.raises(q.QgError) as e:
+        run(fmt, arrays, np.zeros((batch, k2), np.uint16), n, gs=gs)
+    assert e.value.name == "QG_ERR_TOO_LARGE"
+
+
 def test_staging_limit_is_enforced():
     k = q.qg_max_k(q.QG_FMT_AFFINE_U8, 4) + 32
     k -= k % 32
