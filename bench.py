@@ -312,6 +312,8 @@ def run_sweep(args):
         log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%" % (wl.label(), us, gbs, 100 * gbs / HBM_PEAK_GBS))
         del wl
         torch.cuda.empty_cache()
+    if not only or "qgemm" in only:
+        rows.extend(run_qgemm_sweep(args))
     if not only or "step48" in only:
         step = run_decode_step(args)
         per_shape = {r["shape"]: r["us"] for r in rows if r["fmt"] == "fp4" and r["batch"] == 1}
@@ -324,6 +326,53 @@ def run_sweep(args):
     if args.out:
         with open(args.out, "w") as f:
             json.dump(rows, f, indent=1)
+
+
+def run_qgemm_sweep(args):
+    """The small-batch GEMM (qgemm_fp4_e2m1) on the Gemma-4-12B FP4 shapes at
+    m = 8 .. 128 activation rows: algorithmic bytes (weights + scales once,
+    x, y) per launch and MFMA rate, beside the same work done by ceil(m/4)
+    launches of the batch-4 matvec (which re-reads the weights each time)."""
+    import torch
+    import block_quantized_weight_qgemv_amd as q
+    import synth
+    rows = []
+    for name in ("gate_up", "qkv", "fc_down"):
+        wl = Workload("fp4", name, batch=4, gs=32)
+        wbytes = q.qg_bytes_fp4(wl.n, wl.k, 32)
+        sid = synth.shape(name)[0]
+        for m in (8, 16, 32, 64, 128):
+            x = to_dev(synth.activations(sid, m, wl.k))
+            y = torch.empty((m, wl.n), dtype=torch.float32, device="cuda:0")
+
+            def gemm(i):
+                d = wl.dev[i % wl.copies]
+                q.qgemm_fp4_e2m1(d[0], d[1], x, y, 32)
+
+            steps = timed_steps(gemm, args.mode)
+            us = time_steps(gemm, steps, max(1, steps // 10), args.mode) / steps * 1e3
+            nbytes = wbytes + m * wl.k * 2 + m * wl.n * 4
+            gbs = nbytes / (us * 1e-6) / 1e9
+            tflops = 2.0 * m * wl.n * wl.k / (us * 1e-6) / 1e12
+            calls = (m + 3) // 4
+
+            def matvecs(i):
+                for j in range(calls):
+                    wl.launch(i * calls + j)
+
+            msteps = max(10, timed_steps(matvecs, args.mode) // 2)
+            us_mv = time_steps(matvecs, msteps, max(1, msteps // 10), args.mode) / msteps * 1e3
+            rows.append({"fmt": "fp4", "shape": name, "kernel": "qgemm", "n": wl.n, "k": wl.k, "m": m,
+                         "bytes": nbytes, "us": round(us, 3), "GBps": round(gbs, 1),
+                         "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4), "mfma_TFLOPs": round(tflops, 1),
+                         "matvec_b4_x%d_us" % calls: round(us_mv, 3)})
+            log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  %6.1f TFLOP/s  (%d batch-4 matvecs: %.2f us)"
+                % ("qgemm fp4 %s [%dx%d] m=%d" % (name, wl.n, wl.k, m), us, gbs, 100 * gbs / HBM_PEAK_GBS,
+                   tflops, calls, us_mv))
+            del x, y
+        del wl
+        torch.cuda.empty_cache()
+    return rows
 
 
 def run_decode_step(args, layers=48):

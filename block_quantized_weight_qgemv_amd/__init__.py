@@ -25,7 +25,7 @@ QG_FMT_FP8_E4M3 = _b.QG_FMT_FP8_E4M3
 qg_plan = _b.qg_plan
 
 __all__ = [
-    "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3",
+    "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
     "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
@@ -146,6 +146,26 @@ def qgemv_fp4_e2m1(codes, scales, x, y, group_size, plan=None, stream=None):
     st = _lib.qgemv_fp4_e2m1_plan(cp, sp, xp, yp, n, k, int(group_size), batch, out,
                                   _plan_ptr(plan), _stream(stream, y.device))
     _check(st, "qgemv_fp4_e2m1")
+    return y
+
+
+def qgemm_fp4_e2m1(codes, scales, x, y, group_size, stream=None):
+    """Y[m, n] = X[m, k] . W[n, k]^T for m activation rows (any m >= 1; the
+    matvec entry points are faster for m <= 4), W as in qgemv_fp4_e2m1.
+
+    codes uint8 [n, k/2], scales bf16 [n, k/gs], x bf16 [m, k], y float32 or bf16 [m, n].
+    """
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.uint8,), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, m, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 2 != k or tuple(scales.shape) != (n, k // group_size):
+        raise ValueError("shapes: codes %s, scales %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), k, group_size))
+    _same_device(codes, scales, x, y)
+    st = _lib.qgemm_fp4_e2m1(cp, sp, xp, yp, n, k, int(group_size), m, out, _stream(stream, y.device))
+    _check(st, "qgemm_fp4_e2m1")
     return y
 
 

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 # QG_ABI_VERSION of include/qgemv.h that these declarations follow; a
 # library that reports another version is refused at load.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 QG_OK = 0
 QG_OUT_F32 = 0
@@ -56,6 +56,7 @@ SIGNATURES = {
                                       _p, _p]),
     "qgemv_fp8_e4m3_rmsnorm": (_st, [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _p, _p]),
     "qg_rmsnorm_bf16": (_st, [_p, _p, ctypes.c_float, _p, _i64, _i32, _p]),
+    "qgemm_fp4_e2m1": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qg_plan_query": (_st, [_i32, _i64, _i64, _i32, _p]),
     "qg_stream_probe": (_st, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "qg_status_string": (ctypes.c_char_p, [_st]),

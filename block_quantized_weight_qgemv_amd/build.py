@@ -41,7 +41,8 @@ def _run(cmd):
     return out
 
 
-HIP_SOURCES = ["qgemv_api.hip", "qgemv_fp4.hip", "qgemv_affine_u4.hip", "qgemv_affine_u8.hip", "qgemv_fp8.hip"]
+HIP_SOURCES = ["qgemv_api.hip", "qgemv_fp4.hip", "qgemv_affine_u4.hip", "qgemv_affine_u8.hip", "qgemv_fp8.hip",
+               "qgemm.hip"]
 
 
 def build(verbose=False):

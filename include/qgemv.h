@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 2
+#define QG_ABI_VERSION 3
 
 typedef enum qg_status {
     QG_OK = 0,
@@ -244,6 +244,34 @@ qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, c
  * One workgroup per batch row, asynchronous on `stream`. */
 qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *out, int64_t k,
                           int32_t batch, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Small-batch GEMM: more than four activation rows.
+ *
+ * Y[m, n] = X[m, k] . W[n, k]^T for a short prefill or a speculative-decoding
+ * batch, W in the FP4-E2M1 layout of qgemv_fp4_e2m1 (codes [n, k/2], bf16
+ * group scales [n, k/group_size]), read from HBM once per 64 activation rows.
+ * The SharpInference issue ("generalize Gemma 4 batched prefill ..."), items
+ * C1 and C2, weighs a dequantized fp16 weight copy fed to a GEMM against a
+ * kernel that reads the 4-bit weights once; this is the second kind: the
+ * codes are decoded in registers and meet the activations in bf16 MFMA, and
+ * each group's sum is scaled once, y += s * sum_{k in group} e2m1 * x, in
+ * fp32.  The summation order depends on k and the group size only, so the
+ * results are bitwise the same from run to run and for every m (row i of Y
+ * does not depend on the other rows of X); they are not bitwise those of the
+ * matvec (another order), and meet the same 1e-3 bar against the exact sum.
+ *   codes     uint8 [n, k/2] (DEVICE), 16-byte aligned
+ *   scales    bf16 [n, k/group_size] (DEVICE), 2-byte aligned
+ *   x         bf16 [m, k] (DEVICE), 16-byte aligned
+ *   y         [m, n] f32 or bf16 (DEVICE), 4- or 2-byte aligned
+ *   n >= 1, 32 <= k <= 2^30, k % 32 == 0          QG_ERR_BAD_SHAPE
+ *   group_size in {32, 64, 128}, k % group_size == 0   QG_ERR_BAD_GROUP_SIZE
+ *   1 <= m <= QG_GEMM_MAX_M                       QG_ERR_BAD_BATCH
+ * No device memory is allocated; asynchronous on `stream`.  For m <= 4 the
+ * matvec entry points are the faster path. */
+#define QG_GEMM_MAX_M 65536
+qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y, int64_t n,
+                         int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype, hipStream_t stream);
 
 /* QG_ABI_VERSION of the loaded library. */
 int qg_abi_version(void);

@@ -154,3 +154,19 @@ def test_standalone_norm_limits():
     assert fn(A, ODD, 1e-5, A3, 64, 1, None) == MIS
     assert fn(A, A2, -1.0, A3, 64, 1, None) == VALUE
     assert fn(None, A2, 1e-5, A3, 64, 1, None) == NULL
+
+
+def test_qgemm_argument_errors():
+    fn = LIB.qgemm_fp4_e2m1
+    assert fn(None, A2, A3, A4, 64, 256, 32, 8, 0, None) == NULL
+    assert fn(A, A2, A3, A4, 0, 256, 32, 8, 0, None) == SHAPE               # n < 1
+    assert fn(A, A2, A3, A4, 64, 16, 32, 8, 0, None) == SHAPE               # k < 32
+    assert fn(A, A2, A3, A4, 64, 272, 32, 8, 0, None) == SHAPE              # k % 32
+    assert fn(A, A2, A3, A4, 64, 256, 48, 8, 0, None) == GROUP
+    assert fn(A, A2, A3, A4, 64, 320, 128, 8, 0, None) == GROUP             # k % group_size
+    assert fn(A, A2, A3, A4, 64, 256, 32, 0, 0, None) == BATCH
+    assert fn(A, A2, A3, A4, 64, 256, 32, 65537, 0, None) == BATCH          # above QG_GEMM_MAX_M
+    assert fn(A, A2, A3, A4, 64, 256, 32, 8, 2, None) == DTYPE
+    assert fn(ODD, A2, A3, A4, 64, 256, 32, 8, 0, None) == MIS              # codes 8-byte aligned only
+    assert fn(A, A2, ODD, A4, 64, 256, 32, 8, 0, None) == MIS               # x
+    assert fn(A, A2, A3, ctypes.c_void_p(0x400002), 64, 256, 32, 8, 0, None) == MIS   # f32 y 2-byte aligned
