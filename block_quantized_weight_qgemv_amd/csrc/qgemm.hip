@@ -36,14 +36,34 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
     p.m = m;
     p.groups = int32_t(k / group_size);
     p.out_bf16 = out_dtype == QG_OUT_BF16 ? 1 : 0;
-    const dim3 grid(unsigned((n + qg::kGemmRows - 1) / qg::kGemmRows),
-                    unsigned((m + qg::kGemmTokens - 1) / qg::kGemmTokens));
-    switch (group_size) {
-        case 32: hipLaunchKernelGGL(qg::qgemm_fp4_kernel<1>, grid, dim3(256), 0, stream, p); break;
-        case 64: hipLaunchKernelGGL(qg::qgemm_fp4_kernel<2>, grid, dim3(256), 0, stream, p); break;
-        default: hipLaunchKernelGGL(qg::qgemm_fp4_kernel<4>, grid, dim3(256), 0, stream, p); break;
+    // K slices per workgroup, from n and k only (a row's bits must not depend
+    // on m): more slices when there are few 64-row tiles to spread over the
+    // chip, never more than there are 256-wide chunks
+    const int64_t tiles = (n + qg::kGemmRows - 1) / qg::kGemmRows;
+    const int64_t chunks = (k + qg::kGemmKC - 1) / qg::kGemmKC;
+    int ks = tiles <= 64 ? 4 : (tiles <= 160 ? 2 : 1);
+    while (ks > 1 && ks > chunks) ks /= 2;
+    // blocks of 16 activation rows per workgroup: as many as m needs, up to
+    // 4 / ks (LDS holds ks chunks of them)
+    const int tb_max = 4 / ks;
+    const int tb = m <= 16 ? 1 : (m <= 32 || tb_max == 2 ? 2 : 4);
+    const int tbu = tb > tb_max ? tb_max : tb;
+    const dim3 grid(unsigned(tiles), unsigned((m + 16 * tbu - 1) / (16 * tbu)));
+    const dim3 block(unsigned(256 * ks));
+    const int spg = group_size / 32;
+#define QG_GEMM_CASE(S, T, K)                                                                   \
+    if (spg == S && tbu == T && ks == K) {                                                      \
+        hipLaunchKernelGGL((qg::qgemm_fp4_kernel<S, T, K>), grid, block, 0, stream, p);        \
+        return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                         \
     }
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+#define QG_GEMM_SPG(S) QG_GEMM_CASE(S, 1, 1) QG_GEMM_CASE(S, 2, 1) QG_GEMM_CASE(S, 4, 1) \
+    QG_GEMM_CASE(S, 1, 2) QG_GEMM_CASE(S, 2, 2) QG_GEMM_CASE(S, 1, 4)
+    QG_GEMM_SPG(1)
+    QG_GEMM_SPG(2)
+    QG_GEMM_SPG(4)
+#undef QG_GEMM_SPG
+#undef QG_GEMM_CASE
+    return QG_ERR_LAUNCH;     // not reached: every (group size, tb, ks) above has an instance
 }
 
 }  // extern "C"

@@ -10,10 +10,11 @@
 // MMA kernel that reads the 4-bit weights once, and the second winning at
 // short prompts.)
 //
-// A workgroup of four waves owns 64 weight rows (16 per wave) and up to 64
-// activation rows (four blocks of 16).  K is walked in chunks of 256: the
-// workgroup stages the chunk's activations and group scales in LDS while
-// each wave's lanes load their own weight dwords, one chunk ahead.  One MFMA
+// A workgroup of four waves owns 64 weight rows (16 per wave) and 16, 32 or
+// 64 activation rows (TB blocks of 16).  K is walked in chunks of 256: the
+// workgroup stages each chunk's activations and group scales in LDS, and each
+// wave's lanes load their own weight dwords, several chunks ahead through a
+// ring of registers.  One MFMA
 // step (v_mfma_f32_16x16x32_bf16) covers 32 k, which lies inside one scale
 // group (group sizes 32, 64, 128), so the group's raw sums come out of the
 // MFMA accumulator and are scaled once: y += s . sum_{k in group} e2m1 . x.
@@ -42,128 +43,204 @@ struct GemmParams {
 };
 
 constexpr int kGemmRows = 64;      // weight rows per workgroup, 16 per wave
-constexpr int kGemmTokens = 64;    // activation rows per workgroup, 4 blocks of 16
 constexpr int kGemmKC = 256;       // k per chunk: 8 MFMA steps of 32
 constexpr int kGemmXPad = 8;       // LDS row padding (bf16) against bank conflicts
 
+// chunks in flight per lane: the register ring holds PD chunks' loads (two
+// with four K slices: 16 waves per workgroup hide the latency, and a deeper
+// ring would not fit the 128 registers a 1024-thread workgroup leaves)
+constexpr int gemm_depth(int tb, int ks) { return ks == 4 ? 2 : (tb == 1 ? 4 : (tb == 2 ? 3 : 2)); }
+
 // SPG = MFMA steps per scale group (group size / 32): each group's steps form
 // one straight-line chain of MFMAs from a zero accumulator, read once.
-template <int SPG>
-__global__ void __launch_bounds__(256) qgemm_fp4_kernel(const GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[kGemmTokens][kGemmKC + kGemmXPad];
-    __shared__ __attribute__((aligned(16))) uint16_t ss[kGemmKC / 32][kGemmRows];
+// TB = blocks of 16 activation rows per workgroup.
+// KS = K slices: the workgroup has 4 KS waves, slice s (waves 4s..4s+3) takes
+// chunks s, s + KS, s + 2 KS, ... of the same 64 rows, and the slices' sums
+// are added in slice order at the end.  KS depends on n and k only, so a
+// row's bits do not depend on the other activation rows.
+template <int SPG, int TB, int KS>
+__global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p) {
+    static_assert(KS * TB <= 4, "LDS holds KS chunks of 16 TB activation rows");
+    constexpr int kTokens = 16 * TB;
+    constexpr int kXUnits = 2 * TB;                // 16-byte activation units per thread per chunk
+    constexpr int PD = gemm_depth(TB, KS);
+    constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
+    constexpr int BS = 8 / TB > SPG ? 8 / TB : SPG;   // MFMA steps per batch of independent chains
+    constexpr int GB = BS / SPG;                   // scale groups per batch
+    __shared__ __attribute__((aligned(16))) uint16_t xsa[KS][kTokens][kGemmKC + kGemmXPad];
+    __shared__ __attribute__((aligned(16))) uint16_t ssa[KS][kGemmKC / 32][kGemmRows];
 
-    const int tid = threadIdx.x;
+    const int ks = threadIdx.x >> 8;               // K slice
+    const int tid = threadIdx.x & 255;             // thread in the slice
     const int lane = tid & (kWave - 1);
-    const int w = tid >> 6;
+    const int w = tid >> 6;                        // wave in the slice: rows 16w..16w+15
+    auto &xs = xsa[ks];
+    auto &ss = ssa[ks];
     const int g = lane >> 4;                       // k quarter of an MFMA step / D row quarter
     const int li = lane & 15;                      // A row / B column inside a block
     const int64_t rbase = int64_t(blockIdx.x) * kGemmRows;
-    const int t0 = blockIdx.y * kGemmTokens;
-    const int mt = min(kGemmTokens, p.m - t0);     // activation rows of this workgroup
+    const int t0 = blockIdx.y * kTokens;
+    const int mt = min(kTokens, p.m - t0);         // activation rows of this workgroup
     const int nblk = (mt + 15) >> 4;               // blocks of 16 in use (uniform)
     const int64_t row_bytes = p.k / 2;
     const int nch = (p.k + kGemmKC - 1) / kGemmKC;
-    constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
+    const int nit = (nch + KS - 1) / KS;           // chunks per slice (the last may be short)
 
     // this lane's weight row (rows past n read row n-1; their results are dropped)
     const int64_t arow = min(rbase + 16 * w + li, p.n - 1);
     const unsigned char *wrow = p.codes + arow * row_bytes;
 
-    uint32_t wn[8];            // next chunk's weight dwords (one per MFMA step)
-    uint4 xr[8];               // next chunk's activations, staged through registers
-    uint16_t sr[2];            // next chunk's scales
-    auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    // The ring: set d holds one chunk's weight dwords (one per MFMA step), the
+    // thread's activation units and scales.  Every refill issues the same loads
+    // (a chunk past the end reloads the last one, never used), so the
+    // compiler's wait before a set is stored counts exactly the later sets.
+    uint32_t wn[PD][8];
+    uint4 xr[PD][kXUnits];
+    uint16_t sr[PD][2];
+    auto load_chunk = [&](int d, int c_in) __attribute__((always_inline)) {
+        const int c = min(c_in, nch - 1);
         const int64_t kb = int64_t(c) * (kGemmKC / 2);        // byte offset of the chunk in a row
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             // a step past k reads the row's last 16 bytes instead (never used)
             const int64_t off = min(kb + 16 * s, row_bytes - 16) + 4 * g;
-            wn[s] = *reinterpret_cast<const uint32_t *>(wrow + off);
+            wn[d][s] = *reinterpret_cast<const uint32_t *>(wrow + off);
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kXUnits; ++j) {
             const int u = tid + 256 * j;                      // unit of 8 activations
             const int tt = u >> 5, ku = u & 31;
-            const int kk = c * kGemmKC + ku * 8;
+            const int kk = min(c * kGemmKC + ku * 8, p.k - 8);   // past k: a unit never used
             const int tok = t0 + min(tt, mt - 1);
-            xr[j] = kk < p.k ? load_x_unit(p.x + int64_t(tok) * p.k + kk) : make_uint4(0, 0, 0, 0);
+            xr[d][j] = load_x_unit(p.x + int64_t(tok) * p.k + kk);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int e = tid + 256 * j;
             const int grp = e >> 6, r = e & 63;
-            const int gg = c * gpc + grp;
+            const int gg = min(c * gpc + min(grp, gpc - 1), p.groups - 1);
             const int64_t row = min(rbase + r, p.n - 1);
-            sr[j] = (grp < gpc && gg < p.groups) ? p.scales[row * p.groups + gg] : uint16_t(0);
+            sr[d][j] = p.scales[row * p.groups + gg];
         }
     };
 
-    f32x4_t acc[4];
+    f32x4_t acc[TB];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < TB; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[b][v] = 0.0f;
 
-    load_chunk(0);
-    for (int c = 0; c < nch; ++c) {
+    // the ring is filled chunk by chunk: the scheduler may not interleave the
+    // chunks' loads, or the first set's loads would no longer be the oldest
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int u = tid + 256 * j;
-            *reinterpret_cast<uint4 *>(&xs[u >> 5][(u & 31) * 8]) = xr[j];
-        }
+    for (int d = 0; d < PD; ++d) {
+        load_chunk(d, d * KS + ks);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int c0 = 0; c0 < nit; c0 += PD) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int e = tid + 256 * j;
-            ss[e >> 6][e & 63] = sr[j];
-        }
-        __syncthreads();
-        uint32_t wc[8];
+        for (int d = 0; d < PD; ++d) {
+            const int c = (c0 + d) * KS + ks;                 // this slice's chunk
+            const bool active = c < nch;                       // uniform in the wave
+            // stored whether active or not: a branch here would cost the
+            // compiler its count of the loads in flight (it would drain them)
 #pragma unroll
-        for (int s = 0; s < 8; ++s) wc[s] = wn[s];
-        if (c + 1 < nch) load_chunk(c + 1);
-
-        // whole groups in this chunk (k is a multiple of the group size)
-        const int ngr = min(8, (p.k - c * kGemmKC) / 32) / SPG;
+            for (int j = 0; j < kXUnits; ++j) {
+                const int u = tid + 256 * j;
+                const int kk = c * kGemmKC + (u & 31) * 8;
+                // units past k are stored as zeros (the MFMA of a partial last
+                // chunk stops at a whole group, but LDS stays defined)
+                *reinterpret_cast<uint4 *>(&xs[u >> 5][(u & 31) * 8]) = kk < p.k ? xr[d][j] : make_uint4(0, 0, 0, 0);
+            }
 #pragma unroll
-        for (int gi = 0; gi < gpc; ++gi) {
-            if (gi < ngr) {
-                // 8 weights of row li per step, k = 32s + 8g + i: one dword, four pair conversions
-                bf16x8_t a[SPG];
+            for (int j = 0; j < 2; ++j) {
+                const int e = tid + 256 * j;
+                ss[e >> 6][e & 63] = sr[d][j];
+            }
+            __syncthreads();
+            uint32_t wc[8];
 #pragma unroll
-                for (int j = 0; j < SPG; ++j) {
-                    const uint32_t q = wc[gi * SPG + j];
-                    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
-                    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
-                    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
-                    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
-                    a[j] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                                   __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-                }
-                const uint2 sp = *reinterpret_cast<const uint2 *>(&ss[gi][16 * w + 4 * g]);
-                const float sc[4] = {bf16_to_f32(sp.x & 0xFFFFu), bf16_to_f32(sp.x >> 16), bf16_to_f32(sp.y & 0xFFFFu),
-                                     bf16_to_f32(sp.y >> 16)};
+            for (int s = 0; s < 8; ++s) wc[s] = wn[d][s];
+            load_chunk(d, c + PD * KS);
+            if (active) {
+                // The chunk's MFMA chains (one per scale group and block of 16
+                // activation rows) go out back to back, BS steps at a time,
+                // and their sums are read and scaled afterwards: a result read
+                // right behind its MFMA would stall each step for the MFMA's
+                // whole latency.  The code has no branch: in a partial last
+                // chunk the groups past k multiply the zeros staged for them
+                // (the weights there are finite E2M1 codes read in bounds),
+                // and blocks past m are computed but never stored.
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    if (b < nblk) {
-                        f32x4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+                for (int s0 = 0; s0 < 8; s0 += BS) {
+                    f32x4_t dd[GB][TB];
+#pragma unroll
+                    for (int gb = 0; gb < GB; ++gb) {
+                        // 8 weights of row li per step, k = 32s + 8g + i: one dword, four pair conversions
+                        bf16x8_t a[SPG];
 #pragma unroll
                         for (int j = 0; j < SPG; ++j) {
-                            const int s = gi * SPG + j;
-                            const bf16x8_t xv = *reinterpret_cast<const bf16x8_t *>(&xs[16 * b + li][32 * s + 8 * g]);
-                            d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], xv, d, 0, 0, 0);
+                            const uint32_t q = wc[s0 + gb * SPG + j];
+                            const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
+                            const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
+                            const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
+                            const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                            a[j] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                                           __builtin_shufflevector(p2, p3, 0, 1, 2, 3),
+                                                           0, 1, 2, 3, 4, 5, 6, 7);
                         }
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[v], d[v], acc[b][v]);
+                        for (int b = 0; b < TB; ++b) {
+                            f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                            for (int j = 0; j < SPG; ++j) {
+                                const int s = s0 + gb * SPG + j;
+                                const bf16x8_t xv =
+                                    *reinterpret_cast<const bf16x8_t *>(&xs[16 * b + li][32 * s + 8 * g]);
+                                d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], xv, d0, 0, 0, 0);
+                            }
+                            dd[gb][b] = d0;
+                        }
+                    }
+#pragma unroll
+                    for (int gb = 0; gb < GB; ++gb) {
+                        const int gi = s0 / SPG + gb;
+                        const uint2 sp = *reinterpret_cast<const uint2 *>(&ss[gi][16 * w + 4 * g]);
+                        const float sc[4] = {bf16_to_f32(sp.x & 0xFFFFu), bf16_to_f32(sp.x >> 16),
+                                             bf16_to_f32(sp.y & 0xFFFFu), bf16_to_f32(sp.y >> 16)};
+#pragma unroll
+                        for (int b = 0; b < TB; ++b)
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[v], dd[gb][b][v], acc[b][v]);
                     }
                 }
             }
+            __syncthreads();
         }
-        __syncthreads();
     }
 
+    if constexpr (KS > 1) {
+        // slices 1.. leave their sums in LDS (over the staged chunks, free
+        // after the loop's last barrier); slice 0 adds them in slice order
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(&xsa[0][0][0]);
+        static_assert(sizeof(xsa) >= (KS - 1) * 4 * TB * 64 * sizeof(f32x4_t), "reduction space");
+        if (ks > 0) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < TB; ++b) red[(((ks - 1) * 4 + w) * TB + b) * 64 + lane] = acc[b];
+        }
+        __syncthreads();
+        if (ks > 0) return;
+#pragma unroll
+        for (int q = 1; q < KS; ++q)
+#pragma unroll
+            for (int b = 0; b < TB; ++b) {
+                const f32x4_t o = red[(((q - 1) * 4 + w) * TB + b) * 64 + lane];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[b][v] += o[v];
+            }
+    }
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
         const int tok = t0 + 16 * b + li;
         if (b < nblk && tok < p.m) {
 #pragma unroll

@@ -47,9 +47,12 @@ def _run(codes, scales, x, gs, bf16=False):
     return host_y(y)
 
 
+# The workgroup splits K into 4, 2 or 1 slices by n (at most 4096, 10240, or
+# more rows) and by the number of 256-wide chunks; every split is covered.
 CASES = [
     (1, 32, 32, 5), (64, 256, 32, 16), (100, 3840, 32, 16), (1000, 4224, 64, 17), (130, 96, 32, 33),
     (77, 15360, 128, 64), (200, 3840, 32, 65), (33, 512, 64, 100), (300, 4096, 128, 8), (64, 2048, 32, 130),
+    (100, 512, 32, 16), (9000, 512, 32, 20), (9000, 768, 128, 40), (33000, 256, 64, 40), (33000, 512, 32, 70),
 ]
 
 
@@ -63,7 +66,8 @@ def test_qgemm_parity(n, k, gs, m):
     parity.assert_parity(y, y_ref, a_ref, "qgemm n=%d k=%d m=%d" % (n, k, m))
 
 
-@pytest.mark.parametrize("n,k,gs,m", [(150, 3840, 32, 37), (70, 4224, 128, 70)])
+@pytest.mark.parametrize("n,k,gs,m", [(150, 3840, 32, 37), (70, 4224, 128, 70), (9000, 1024, 64, 35),
+                                      (33000, 512, 32, 70)])
 def test_qgemm_rows_alone_repeat_and_bf16(n, k, gs, m):
     codes, scales, x = _inputs(n, k, gs, m, 9)
     log("qgemm rows alone n=%d k=%d m=%d" % (n, k, m))
