@@ -10,6 +10,7 @@
 #include "qgemv.h"
 #include "qgemv_launch.hpp"
 #include "qgemv_kernels.hpp"
+#include "qgemv_fp8_mfma.hpp"
 #include "stream_probe.hpp"
 
 #include <atomic>
@@ -201,10 +202,58 @@ bool row_instance_for(qg_format f, int r, int b, int j) {
     }
 }
 
+// FP8 with three or four activation rows runs on the matrix-core kernel
+// (qgemv_fp8_mfma.hpp) for every shape: 4-row tiles, x in LDS.  Its default launch is one workgroup of 8
+// waves per CU (fewer workgroups when tiles are few); rows_per_tile is fixed.
+Plan fp8_default_plan(const Params &p, int cus) {
+    Plan pl;
+    pl.row_kernel = false;
+    pl.passes = p.passes;
+    pl.rows_per_tile = qg::kFp8TileRows;
+    pl.waves_per_block = 8;
+    const int64_t tiles = (p.n + qg::kFp8TileRows - 1) / qg::kFp8TileRows;
+    int64_t blocks = cus;
+    const int64_t max_blocks = (tiles + pl.waves_per_block - 1) / pl.waves_per_block;
+    if (blocks > max_blocks) blocks = max_blocks;
+    pl.blocks = int(blocks < 1 ? 1 : blocks);
+    return pl;
+}
+
+qg_status run_fp8(Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream, int cus) {
+    p.passes = (p.chunks + qg::kFp8Slots - 1) / qg::kFp8Slots;
+    Plan pl = fp8_default_plan(p, cus);
+    if (override_plan) {
+        if (override_plan->waves_per_block) pl.waves_per_block = override_plan->waves_per_block;
+        if (override_plan->blocks) {
+            pl.blocks = override_plan->blocks;
+        } else {
+            const int64_t tiles = (p.n + qg::kFp8TileRows - 1) / qg::kFp8TileRows;
+            const int64_t max_blocks = (tiles + pl.waves_per_block - 1) / pl.waves_per_block;
+            int64_t b = int64_t(cus) * 8 / pl.waves_per_block;
+            pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
+        }
+    }
+    // LDS: x and two zero units (Fp8XLayout), the tile counter, the norm's group sums
+    const int64_t norm_bytes = p.norm ? int64_t(batch) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
+    int64_t lds = int64_t(batch) * p.k * 2 + qg::kLdsSink;
+    // the shared-tile counter, where it fits (otherwise each wave takes a
+    // fixed range of tiles; the result is the same bits either way)
+    if (lds + 16 + norm_bytes <= kMaxLds) {
+        p.counter_offset = int32_t(lds);
+        lds += 16;
+    }
+    p.norm_offset = int32_t(lds);
+    lds += norm_bytes;
+    if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
+    p.total_waves = pl.blocks * pl.waves_per_block;
+    return qgl::launch_fp8(p, pl, batch, lds, stream);
+}
+
 qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream) {
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
+    if (f == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch) return run_fp8(p, batch, override_plan, stream, cus);
     const Split sp = split_of(f, p);
     if (sp.ok) {
         p.segs = sp.segs;
@@ -490,6 +539,14 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     p.groups = gs ? int32_t(k / gs) : 0;
     p.group_shift = gs ? log2i(gs / fmt_info(format).wpc) : 0;
     p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));
+    if (format == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch) {
+        p.passes = (p.chunks + qg::kFp8Slots - 1) / qg::kFp8Slots;
+        const Plan pl = fp8_default_plan(p, cus);
+        out->rows_per_tile = pl.rows_per_tile;
+        out->waves_per_block = pl.waves_per_block;
+        out->blocks = pl.blocks;
+        return QG_OK;
+    }
     const Split sp = split_of(format, p);
     p.segs = sp.ok ? sp.segs : 0;
     p.passes = sp.ok ? sp.passes : passes_of(p.chunks);

@@ -299,10 +299,14 @@ __device__ __forceinline__ int row_of(int i, int per) {
 // by the loading waves right after their first loads are issued (the caller
 // can send its own loads behind them and wait for these alone).  With xdst
 // (and gdst) given, the raw units of x (and of gamma, [k/8]) are copied to LDS
-// on the way.
-template <int B, class Between>
+// on the way: unit u of batch row b to xdst[xidx(b, u, k / 8)].
+struct PackedRows {
+    __device__ int operator()(int b, int u, int upr) const { return b * upr + u; }
+};
+
+template <int B, class Between, class XIndex = PackedRows>
 __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst,
-                                          Between &&between) {
+                                          Between &&between, XIndex xidx = XIndex{}) {
     using Red = WaveSum<4>;
     const int lane = threadIdx.x & (kWave - 1);
     const int W = min(int(blockDim.x >> 6), kStageThreads / kWave);    // loading waves
@@ -330,7 +334,7 @@ __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&
         for (int i = 0; i < 4; ++i) {
             const bool real = g0 + i * W < ng && uu[i] < upr;
             sq[i] = real ? unit_sumsq(v[i]) : 0.0f;
-            if (xdst && real) xdst[bb[i] * upr + uu[i]] = v[i];
+            if (xdst && real) xdst[xidx(bb[i], uu[i], upr)] = v[i];
             if (gdst && real && g0 + i * W < gpr) gdst[uu[i]] = gv[i];
         }
         Red::run(sq);

@@ -27,18 +27,20 @@ struct Plan {
 };
 
 
-template <class Kern>
-inline qg_status launch(Kern kern, const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
+// One function per kernel instance, so that each instance raises its own
+// LDS limit once.
+template <auto Kern>
+inline qg_status launch(const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
     if (lds > 64 * 1024) {
         static std::once_flag attr_once;
         static hipError_t attr_err = hipSuccess;
         std::call_once(attr_once, [&] {
-            attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+            attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
         });
         if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
     }
-    hipLaunchKernelGGL(kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
+    hipLaunchKernelGGL(Kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -61,18 +63,15 @@ qg_status launch_row_j(const Params &p, const Plan &pl, int64_t lds, hipStream_t
     switch (pl.passes) {
         case 1:
             if constexpr (row_instance<Fmt, R, B, 1>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1, B * 1 * Fmt::kPieces), 1, kNorm>, p, pl,
-                              lds, s);
+                return launch<qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 1, B * 1 * Fmt::kPieces), 1, kNorm>>(p, pl, lds, s);
             break;
         case 2:
             if constexpr (row_instance<Fmt, R, B, 2>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2, B * 2 * Fmt::kPieces), 2, kNorm>, p, pl,
-                              lds, s);
+                return launch<qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 2, B * 2 * Fmt::kPieces), 2, kNorm>>(p, pl, lds, s);
             break;
         case 4:
             if constexpr (row_instance<Fmt, R, B, 4>())
-                return launch(qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4, B * 4 * Fmt::kPieces), 4, kNorm>, p, pl,
-                              lds, s);
+                return launch<qg::qgemv_row_kernel<Fmt, R, B, row_depth(R, 4, B * 4 * Fmt::kPieces), 4, kNorm>>(p, pl, lds, s);
             break;
     }
     return QG_ERR_LAUNCH;     // not reached: the planner only picks existing instances
@@ -84,10 +83,10 @@ template <class Fmt, int R, int B>
 qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
     if (p.norm) {
         if (pl.row_kernel) return launch_row_j<Fmt, R, B, true>(p, pl, lds, s);
-        return launch(qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), true>, p, pl, lds, s);
+        return launch<qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), true>>(p, pl, lds, s);
     }
     if (pl.row_kernel) return launch_row_j<Fmt, R, B, false>(p, pl, lds, s);
-    return launch(qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), false>, p, pl, lds, s);
+    return launch<qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), false>>(p, pl, lds, s);
 }
 
 template <class Fmt, int R>

@@ -136,6 +136,15 @@ qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales,
  *   codes      DEVICE uint8 [n, k].
  *   row_scale  DEVICE float [n].
  *   W^[n,k] = row_scale[n] * E4M3(code[n,k]); a NaN code gives a NaN row.
+ *
+ * With one or two activation rows the products are summed by the vector unit
+ * (two-wide bf16 dots); with three or four, by the matrix cores in 4x4x4
+ * blocks (4 weight rows x 4 batch rows per block), whose cost does not grow
+ * with the batch.  The two orders of addition differ, so a row's bits from a
+ * batch of 1 or 2 can differ from its bits in a batch of 3 or 4 (both within
+ * the same bound of the exact sum); inside each group of batch sizes they
+ * are identical.  The matrix-core path takes 4-row tiles: rows_per_tile of a
+ * qg_plan is ignored there.
  */
 qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale,
                          const uint16_t *x, void *y,
@@ -148,8 +157,9 @@ qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale,
  * the same arguments plus a qg_plan whose non-zero fields override that
  * choice (for tuning a deployment's own shapes); plan == NULL is the plain
  * call.  Results are bitwise the same for every plan: a row's terms are
- * added in an order fixed by the format and k alone, whichever wavefront,
- * tile shape or grid computes it.
+ * added in an order fixed by the format and k alone (for FP8, also by
+ * whether the batch is below 3), whichever wavefront, tile shape or grid
+ * computes it.
  * ---------------------------------------------------------------------- */
 
 typedef struct qg_plan {

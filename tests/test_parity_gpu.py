@@ -147,6 +147,9 @@ def test_staging_limit_is_enforced():
 
 @pytest.mark.parametrize("n,k,batch", [
     (1, 16, 1), (8, 48, 2), (50, 3840, 4), (257, 1040, 1), (19, 4096, 3), (2, 15360, 1),
+    # matrix-core path (batch 3, 4): a single row, a ragged last pass, rows of
+    # several steps with a ragged tail, a row count off the 4-row tiles
+    (1, 16, 3), (7, 272, 4), (1003, 4112, 3), (4097, 1024, 4), (30, 9984, 4),
 ])
 def test_fp8_shapes(n, k, batch):
     _case("fp8", n, k, None, batch, seed=n * 7 + k)
@@ -295,12 +298,24 @@ def test_batch_rows_match_single_calls_bitwise(fmt, gs, k):
     x4 = synth.activations(9, 4, k)
     log("batch consistency %s" % fmt)
     y4 = run(fmt, arrays, x4, n, gs=gs)
-    for b in range(4):
-        y1 = run(fmt, arrays, x4[b:b + 1], n, gs=gs)
-        assert np.array_equal(y1[0], y4[b]), (fmt, b)
-    for bsz in (2, 3):
-        yb = run(fmt, arrays, x4[:bsz], n, gs=gs)
-        assert np.array_equal(yb, y4[:bsz])
+    ys = {bsz: run(fmt, arrays, x4[:bsz], n, gs=gs) for bsz in (1, 2, 3)}
+    ys[4] = y4
+    singles = [run(fmt, arrays, x4[b:b + 1], n, gs=gs)[0] for b in range(4)]
+    if fmt != "fp8":
+        for b in range(4):
+            assert np.array_equal(singles[b], y4[b]), (fmt, b)
+        for bsz in (2, 3):
+            assert np.array_equal(ys[bsz], y4[:bsz])
+    else:
+        # FP8 sums on the vector unit below 3 activation rows and on the
+        # matrix cores from 3 on: bitwise inside each group, and both groups
+        # within the parity bound of the exact result
+        for b in range(2):
+            assert np.array_equal(singles[b], ys[2][b]), b
+        assert np.array_equal(ys[3], y4[:3])
+        y_ref, a_ref = _oracle(fmt, arrays, x4, gs)
+        parity.assert_parity(y4, y_ref, a_ref)
+        parity.assert_parity(np.stack(singles), y_ref, a_ref)
 
 
 PLANS = [None, {"rows_per_tile": 1}, {"rows_per_tile": 2}, {"rows_per_tile": 4},
@@ -310,12 +325,13 @@ PLANS = [None, {"rows_per_tile": 1}, {"rows_per_tile": 2}, {"rows_per_tile": 4},
          {"waves_per_block": 3, "blocks": 7}]
 
 
-@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 3840), ("u4", 64, 15360), ("u8", 128, 1024), ("fp8", None, 2048)])
-def test_launch_shapes_bitwise_identical(fmt, gs, k):
+@pytest.mark.parametrize("fmt,gs,k,batch", [("fp4", 32, 3840, 2), ("u4", 64, 15360, 2), ("u8", 128, 1024, 2),
+                                            ("fp8", None, 2048, 2), ("fp8", None, 3840, 4), ("fp8", None, 5120, 3)])
+def test_launch_shapes_bitwise_identical(fmt, gs, k, batch):
     n = 1001
     w = synth.weights(10, n, k)
     arrays = _quantize(fmt, w, gs)
-    x = synth.activations(10, 2, k)
+    x = synth.activations(10, batch, k)
     ys = []
     for plan in PLANS:
         log("plan %s %s" % (fmt, plan))
