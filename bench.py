@@ -316,7 +316,8 @@ def run_sweep(args):
         rows.extend(run_qgemm_sweep(args))
     if not only or "step48" in only:
         step = run_decode_step(args)
-        per_shape = {r["shape"]: r["us"] for r in rows if r["fmt"] == "fp4" and r["batch"] == 1}
+        per_shape = {r["shape"]: r["us"] for r in rows
+                     if r["fmt"] == "fp4" and r.get("kernel") != "qgemm" and r.get("batch") == 1}
         if all(s in per_shape for s in ("qkv", "o_proj", "gate_up", "fc_down")):
             # the step beside 48 x the sum of the per-shape times measured alone
             step["sum_of_shapes_us"] = round(48 * sum(per_shape[s] for s in ("qkv", "o_proj", "gate_up", "fc_down")), 2)
