@@ -27,9 +27,13 @@
 // rows 0..3, times the row scale.  The order of every addition is fixed by k
 // alone: not by the tile, the wavefront, the launch shape or the batch size.
 //
-// Steps: a tile's passes (ceil(chunks / 16)) are cut into steps of PS passes;
-// loads run D steps ahead.  Chunks past the row end read zeros through the
-// buffer resource and take x from zero units in LDS.
+// Steps: a tile's passes (ceil(chunks / 16)) are cut into steps of PS passes,
+// each one buffer of loads; loads run D steps ahead.  Rows of at most 16
+// passes (k <= 4096) are one or two steps of 8 passes, a compile-time shape
+// (kH): each lane's slice of x is then the same for every tile and is read
+// from LDS into registers once.  Longer rows take steps of 4, 8 or 16 passes
+// and read x from LDS pass by pass.  Chunks past the row end read zeros
+// through the buffer resource and take x from zero units in LDS.
 #pragma once
 
 #include "qgemv_common.hpp"
@@ -52,14 +56,17 @@ constexpr int kFp8ChunksPerWave = 16;  // shared tiles are handed out in about 1
 // kernel 146.3, 148.6, 159.9, 166.0; this kernel 149.9, 152.2, 153.9, 156.7).
 constexpr int kFp8MfmaMinBatch = 3;
 
-// Passes per step: a row of at most 16 passes is one step (4, 8 or 16
-// passes, the fewest that hold it), so every tile issues the same per-lane
-// offsets and they stay in registers; longer rows take the step of 4, 8 or 16
-// passes that pads them the least (the larger on a tie).  Depends on the
-// number of chunks alone.
+// Rows of at most 16 passes: halves (steps of 8 passes) per tile, x in
+// registers; 0 for longer rows.
+__host__ __device__ constexpr int fp8_mfma_halves(int chunks) {
+    const int passes = (chunks + kFp8Slots - 1) / kFp8Slots;
+    return passes <= 8 ? 1 : (passes <= 16 ? 2 : 0);
+}
+
+// Passes per step of a longer row: 4, 8 or 16, whichever pads its passes the
+// least (the larger on a tie).  Depends on the number of chunks alone.
 __host__ __device__ constexpr int fp8_mfma_step_passes(int chunks) {
     const int passes = (chunks + kFp8Slots - 1) / kFp8Slots;
-    if (passes <= 16) return passes <= 4 ? 4 : (passes <= 8 ? 8 : 16);
     int best = 16, best_pad = ((passes + 15) / 16) * 16 - passes;
     for (int ps = 8; ps >= 4; ps /= 2) {
         const int pad = ((passes + ps - 1) / ps) * ps - passes;
@@ -98,9 +105,13 @@ __device__ __forceinline__ float mfma_row_sum(float v) {
     return a + b;
 }
 
-// kOneStep: the row is one step (G = 1), known at compile time.
-template <int B, int PS, int D, bool kNorm, bool kOneStep>
+// kH > 0: rows of kH steps of PS = 8 passes, x in registers, D = 2 buffers
+// (with kH = 2, buffer h always holds half h of a tile).  kH = 0: rows of
+// any length, x read from LDS pass by pass.
+template <int B, int PS, int D, bool kNorm, int kH>
 __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
+    constexpr bool kXReg = kH > 0;
+    static_assert(!kXReg || (PS == 8 && D == 2), "register-x shapes: steps of 8 passes, two buffers");
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int lane = threadIdx.x & (kWave - 1);
     const int ri = lane & 3;                  // A: tile row; B, D: batch column
@@ -108,16 +119,16 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
     const int jb = ri < B ? ri : B - 1;       // batch row this lane's B column carries
 
     // Tiles are whole groups of 4 rows from row 0, split evenly over the
-    // workgroups.  A wave's work is a sequence of items, each one buffer of
-    // loads:
-    //  * rows of one step, with room in LDS for a counter (p.counter_offset):
-    //    items are the workgroup's tiles, cut into chunks of C consecutive
-    //    tiles; wave w starts with chunk w and later chunks come from the
-    //    counter, first come first served (the waves of a workgroup are
-    //    served unevenly by the memory system; this way they finish together);
-    //  * otherwise: the steps of a contiguous range of tiles per wave.
-    // Items come in increasing order, and an item at or past n_items stands
-    // for "nothing" (its loads read no memory).
+    // workgroups.  A wave's work is a sequence of items in increasing order
+    // (an item at or past n_items stands for "nothing": its loads read no
+    // memory):
+    //  * kH > 0, with room in LDS for a counter (p.counter_offset): items are
+    //    the workgroup's tiles, cut into chunks of C consecutive tiles; wave w
+    //    starts with chunk w and later chunks come from the counter, first
+    //    come first served (the waves of a workgroup are served unevenly by
+    //    the memory system; this way they finish together);
+    //  * kH > 0 otherwise: the tiles of a contiguous range per wave;
+    //  * kH = 0: the steps of a contiguous range of tiles per wave.
     const int64_t tiles_all = (p.n + kFp8TileRows - 1) / kFp8TileRows;
     const int nb = gridDim.x;
     const int64_t blk = logical_block();
@@ -128,9 +139,9 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
     const int64_t tb = t_begin + int64_t(w) * T / W;
     const int64_t te = t_begin + int64_t(w + 1) * T / W;
     const int passes = p.passes;                              // ceil(chunks / 16)
-    const int G = kOneStep ? 1 : (passes + PS - 1) / PS;      // steps per tile
-    const bool shared = kOneStep && p.counter_offset != 0;    // uniform
-    const int n_items = shared ? T : int(te - tb) * G;
+    const int G = kXReg ? kH : (passes + PS - 1) / PS;        // steps per tile
+    const bool shared = kXReg && p.counter_offset != 0;       // uniform
+    const int n_items = shared ? T : int(te - tb) * (kXReg ? 1 : G);
     const int C = max(1, T / (kFp8ChunksPerWave * W));        // tiles per shared chunk
     unsigned *counter = reinterpret_cast<unsigned *>(smem + p.counter_offset);
     int chunk = w, cur = w * C;
@@ -146,30 +157,31 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
         cur = __builtin_amdgcn_readfirstlane(cur < T ? cur + 1 : cur);
         return __builtin_amdgcn_readfirstlane(t);
     };
-    auto first_item = [&](int d) __attribute__((always_inline)) { return shared ? next_tile() : d; };
-    auto next_item = [&](int prev) __attribute__((always_inline)) { return shared ? next_tile() : prev + D; };
-    // first row of an item's tile, and its step within the tile
-    auto locate = [&](int item, int64_t &row0, int &g) __attribute__((always_inline)) {
-        if (shared) {
-            row0 = (t_begin + item) * kFp8TileRows;
-            g = 0;
+    // first row of an item's tile, and its step within the tile (kH > 0:
+    // the step is the buffer's half, given)
+    auto locate = [&](int item, int half, int64_t &row0, int &g) __attribute__((always_inline)) {
+        if (kXReg) {
+            row0 = ((shared ? t_begin : tb) + item) * kFp8TileRows;
+            g = half;
         } else {
-            const int tq = kOneStep ? item : item / G;
-            g = kOneStep ? 0 : item - tq * G;
+            const int tq = item / G;
+            g = item - tq * G;
             row0 = (tb + tq) * kFp8TileRows;
         }
     };
+    // the buffer a ring slot's half is (kH = 2: slot d holds half d)
+    auto half_of = [](int d) { return kH == 2 ? d : 0; };
 
     struct Buf {
         uint4 c[PS];
         uint32_t rs;       // row scale of tile row (lane >> 2) & 3
     };
     const uint32_t row_bytes = uint32_t(p.row_bytes);
-    auto issue = [&](Buf &bf, int item_in) __attribute__((always_inline)) {
+    auto issue = [&](Buf &bf, int item_in, int half) __attribute__((always_inline)) {
         const int item = __builtin_amdgcn_readfirstlane(item_in);
         int64_t row0;
         int g;
-        locate(item, row0, g);
+        locate(item, half, row0, g);
         const int64_t valid = item < n_items ? min(int64_t(kFp8TileRows), p.n - row0) : 0;
         const int64_t rb = valid ? row0 : 0;
         const rsrc_t rc = make_rsrc(p.codes + rb * p.row_bytes, uint32_t(valid) * row_bytes);
@@ -196,15 +208,21 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
         const int b = row_of<B>(u, upr);
         return xl(b, u - b * upr, upr);
     };
+    // LDS unit of the first half of the activations of pass gq (the second
+    // half is R + 1 units further)
+    auto x_at = [&](int gq) {
+        const int c = slot + kFp8Slots * gq;
+        return c < p.chunks ? c * B + jb : xl.R;
+    };
     constexpr int kStepLoads = PS + 1;
     Buf buf[D];
     int sl[D];
-    sl[0] = first_item(0);
+    sl[0] = shared ? next_tile() : 0;
     if (shared && threadIdx.x == 0) *counter = unsigned(W);       // the next chunk to hand out
     if constexpr (kNorm) {
         float rn[B];
         block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, nullptr, [&] {
-            issue(buf[0], sl[0]);
+            issue(buf[0], sl[0], half_of(0));
             wait_vm_loads<kStepLoads>();
         }, xl);
         for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
@@ -222,7 +240,7 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
             for (int i = 0; i < kXu; ++i)
                 xr[i] = load_x_unit(p.x + int64_t(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1)) * 8);
         }
-        issue(buf[0], sl[0]);
+        issue(buf[0], sl[0], half_of(0));
         if (few) {
             wait_vm_loads<kStepLoads>();
 #pragma unroll
@@ -238,49 +256,65 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
     __syncthreads();
 #pragma unroll
     for (int d = 1; d < D; ++d) {
-        sl[d] = first_item(d);
-        issue(buf[d], sl[d]);
+        sl[d] = kH == 2 ? sl[0] : (shared ? next_tile() : d);
+        issue(buf[d], sl[d], half_of(d));
+    }
+    // the lane's slice of x for every pass of a tile (kH > 0)
+    constexpr int kXr = kXReg ? kH * PS : 1;
+    uint4 xreg[kXr][2];
+    if constexpr (kXReg) {
+#pragma unroll
+        for (int gq = 0; gq < kXr; ++gq) {
+            const int a = x_at(gq);
+            xreg[gq][0] = xlds[a];
+            xreg[gq][1] = xlds[a + xl.R + 1];
+        }
     }
 
     mfma_f32x4_t acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto consume = [&](const Buf &bf, int item) __attribute__((always_inline)) {
+    auto mul_pass = [&](const uint4 cq, const uint4 x0, const uint4 x1) __attribute__((always_inline)) {
+        const uint32_t xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const uint32_t wv[4] = {cq.x, cq.y, cq.z, cq.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[m], 1.0f, false);
+            const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[m], 1.0f, true);
+            const u32x2_t a2 = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            const u32x2_t b2 = {xv[2 * m], xv[2 * m + 1]};
+            const mfma_i16x4_t a = __builtin_bit_cast(mfma_i16x4_t, a2);
+            const mfma_i16x4_t bx = __builtin_bit_cast(mfma_i16x4_t, b2);
+            if (m & 1)
+                acc1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, bx, acc1, 0, 0, 0);
+            else
+                acc0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, bx, acc0, 0, 0, 0);
+        }
+    };
+    auto consume = [&](const Buf &bf, int item, int half) __attribute__((always_inline)) {
         int64_t row0;
         int g;
-        locate(item, row0, g);
-        // x of pass q + 1 is read from LDS before pass q is multiplied
-        auto x_at = [&](int q) {
-            const int c = slot + kFp8Slots * (g * PS + q);
-            return c < p.chunks ? c * B + jb : xl.R;
-        };
-        uint4 xn0 = xlds[x_at(0)], xn1 = xlds[x_at(0) + xl.R + 1];
+        locate(item, half, row0, g);
+        if constexpr (kXReg) {
 #pragma unroll
-        for (int q = 0; q < PS; ++q) {
-            const uint4 x0 = xn0, x1 = xn1;
-            if (q + 1 < PS) {
-                const int a = x_at(q + 1);
-                xn0 = xlds[a];
-                xn1 = xlds[a + xl.R + 1];
-                // keep these reads ahead of this pass's work (the scheduler
-                // would otherwise sink them to their use and expose their latency)
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            const uint32_t xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const uint32_t wv[4] = {bf.c[q].x, bf.c[q].y, bf.c[q].z, bf.c[q].w};
+            for (int q = 0; q < PS; ++q) mul_pass(bf.c[q], xreg[half * PS + q][0], xreg[half * PS + q][1]);
+        } else {
+            // x of pass q + 1 is read from LDS before pass q is multiplied
+            int a = x_at(g * PS);
+            uint4 xn0 = xlds[a], xn1 = xlds[a + xl.R + 1];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const bf16x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[m], 1.0f, false);
-                const bf16x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wv[m], 1.0f, true);
-                const u32x2_t a2 = {__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-                const u32x2_t b2 = {xv[2 * m], xv[2 * m + 1]};
-                const mfma_i16x4_t a = __builtin_bit_cast(mfma_i16x4_t, a2);
-                const mfma_i16x4_t bx = __builtin_bit_cast(mfma_i16x4_t, b2);
-                if (m & 1)
-                    acc1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, bx, acc1, 0, 0, 0);
-                else
-                    acc0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, bx, acc0, 0, 0, 0);
+            for (int q = 0; q < PS; ++q) {
+                const uint4 x0 = xn0, x1 = xn1;
+                if (q + 1 < PS) {
+                    a = x_at(g * PS + q + 1);
+                    xn0 = xlds[a];
+                    xn1 = xlds[a + xl.R + 1];
+                    // keep these reads ahead of this pass's work (the scheduler
+                    // would otherwise sink them to their use and expose their latency)
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                mul_pass(bf.c[q], x0, x1);
             }
         }
-        if (kOneStep || g == G - 1) {
+        if (g == G - 1) {
             float tot[kFp8TileRows];
 #pragma unroll
             for (int i = 0; i < kFp8TileRows; ++i) tot[i] = mfma_row_sum(acc0[i] + acc1[i]);
@@ -298,22 +332,31 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
         }
     };
 
-    // Buffers hold items in increasing order; the loop runs while the last
-    // one holds an item (then all do), each buffer is refilled right after it
-    // is consumed (refills past the end read nothing from memory), and the
-    // loop's only exit is its test at the top.
+    // Buffers hold items in increasing order (kH = 2: both buffers the same
+    // tile); the loop runs while the last one holds an item (then all do),
+    // each buffer is refilled right after it is consumed (refills past the
+    // end read nothing from memory), and the loop's only exit is its test at
+    // the top.
+    auto advance = [&](int d) __attribute__((always_inline)) -> int {
+        if constexpr (kH == 2) return d == 0 ? (shared ? next_tile() : sl[0] + 1) : sl[0];
+        return shared ? next_tile() : sl[d] + D;
+    };
+    // (The scheduling barriers keep each buffer's work in its place: hoisted
+    // into the previous buffer's passes, the next buffer's tile-end reads
+    // made the wait there cover every load in flight.)
     while (sl[D - 1] < n_items) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
-            const int nx = next_item(sl[d]);
-            consume(buf[d], sl[d]);
+            const int nx = advance(d);
+            consume(buf[d], sl[d], half_of(d));
             sl[d] = nx;
-            issue(buf[d], nx);
+            issue(buf[d], nx, half_of(d));
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 #pragma unroll
     for (int d = 0; d < D - 1; ++d)
-        if (sl[d] < n_items) consume(buf[d], sl[d]);
+        if (sl[d] < n_items) consume(buf[d], sl[d], half_of(d));
     wait_vm_loads<0>();
 }
 
