@@ -5,6 +5,8 @@
 #include "qgemv.h"
 #include "qgemm_kernels.hpp"
 
+#include <mutex>
+
 namespace {
 
 bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -48,9 +50,43 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
     const int tb_max = 4 / ks;
     const int tb = m <= 16 ? 1 : (m <= 32 || tb_max == 2 ? 2 : 4);
     const int tbu = tb > tb_max ? tb_max : tb;
+    const int spg = group_size / 32;
+    // up to 16 activation rows whose x fits in LDS: x staged once per
+    // workgroup, weight tiles streamed without barriers (the same bits)
+    const int64_t small_lds = qg::gemm_small_lds(k, m);
+    if (m <= 16 && small_lds <= 128 * 1024) {
+        int cus = 0, dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            return QG_ERR_DEVICE;
+        // one workgroup per CU (x fills most of its LDS), with as many waves
+        // as the 16-row tiles need to cover the chip, 1..8
+        const int64_t rtiles = (n + 15) / 16;
+        int64_t wpb = (rtiles + cus - 1) / cus;
+        wpb = wpb < 1 ? 1 : (wpb > qg::kGemmSmallWaves ? qg::kGemmSmallWaves : wpb);
+        int64_t blocks = (rtiles + wpb - 1) / wpb;
+        if (blocks > cus) blocks = cus;
+        const dim3 sgrid{unsigned(blocks)}, sblock{unsigned(64 * wpb)};
+#define QG_GEMM_SMALL(S, K)                                                                             \
+        if (spg == S && ks == K) {                                                                      \
+            static std::once_flag once;                                                                 \
+            static hipError_t attr = hipSuccess;                                                        \
+            std::call_once(once, [] {                                                                   \
+                attr = hipFuncSetAttribute(reinterpret_cast<const void *>(qg::qgemm_fp4_small_kernel<S, K>), \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);      \
+            });                                                                                         \
+            if (attr != hipSuccess) return QG_ERR_LAUNCH;                                               \
+            hipLaunchKernelGGL((qg::qgemm_fp4_small_kernel<S, K>), sgrid, sblock, size_t(small_lds), stream, p); \
+            return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                             \
+        }
+        QG_GEMM_SMALL(1, 1) QG_GEMM_SMALL(1, 2) QG_GEMM_SMALL(1, 4)
+        QG_GEMM_SMALL(2, 1) QG_GEMM_SMALL(2, 2) QG_GEMM_SMALL(2, 4)
+        QG_GEMM_SMALL(4, 1) QG_GEMM_SMALL(4, 2) QG_GEMM_SMALL(4, 4)
+#undef QG_GEMM_SMALL
+        return QG_ERR_LAUNCH;     // not reached
+    }
     const dim3 grid(unsigned(tiles), unsigned((m + 16 * tbu - 1) / (16 * tbu)));
     const dim3 block(unsigned(256 * ks));
-    const int spg = group_size / 32;
 #define QG_GEMM_CASE(S, T, K)                                                                   \
     if (spg == S && tbu == T && ks == K) {                                                      \
         hipLaunchKernelGGL((qg::qgemm_fp4_kernel<S, T, K>), grid, block, 0, stream, p);        \

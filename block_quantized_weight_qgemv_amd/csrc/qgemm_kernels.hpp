@@ -258,4 +258,194 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
     }
 }
 
+// ------------------------------------------------------------------ m <= 16
+
+// Up to 16 activation rows, whose x (m rows, k rounded up to whole 256-wide
+// chunks, zeros past k) fits in LDS: the workgroup stages all of x once, and
+// each wave then streams its own 16-row weight tiles with no barrier, loads
+// running several chunks ahead in a register ring.  The MFMA takes x as A
+// (rows = activation rows) and the weights as B, so lane l gets
+// D[4(l/16)+v][l%16] = the sums of activation rows 4(l/16)+v for weight row
+// l%16: the weight row whose codes and group scale the lane loaded itself.
+//
+// The order of every addition is that of qgemm_fp4_kernel with the same KS
+// (which depends on n and k alone): chunk c is summed into slice c % KS, a
+// group's MFMA chain starts from zero and is scaled into its slice in group
+// order, and the slices are added in slice order at the end.  The MFMA
+// operands of a group are the same values in both kernels.  So a row's bits
+// are the same whichever kernel, m or launch computes it.
+constexpr int kGemmSmallWaves = 8;                 // most waves per workgroup
+constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane
+
+template <int SPG, int KS>
+__global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(const GemmParams p) {
+    constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
+    constexpr int PD = kGemmSmallDepth;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *xs = reinterpret_cast<uint16_t *>(smem);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g = lane >> 4;                       // k quarter of an MFMA step; D row quarter
+    const int li = lane & 15;                      // A row (activation row) and B column (weight row)
+    const int nch = (p.k + kGemmKC - 1) / kGemmKC;
+    const int xstride = nch * kGemmKC + kGemmXPad; // bf16 per staged activation row
+    const int64_t row_bytes = p.k / 2;
+
+    // x -> LDS once: m rows, zeros from k to the end of the last chunk;
+    // kStage loads in flight per thread (one at a time, every thread would
+    // wait out the load latency once per unit)
+    constexpr int kStage = 16;
+    const int upr = xstride / 8;                   // 16-byte units per staged row
+    const int units = p.m * upr;
+    for (int u0 = threadIdx.x; u0 < units; u0 += kStage * int(blockDim.x)) {
+        uint4 v[kStage];
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int u = min(u0 + i * int(blockDim.x), units - 1);
+            const int t = u / upr, ku = (u - t * upr) * 8;
+            v[i] = load_x_unit(p.x + int64_t(t) * p.k + min(ku, p.k - 8));
+        }
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int u = u0 + i * int(blockDim.x);
+            if (u < units) {
+                const int t = u / upr, ku = (u - t * upr) * 8;
+                *reinterpret_cast<uint4 *>(xs + t * xstride + ku) = ku < p.k ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    __syncthreads();
+
+    // 16-row tiles split evenly over the grid's waves (contiguous ranges);
+    // a wave's items are its tiles' chunks in order
+    const int64_t tiles = (p.n + 15) / 16;
+    const int wpb = blockDim.x >> 6;
+    const int64_t gw = int64_t(blockIdx.x) * wpb + wave_in_block();
+    const int64_t nw = int64_t(gridDim.x) * wpb;
+    const int64_t tb = gw * tiles / nw, te = (gw + 1) * tiles / nw;
+    const int items = int(te - tb) * nch;
+    // activation row this lane's A operand reads (rows past m repeat row
+    // m - 1: their sums are never stored)
+    const uint16_t *xrow = xs + min(li, p.m - 1) * xstride + 8 * g;
+
+    struct Buf {
+        uint32_t w[8];                             // one dword of codes per MFMA step
+        uint32_t sc[gpc];                          // the lane's row's group scales (bf16 bits)
+    };
+    auto issue = [&](Buf &bf, int item_in) __attribute__((always_inline)) {
+        const int item = __builtin_amdgcn_readfirstlane(min(item_in, max(items - 1, 0)));
+        const int tq = __builtin_amdgcn_readfirstlane(item / nch);
+        const int c = item - tq * nch;
+        // rows past n read row n - 1; steps past k read the row's last 16
+        // bytes (their activations are zeros)
+        const int64_t row = min((tb + tq) * 16 + li, p.n - 1);
+        const unsigned char *wrow = p.codes + row * row_bytes;
+        const int64_t kb = int64_t(c) * (kGemmKC / 2);
+        // (cached loads: a chunk's 8 loads take 4-byte pieces of the same
+        // 128-byte line of each row, which the vector cache merges)
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            bf.w[s] = *reinterpret_cast<const uint32_t *>(wrow + min(kb + 16 * s, row_bytes - 16) + 4 * g);
+#pragma unroll
+        for (int j = 0; j < gpc; ++j) bf.sc[j] = p.scales[row * p.groups + min(c * gpc + j, p.groups - 1)];
+    };
+
+    f32x4_t acc[KS];
+#pragma unroll
+    for (int q = 0; q < KS; ++q)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[q][v] = 0.0f;
+
+    auto consume = [&](const Buf &bf, int item) __attribute__((always_inline)) {
+        const int tq = __builtin_amdgcn_readfirstlane(item / nch);
+        const int c = item - tq * nch;
+        // every group's chain first, then the folds in group order
+        f32x4_t dd[gpc];
+#pragma unroll
+        for (int j = 0; j < gpc; ++j) {
+            f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < SPG; ++t) {
+                const int s = j * SPG + t;
+                const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xrow + c * kGemmKC + 32 * s);
+                const uint32_t q = bf.w[s];
+                const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
+                const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
+                const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
+                const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                const bf16x8_t wb = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                                            __builtin_shufflevector(p2, p3, 0, 1, 2, 3),
+                                                            0, 1, 2, 3, 4, 5, 6, 7);
+                d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, d0, 0, 0, 0);
+            }
+            dd[j] = d0;
+        }
+        auto fold = [&](f32x4_t &a) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < gpc; ++j) {
+                const float sv = bf16_to_f32(bf.sc[j] & 0xFFFFu);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) a[v] = fmaf(sv, dd[j][v], a[v]);
+            }
+        };
+        if constexpr (KS == 1) {
+            fold(acc[0]);
+        } else {
+            const int sl = c % KS;                 // uniform
+#pragma unroll
+            for (int q = 0; q < KS; ++q)
+                if (sl == q) fold(acc[q]);
+        }
+        if (c == nch - 1) {
+            f32x4_t tot = acc[0];
+#pragma unroll
+            for (int q = 1; q < KS; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) tot[v] += acc[q][v];
+            const int64_t row = (tb + tq) * 16 + li;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = 4 * g + v;
+                if (tok < p.m && row < p.n) {
+                    if (p.out_bf16)
+                        reinterpret_cast<uint16_t *>(p.y)[int64_t(tok) * p.n + row] =
+                            static_cast<uint16_t>(f32_to_bf16_rne(tot[v]));
+                    else
+                        reinterpret_cast<float *>(p.y)[int64_t(tok) * p.n + row] = tot[v];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < KS; ++q)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[q][v] = 0.0f;
+        }
+    };
+
+    // the ring: buffers hold items in increasing order; refills past the end
+    // reload the last item (never consumed)
+    Buf buf[PD];
+    int sl[PD];
+#pragma unroll
+    for (int d = 0; d < PD; ++d) {
+        sl[d] = d;
+        issue(buf[d], d);
+    }
+    while (sl[PD - 1] < items) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) {
+            consume(buf[d], sl[d]);
+            sl[d] += PD;
+            issue(buf[d], sl[d]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < PD - 1; ++d)
+        if (sl[d] < items) consume(buf[d], sl[d]);
+}
+
+// LDS bytes of qgemm_fp4_small_kernel's staged activations
+__host__ __device__ constexpr int64_t gemm_small_lds(int64_t k, int m) {
+    return int64_t(m) * (((k + kGemmKC - 1) / kGemmKC) * kGemmKC + kGemmXPad) * 2;
+}
+
 }  // namespace qg

@@ -277,6 +277,10 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
  *   n >= 1, 32 <= k <= 2^30, k % 32 == 0          QG_ERR_BAD_SHAPE
  *   group_size in {32, 64, 128}, k % group_size == 0   QG_ERR_BAD_GROUP_SIZE
  *   1 <= m <= QG_GEMM_MAX_M                       QG_ERR_BAD_BATCH
+ * Up to 16 activation rows whose x fits in LDS (m * k * 2 bytes, k rounded
+ * up to 256, at most 128 KiB) stage x once per workgroup and stream the
+ * weight tiles without barriers; more rows take a kernel that stages x chunk
+ * by chunk.  Both add a row's terms in the same order.
  * No device memory is allocated; asynchronous on `stream`.  For m <= 4 the
  * matvec entry points are the faster path. */
 #define QG_GEMM_MAX_M 65536

@@ -102,3 +102,16 @@ def test_qgemm_zero_scales_give_zero_rows():
     scales[::3] = 0
     y = _run(codes, scales, x, gs)
     assert np.all(y[:, ::3] == 0)
+
+
+@pytest.mark.parametrize("n,k,gs", [(2000, 3840, 32), (130, 4096, 64), (20000, 1024, 128)])
+def test_qgemm_small_m_kernel_matches_general_kernel_bitwise(n, k, gs):
+    """Up to 16 activation rows whose x fits in LDS take the streaming kernel;
+    17 rows take the general one.  Both add a row's terms in the same order."""
+    codes, scales, x = _inputs(n, k, gs, 17, 11)
+    log("qgemm small-m vs general n=%d k=%d gs=%d" % (n, k, gs))
+    y17 = _run(codes, scales, x, gs)
+    y16 = _run(codes, scales, x[:16], gs)
+    assert np.array_equal(y16, y17[:16])
+    y_ref, a_ref = G.gemv_fp4_e2m1(codes, scales, x, gs)
+    parity.assert_parity(y17, y_ref, a_ref, "qgemm n=%d k=%d m=17" % (n, k))
