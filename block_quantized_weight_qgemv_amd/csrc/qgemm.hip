@@ -67,21 +67,26 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
         int64_t blocks = (rtiles + wpb - 1) / wpb;
         if (blocks > cus) blocks = cus;
         const dim3 sgrid{unsigned(blocks)}, sblock{unsigned(64 * wpb)};
-#define QG_GEMM_SMALL(S, K)                                                                             \
-        if (spg == S && ks == K) {                                                                      \
+        // a chunk's group scales as one vector load when they are aligned
+        const int gpc = 8 / spg;
+        const bool vs = p.groups % gpc == 0 && aligned_to(scales, uintptr_t(2 * gpc));
+#define QG_GEMM_SMALL(S, K, V)                                                                          \
+        if (spg == S && ks == K && vs == V) {                                                           \
             static std::once_flag once;                                                                 \
             static hipError_t attr = hipSuccess;                                                        \
             std::call_once(once, [] {                                                                   \
-                attr = hipFuncSetAttribute(reinterpret_cast<const void *>(qg::qgemm_fp4_small_kernel<S, K>), \
+                attr = hipFuncSetAttribute(reinterpret_cast<const void *>(qg::qgemm_fp4_small_kernel<S, K, V>), \
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);      \
             });                                                                                         \
             if (attr != hipSuccess) return QG_ERR_LAUNCH;                                               \
-            hipLaunchKernelGGL((qg::qgemm_fp4_small_kernel<S, K>), sgrid, sblock, size_t(small_lds), stream, p); \
+            hipLaunchKernelGGL((qg::qgemm_fp4_small_kernel<S, K, V>), sgrid, sblock, size_t(small_lds), stream, p); \
             return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                             \
         }
-        QG_GEMM_SMALL(1, 1) QG_GEMM_SMALL(1, 2) QG_GEMM_SMALL(1, 4)
-        QG_GEMM_SMALL(2, 1) QG_GEMM_SMALL(2, 2) QG_GEMM_SMALL(2, 4)
-        QG_GEMM_SMALL(4, 1) QG_GEMM_SMALL(4, 2) QG_GEMM_SMALL(4, 4)
+#define QG_GEMM_SMALL_V(S, K) QG_GEMM_SMALL(S, K, true) QG_GEMM_SMALL(S, K, false)
+        QG_GEMM_SMALL_V(1, 1) QG_GEMM_SMALL_V(1, 2) QG_GEMM_SMALL_V(1, 4)
+        QG_GEMM_SMALL_V(2, 1) QG_GEMM_SMALL_V(2, 2) QG_GEMM_SMALL_V(2, 4)
+        QG_GEMM_SMALL_V(4, 1) QG_GEMM_SMALL_V(4, 2) QG_GEMM_SMALL_V(4, 4)
+#undef QG_GEMM_SMALL_V
 #undef QG_GEMM_SMALL
         return QG_ERR_LAUNCH;     // not reached
     }

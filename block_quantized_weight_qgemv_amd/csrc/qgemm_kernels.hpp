@@ -277,7 +277,31 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
 constexpr int kGemmSmallWaves = 8;                 // most waves per workgroup
 constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane
 
-template <int SPG, int KS>
+// Exchange of a 4 x 4 block of dwords among lanes l, l + 16, l + 32, l + 48
+// (index g = l >> 4): lane g's d[r] becomes lane r's d[g] before.  Two
+// permlane32 swaps (lanes g and g + 2) then two permlane16 swaps (g and
+// g + 1); swap32(a, b) trades a's upper 32 lanes for b's lower 32 lanes, and
+// swap16(a, b) a's odd 16-lane rows for b's even rows.  All lanes active.
+__device__ __forceinline__ void transpose4_lanes(uint4 &d) {
+    auto sw32 = [](uint32_t &a, uint32_t &b) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    auto sw16 = [](uint32_t &a, uint32_t &b) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    sw32(d.x, d.z);
+    sw32(d.y, d.w);
+    sw16(d.x, d.y);
+    sw16(d.z, d.w);
+}
+
+// VS: a chunk's gpc group scales of a row are read as one vector (they are
+// aligned to 2 * gpc bytes when the groups per row are a multiple of gpc).
+template <int SPG, int KS, bool VS>
 __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(const GemmParams p) {
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
     constexpr int PD = kGemmSmallDepth;
@@ -328,25 +352,48 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
     const uint16_t *xrow = xs + min(li, p.m - 1) * xstride + 8 * g;
 
     struct Buf {
-        uint32_t w[8];                             // one dword of codes per MFMA step
+        uint4 w[2];                                // 16-byte pieces 4j + g of the chunk row
         uint32_t sc[gpc];                          // the lane's row's group scales (bf16 bits)
     };
+    typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
+    typedef unsigned short u16x4_t __attribute__((ext_vector_type(4)));
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
     auto issue = [&](Buf &bf, int item_in) __attribute__((always_inline)) {
         const int item = __builtin_amdgcn_readfirstlane(min(item_in, max(items - 1, 0)));
         const int tq = __builtin_amdgcn_readfirstlane(item / nch);
         const int c = item - tq * nch;
-        // rows past n read row n - 1; steps past k read the row's last 16
-        // bytes (their activations are zeros)
+        // rows past n read row n - 1; pieces past k read the row's last 16
+        // bytes (their activations are zeros).  Each lane reads whole 16-byte
+        // pieces (piece 4j + g of its row's chunk); the MFMA's layout (dword
+        // g of every piece) comes from a 4 x 4 exchange among the four lanes
+        // of the row at consumption.
         const int64_t row = min((tb + tq) * 16 + li, p.n - 1);
         const unsigned char *wrow = p.codes + row * row_bytes;
         const int64_t kb = int64_t(c) * (kGemmKC / 2);
-        // (cached loads: a chunk's 8 loads take 4-byte pieces of the same
-        // 128-byte line of each row, which the vector cache merges)
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            bf.w[s] = *reinterpret_cast<const uint32_t *>(wrow + min(kb + 16 * s, row_bytes - 16) + 4 * g);
+        for (int j = 0; j < 2; ++j)
+            bf.w[j] = *reinterpret_cast<const uint4 *>(wrow + min(kb + 16 * (4 * j + g), row_bytes - 16));
+        const uint16_t *srow = p.scales + row * p.groups;
+        if constexpr (VS) {
+            // the chunk's groups, or the row's last gpc groups past the end
+            const int g0 = min(c * gpc, p.groups - gpc);
+            if constexpr (gpc == 8) {
+                const u16x8_t v = *reinterpret_cast<const u16x8_t *>(srow + g0);
 #pragma unroll
-        for (int j = 0; j < gpc; ++j) bf.sc[j] = p.scales[row * p.groups + min(c * gpc + j, p.groups - 1)];
+                for (int j = 0; j < 8; ++j) bf.sc[j] = v[j];
+            } else if constexpr (gpc == 4) {
+                const u16x4_t v = *reinterpret_cast<const u16x4_t *>(srow + g0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bf.sc[j] = v[j];
+            } else {
+                const u16x2_t v = *reinterpret_cast<const u16x2_t *>(srow + g0);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) bf.sc[j] = v[j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < gpc; ++j) bf.sc[j] = srow[min(c * gpc + j, p.groups - 1)];
+        }
     };
 
     f32x4_t acc[KS];
@@ -355,9 +402,18 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
 #pragma unroll
         for (int v = 0; v < 4; ++v) acc[q][v] = 0.0f;
 
-    auto consume = [&](const Buf &bf, int item) __attribute__((always_inline)) {
+    auto consume = [&](const Buf &bf_in, int item) __attribute__((always_inline)) {
         const int tq = __builtin_amdgcn_readfirstlane(item / nch);
         const int c = item - tq * nch;
+        Buf bf = bf_in;
+        // dword g of each MFMA step's 16-byte piece: w[s] below
+        transpose4_lanes(bf.w[0]);
+        transpose4_lanes(bf.w[1]);
+        const uint32_t wst[8] = {bf.w[0].x, bf.w[0].y, bf.w[0].z, bf.w[0].w,
+                                 bf.w[1].x, bf.w[1].y, bf.w[1].z, bf.w[1].w};
+        // past the end of a partial chunk the vector scales belong to the
+        // row's last groups: those groups multiply zeros, as do the general
+        // kernel's (whose scale there is the last group's)
         // every group's chain first, then the folds in group order
         f32x4_t dd[gpc];
 #pragma unroll
@@ -367,7 +423,7 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
             for (int t = 0; t < SPG; ++t) {
                 const int s = j * SPG + t;
                 const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xrow + c * kGemmKC + 32 * s);
-                const uint32_t q = bf.w[s];
+                const uint32_t q = wst[s];
                 const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
                 const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
                 const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
