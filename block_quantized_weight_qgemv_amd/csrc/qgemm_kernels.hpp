@@ -51,6 +51,28 @@ constexpr int kGemmXPad = 8;       // LDS row padding (bf16) against bank confli
 // ring would not fit the 128 registers a 1024-thread workgroup leaves)
 constexpr int gemm_depth(int tb, int ks) { return ks == 4 ? 2 : (tb == 1 ? 4 : (tb == 2 ? 3 : 2)); }
 
+// Exchange of a 4 x 4 block of dwords among lanes l, l + 16, l + 32, l + 48
+// (index g = l >> 4): lane g's d[r] becomes lane r's d[g] before.  Two
+// permlane32 swaps (lanes g and g + 2) then two permlane16 swaps (g and
+// g + 1); swap32(a, b) trades a's upper 32 lanes for b's lower 32 lanes, and
+// swap16(a, b) a's odd 16-lane rows for b's even rows.  All lanes active.
+__device__ __forceinline__ void transpose4_lanes(uint4 &d) {
+    auto sw32 = [](uint32_t &a, uint32_t &b) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    auto sw16 = [](uint32_t &a, uint32_t &b) {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    };
+    sw32(d.x, d.z);
+    sw32(d.y, d.w);
+    sw16(d.x, d.y);
+    sw16(d.z, d.w);
+}
+
 // SPG = MFMA steps per scale group (group size / 32): each group's steps form
 // one straight-line chain of MFMAs from a zero accumulator, read once.
 // TB = blocks of 16 activation rows per workgroup.
@@ -94,18 +116,19 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
     // thread's activation units and scales.  Every refill issues the same loads
     // (a chunk past the end reloads the last one, never used), so the
     // compiler's wait before a set is stored counts exactly the later sets.
-    uint32_t wn[PD][8];
+    uint4 wn[PD][2];                               // 16-byte pieces 4j + g of the chunk row
     uint4 xr[PD][kXUnits];
     uint16_t sr[PD][2];
     auto load_chunk = [&](int d, int c_in) __attribute__((always_inline)) {
         const int c = min(c_in, nch - 1);
         const int64_t kb = int64_t(c) * (kGemmKC / 2);        // byte offset of the chunk in a row
+        // whole 16-byte pieces (4j + g) per lane; the MFMA layout (dword g of
+        // every piece) comes from a 4 x 4 exchange among the row's four lanes
+        // at consumption.  A piece past k reads the row's last 16 bytes
+        // instead (never used).
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            // a step past k reads the row's last 16 bytes instead (never used)
-            const int64_t off = min(kb + 16 * s, row_bytes - 16) + 4 * g;
-            wn[d][s] = *reinterpret_cast<const uint32_t *>(wrow + off);
-        }
+        for (int j = 0; j < 2; ++j)
+            wn[d][j] = *reinterpret_cast<const uint4 *>(wrow + min(kb + 16 * (4 * j + g), row_bytes - 16));
 #pragma unroll
         for (int j = 0; j < kXUnits; ++j) {
             const int u = tid + 256 * j;                      // unit of 8 activations
@@ -158,10 +181,11 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
                 ss[e >> 6][e & 63] = sr[d][j];
             }
             __syncthreads();
-            uint32_t wc[8];
-#pragma unroll
-            for (int s = 0; s < 8; ++s) wc[s] = wn[d][s];
+            uint4 wp[2] = {wn[d][0], wn[d][1]};
             load_chunk(d, c + PD * KS);
+            transpose4_lanes(wp[0]);
+            transpose4_lanes(wp[1]);
+            const uint32_t wc[8] = {wp[0].x, wp[0].y, wp[0].z, wp[0].w, wp[1].x, wp[1].y, wp[1].z, wp[1].w};
             if (active) {
                 // The chunk's MFMA chains (one per scale group and block of 16
                 // activation rows) go out back to back, BS steps at a time,
@@ -276,28 +300,6 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
 // are the same whichever kernel, m or launch computes it.
 constexpr int kGemmSmallWaves = 8;                 // most waves per workgroup
 constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane
-
-// Exchange of a 4 x 4 block of dwords among lanes l, l + 16, l + 32, l + 48
-// (index g = l >> 4): lane g's d[r] becomes lane r's d[g] before.  Two
-// permlane32 swaps (lanes g and g + 2) then two permlane16 swaps (g and
-// g + 1); swap32(a, b) trades a's upper 32 lanes for b's lower 32 lanes, and
-// swap16(a, b) a's odd 16-lane rows for b's even rows.  All lanes active.
-__device__ __forceinline__ void transpose4_lanes(uint4 &d) {
-    auto sw32 = [](uint32_t &a, uint32_t &b) {
-        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
-        a = r[0];
-        b = r[1];
-    };
-    auto sw16 = [](uint32_t &a, uint32_t &b) {
-        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
-        a = r[0];
-        b = r[1];
-    };
-    sw32(d.x, d.z);
-    sw32(d.y, d.w);
-    sw16(d.x, d.y);
-    sw16(d.z, d.w);
-}
 
 // VS: a chunk's gpc group scales of a row are read as one vector (they are
 // aligned to 2 * gpc bytes when the groups per row are a multiple of gpc).
