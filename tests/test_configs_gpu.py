@@ -105,3 +105,37 @@ def test_affine_shapes(bits, name):
 @pytest.mark.parametrize("batch", [1, 4])
 def test_fp8_lm_head(batch):
     _full_size("fp8", "lm_head", batch=batch)
+
+
+@pytest.mark.parametrize("name,m", [("gate_up", 16), ("fc_down", 64)])
+def test_fp4_gemm_gemma_shapes(name, m):
+    """The small-batch GEMM at a benchmarked shape: gate_up at 16 activation
+    rows (x staged once per workgroup) and fc_down at 64 (x staged chunk by
+    chunk, K slices).  Sampled rows against the oracle; a second launch and
+    a single activation row reproduce the bits."""
+    sid, n, k = synth.shape(name)
+    gs = 32
+    log("full-size GEMM fp4 %s [%d x %d] m=%d: generating" % (name, n, k, m))
+    w = synth.weights(sid, n, k)
+    codes, scales = q.qg_quantize_fp4_e2m1(w, gs)
+    del w
+    x = synth.activations(sid + 7, m, k)
+    dc, ds, xd = dev(codes), dev(scales), dev(x)
+    log("full-size GEMM fp4 %s m=%d: launching" % (name, m))
+    y = out_tensor(m, n)
+    q.qgemm_fp4_e2m1(dc, ds, xd, y, gs)
+    y1 = host_y(y)
+    q.qgemm_fp4_e2m1(dc, ds, xd, y, gs)
+    assert np.array_equal(host_y(y), y1), "second launch differs"
+    y_one = out_tensor(1, n)
+    q.qgemm_fp4_e2m1(dc, ds, dev(x[m - 1:m]), y_one, gs)
+    assert np.array_equal(host_y(y_one)[0], y1[m - 1]), "single row differs"
+    del dc, ds
+    torch.cuda.empty_cache()
+    assert np.isfinite(y1).all()
+    rows = synth.sample_rows(n, SAMPLE, seed=sid)
+    ora = Q.quantize_fp4_e2m1(synth.weight_rows(sid, n, k, rows), gs)
+    assert np.array_equal(codes[rows], ora[0]) and np.array_equal(scales[rows], ora[1])
+    y_ref, a_ref = G.gemv_fp4_e2m1(ora[0], ora[1], x, gs)
+    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "GEMM %s m=%d" % (name, m))
+    log("full-size GEMM fp4 %s m=%d: %r" % (name, m, r))
