@@ -477,6 +477,54 @@ def run_probe(args):
             json.dump(rows, f, indent=1)
 
 
+def run_probe_sizes(args):
+    """The stream probe at each sweep workload's algorithmic byte count
+    (windows of that size rotating through 2 GiB, so the Infinity Cache cannot
+    serve them; best of a few launch shapes), beside the workload's own time
+    in the same session: how close each launch gets to a plain read of its
+    bytes, launch overhead and ramp included for both."""
+    import torch
+    import block_quantized_weight_qgemv_amd as q
+    total = 2 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda:0").fill_(7)
+    rows = []
+    for fmt, name, batch, gs in SWEEP:
+        if fmt == "fp4" and name == "tiny":
+            continue
+        wl = Workload(fmt, name, batch=batch, gs=gs)
+        steps = timed_steps(wl.launch, args.mode)
+        us = time_steps(wl.launch, steps, max(1, steps // 10), args.mode) / steps * 1e3
+        nbytes = wl.bytes
+        del wl
+        torch.cuda.empty_cache()
+        window = (nbytes + 15) // 16 * 16
+        nwin = max(1, total // window)
+        views = [buf[i * window:(i + 1) * window] for i in range(nwin)]
+        best = None
+        for pattern in (4, 5):
+            for unroll in (8, 16):
+                for waves_per_cu in (8, 16):
+                    tpb = 512
+                    blocks = 256 * waves_per_cu * 64 // tpb
+                    out = torch.empty(blocks * tpb, dtype=torch.int32, device="cuda:0")
+                    launch = lambda i: q.qg_stream_probe(views[i % nwin], pattern, unroll, blocks, tpb, out)
+                    ps = timed_steps(launch, args.mode)
+                    pus = time_steps(launch, ps, max(1, ps // 10), args.mode) / ps * 1e3
+                    if best is None or pus < best[0]:
+                        best = (pus, pattern, unroll, blocks)
+        row = {"fmt": fmt, "shape": name, "batch": batch, "bytes": nbytes, "us": round(us, 3),
+               "probe_us": round(best[0], 3), "probe_config": {"pattern": best[1], "unroll": best[2],
+                                                              "blocks": best[3], "threads": 512},
+               "us_over_probe": round(us / best[0], 3)}
+        rows.append(row)
+        log("%-4s %-10s B=%d %11d B  matvec %8.2f us  read stream %8.2f us  ratio %.3f  (%.1f%% / %.1f%% of 8 TB/s)"
+            % (fmt, name, batch, nbytes, us, best[0], us / best[0],
+               100 * nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 100 * nbytes / (best[0] * 1e-6) / 1e9 / HBM_PEAK_GBS))
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
 def _pmc_median(run_dir, counter, kernel_substr):
     import csv
     import glob
@@ -613,6 +661,8 @@ def main(argv=None):
     ap.add_argument("--out", default="")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--probe", action="store_true", help="stream-probe read bandwidth sweep")
+    ap.add_argument("--probe-sizes", action="store_true",
+                    help="stream probe at each sweep workload's byte count, beside the workload")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
                     help="fetch, write, copy-fetch and copy-write rocprofv3 --pmc output dirs")
     ap.add_argument("--summarize-trace", metavar="DIR", help="rocprofv3 --kernel-trace --stats output dir")
@@ -643,6 +693,8 @@ def main(argv=None):
         run_calibrate_copy(args)
     elif args.probe:
         run_probe(args)
+    elif args.probe_sizes:
+        run_probe_sizes(args)
     elif args.sweep:
         run_sweep(args)
     else:
