@@ -11,6 +11,22 @@ namespace {
 
 bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// compute units of the current device, read once per device
+constexpr int kMaxDevices = 64;
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(g_cu_once[dev], [dev] {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+        g_cu_count[dev] = v;
+    });
+    return g_cu_count[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -55,10 +71,8 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
     // workgroup, weight tiles streamed without barriers (the same bits)
     const int64_t small_lds = qg::gemm_small_lds(k, m);
     if (m <= 16 && small_lds <= 128 * 1024) {
-        int cus = 0, dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-            return QG_ERR_DEVICE;
+        const int cus = device_cus();
+        if (cus < 1) return QG_ERR_DEVICE;
         // one workgroup per CU (x fills most of its LDS), with as many waves
         // as the 16-row tiles need to cover the chip, 1..8
         const int64_t rtiles = (n + 15) / 16;
