@@ -521,3 +521,16 @@ def test_shared_tiles_bitwise_across_plans(fmt, n, k, gs, batch):
     parity.assert_parity(ys[0], y_ref, a_ref, "%s n=%d k=%d" % (fmt, n, k))
     for plan, y in zip(SHARING_PLANS[1:], ys[1:]):
         assert np.array_equal(y, ys[0]), plan
+
+
+def test_fp8_plan_query_by_batch():
+    """The plan the library reports for FP8: one-row tiles on the vector
+    kernel at batch 1 and 2, 4-row tiles on the matrix-core kernel at 3 and
+    4, one workgroup per compute unit for the lm_head, fewer for few rows."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for batch in (1, 2, 3, 4):
+        p = q.qg_plan_query(q.QG_FMT_FP8_E4M3, 262144, 3840, batch)
+        assert p["rows_per_tile"] == (1 if batch < 3 else 4), (batch, p)
+        assert p["waves_per_block"] == 8 and p["blocks"] == cus, (batch, p)
+    p = q.qg_plan_query(q.QG_FMT_FP8_E4M3, 40, 3840, 4)      # 10 tiles of 4 rows: 2 workgroups of 8 waves
+    assert p["rows_per_tile"] == 4 and p["blocks"] == 2, p
