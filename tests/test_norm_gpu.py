@@ -115,6 +115,7 @@ CASES = [
     ("u4", 900, 4096, 64, 1), ("u4", 250, 15360, 64, 3), ("u8", 800, 3840, 64, 2),
     ("u8", 120, 14336, 64, 1), ("fp8", 1500, 3840, None, 1), ("fp8", 600, 3840, None, 4),
     ("fp4", 90, 3872, 32, 2),          # the LDS kernel
+    ("fp8", 333, 5120, None, 3),       # the matrix-core kernel, rows of several steps
 ]
 
 

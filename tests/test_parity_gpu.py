@@ -382,10 +382,12 @@ def _guarded(a, fill_byte):
     return d, d[GUARD:GUARD + raw.size]
 
 
-@pytest.mark.parametrize("fmt,gs", [("fp4", 64), ("u4", 64), ("u8", 32), ("fp8", None)])
-def test_poisoned_neighbours_are_never_read_or_written(fmt, gs):
-    """NaN in every byte around the inputs; y pre-filled with NaN and fenced by canaries."""
-    n, k, batch = 123, 3904 if fmt != "fp8" else 3856, 2
+@pytest.mark.parametrize("fmt,gs,batch", [("fp4", 64, 2), ("u4", 64, 2), ("u8", 32, 2), ("fp8", None, 2),
+                                          ("fp8", None, 4)])
+def test_poisoned_neighbours_are_never_read_or_written(fmt, gs, batch):
+    """NaN in every byte around the inputs; y pre-filled with NaN and fenced by
+    canaries.  FP8 at batch 4 runs on the matrix-core kernel."""
+    n, k = 123, 3904 if fmt != "fp8" else 3856
     w = synth.weights(13, n, k)
     arrays = _quantize(fmt, w, gs)
     x = synth.activations(13, batch, k)
@@ -403,7 +405,7 @@ def test_poisoned_neighbours_are_never_read_or_written(fmt, gs):
     yfull = torch.full(((batch * n * 4) + 2 * GUARD,), 0xAB, dtype=torch.uint8, device="cuda:0")
     yv = yfull[GUARD:GUARD + batch * n * 4].view(torch.float32).view(batch, n)
     yv.fill_(float("nan"))
-    log("poison %s" % fmt)
+    log("poison %s batch=%d" % (fmt, batch))
     views = [v for _, v in dev_arrays]
     if fmt == "fp4":
         q.qgemv_fp4_e2m1(views[0], views[1], xv, yv, gs)
