@@ -80,8 +80,9 @@ def test_qgemm_rows_alone_repeat_and_bf16(n, k, gs, m):
     assert np.array_equal(y16, F.f64_to_bf16_bits(y.astype(np.float64)))
 
 
-def test_qgemm_writes_only_y():
-    n, k, gs, m = 90, 1024, 32, 21
+@pytest.mark.parametrize("m", [21, 13])           # the general kernel, the streaming one
+def test_qgemm_writes_only_y(m):
+    n, k, gs = 90, 1024, 32
     codes, scales, x = _inputs(n, k, gs, m, 4)
     log("qgemm canaries n=%d k=%d m=%d" % (n, k, m))
     pad = 4096
