@@ -76,31 +76,36 @@ __device__ __forceinline__ void transpose4_lanes(uint4 &d) {
 // SPG = MFMA steps per scale group (group size / 32): each group's steps form
 // one straight-line chain of MFMAs from a zero accumulator, read once.
 // TB = blocks of 16 activation rows per workgroup.
-// KS = K slices: the workgroup has 4 KS waves, slice s (waves 4s..4s+3) takes
-// chunks s, s + KS, s + 2 KS, ... of the same 64 rows, and the slices' sums
-// are added in slice order at the end.  KS depends on n and k only, so a
+// KS = K slices: the workgroup has WPS KS waves, slice s (waves WPS s ..
+// WPS s + WPS - 1) takes chunks s, s + KS, s + 2 KS, ... of the same 16 WPS
+// rows, and the slices' sums are added in slice order at the end.
+// WPS = waves per slice (4, or 1 where few row tiles would leave compute
+// units idle; the order of additions is the same).  KS depends on n and k only, so a
 // row's bits do not depend on the other activation rows.
-template <int SPG, int TB, int KS>
-__global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p) {
+template <int SPG, int TB, int KS, int WPS>
+__global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmParams p) {
     static_assert(KS * TB <= 4, "LDS holds KS chunks of 16 TB activation rows");
     constexpr int kTokens = 16 * TB;
-    constexpr int kXUnits = 2 * TB;                // 16-byte activation units per thread per chunk
+    constexpr int ST = 64 * WPS;                   // threads per K slice
+    constexpr int RW = 16 * WPS;                   // weight rows per workgroup
+    static_assert((512 * TB) % ST == 0, "whole activation units per thread");
+    constexpr int kXUnits = 512 * TB / ST;         // 16-byte activation units per thread per chunk
     constexpr int PD = gemm_depth(TB, KS);
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
     constexpr int BS = 8 / TB > SPG ? 8 / TB : SPG;   // MFMA steps per batch of independent chains
     constexpr int GB = BS / SPG;                   // scale groups per batch
     __shared__ __attribute__((aligned(16))) uint16_t xsa[KS][kTokens][kGemmKC + kGemmXPad];
-    __shared__ __attribute__((aligned(16))) uint16_t ssa[KS][kGemmKC / 32][kGemmRows];
+    __shared__ __attribute__((aligned(16))) uint16_t ssa[KS][kGemmKC / 32][RW];
 
-    const int ks = threadIdx.x >> 8;               // K slice
-    const int tid = threadIdx.x & 255;             // thread in the slice
+    const int ks = threadIdx.x / ST;               // K slice
+    const int tid = threadIdx.x % ST;              // thread in the slice
     const int lane = tid & (kWave - 1);
     const int w = tid >> 6;                        // wave in the slice: rows 16w..16w+15
     auto &xs = xsa[ks];
     auto &ss = ssa[ks];
     const int g = lane >> 4;                       // k quarter of an MFMA step / D row quarter
     const int li = lane & 15;                      // A row / B column inside a block
-    const int64_t rbase = int64_t(blockIdx.x) * kGemmRows;
+    const int64_t rbase = int64_t(blockIdx.x) * RW;
     const int t0 = blockIdx.y * kTokens;
     const int mt = min(kTokens, p.m - t0);         // activation rows of this workgroup
     const int nblk = (mt + 15) >> 4;               // blocks of 16 in use (uniform)
@@ -131,7 +136,7 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
             wn[d][j] = *reinterpret_cast<const uint4 *>(wrow + min(kb + 16 * (4 * j + g), row_bytes - 16));
 #pragma unroll
         for (int j = 0; j < kXUnits; ++j) {
-            const int u = tid + 256 * j;                      // unit of 8 activations
+            const int u = tid + ST * j;                       // unit of 8 activations
             const int tt = u >> 5, ku = u & 31;
             const int kk = min(c * kGemmKC + ku * 8, p.k - 8);   // past k: a unit never used
             const int tok = t0 + min(tt, mt - 1);
@@ -139,8 +144,8 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int e = tid + 256 * j;
-            const int grp = e >> 6, r = e & 63;
+            const int e = tid + ST * j;
+            const int grp = e / RW, r = e % RW;
             const int gg = min(c * gpc + min(grp, gpc - 1), p.groups - 1);
             const int64_t row = min(rbase + r, p.n - 1);
             sr[d][j] = p.scales[row * p.groups + gg];
@@ -169,7 +174,7 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
             // compiler its count of the loads in flight (it would drain them)
 #pragma unroll
             for (int j = 0; j < kXUnits; ++j) {
-                const int u = tid + 256 * j;
+                const int u = tid + ST * j;
                 const int kk = c * kGemmKC + (u & 31) * 8;
                 // units past k are stored as zeros (the MFMA of a partial last
                 // chunk stops at a whole group, but LDS stays defined)
@@ -177,8 +182,8 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const int e = tid + 256 * j;
-                ss[e >> 6][e & 63] = sr[d][j];
+                const int e = tid + ST * j;
+                ss[e / RW][e % RW] = sr[d][j];
             }
             __syncthreads();
             uint4 wp[2] = {wn[d][0], wn[d][1]};
@@ -247,10 +252,10 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
         // slices 1.. leave their sums in LDS (over the staged chunks, free
         // after the loop's last barrier); slice 0 adds them in slice order
         f32x4_t *red = reinterpret_cast<f32x4_t *>(&xsa[0][0][0]);
-        static_assert(sizeof(xsa) >= (KS - 1) * 4 * TB * 64 * sizeof(f32x4_t), "reduction space");
+        static_assert(sizeof(xsa) >= (KS - 1) * WPS * TB * 64 * sizeof(f32x4_t), "reduction space");
         if (ks > 0) {
 #pragma unroll
-            for (int b = 0; b < TB; ++b) red[(((ks - 1) * 4 + w) * TB + b) * 64 + lane] = acc[b];
+            for (int b = 0; b < TB; ++b) red[(((ks - 1) * WPS + w) * TB + b) * 64 + lane] = acc[b];
         }
         __syncthreads();
         if (ks > 0) return;
@@ -258,7 +263,7 @@ __global__ void __launch_bounds__(256 * KS) qgemm_fp4_kernel(const GemmParams p)
         for (int q = 1; q < KS; ++q)
 #pragma unroll
             for (int b = 0; b < TB; ++b) {
-                const f32x4_t o = red[(((q - 1) * 4 + w) * TB + b) * 64 + lane];
+                const f32x4_t o = red[(((q - 1) * WPS + w) * TB + b) * 64 + lane];
 #pragma unroll
                 for (int v = 0; v < 4; ++v) acc[b][v] += o[v];
             }

@@ -66,8 +66,11 @@ def test_qgemm_parity(n, k, gs, m):
     parity.assert_parity(y, y_ref, a_ref, "qgemm n=%d k=%d m=%d" % (n, k, m))
 
 
+# the last two take one wave per K slice (16-row workgroups: few row tiles,
+# x too large for the streaming kernel at m rows) with 2 and 1 K slices; their
+# single rows run on the streaming kernel
 @pytest.mark.parametrize("n,k,gs,m", [(150, 3840, 32, 37), (70, 4224, 128, 70), (9000, 1024, 64, 35),
-                                      (33000, 512, 32, 70)])
+                                      (33000, 512, 32, 70), (4200, 8192, 32, 16), (10300, 8448, 32, 8)])
 def test_qgemm_rows_alone_repeat_and_bf16(n, k, gs, m):
     codes, scales, x = _inputs(n, k, gs, m, 9)
     log("qgemm rows alone n=%d k=%d m=%d" % (n, k, m))
