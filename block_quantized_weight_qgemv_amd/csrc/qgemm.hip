@@ -119,7 +119,17 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
     const dim3 block(unsigned(64 * wps * ks));
 #define QG_GEMM_CASE(S, T, K, W)                                                                \
     if (spg == S && tbu == T && ks == K && wps == W) {                                          \
-        hipLaunchKernelGGL((qg::qgemm_fp4_kernel<S, T, K, W>), grid, block, 0, stream, p);     \
+        constexpr int64_t lds = qg::gemm_general_lds(T, K, W);                                  \
+        if (lds > 64 * 1024) {                                                                  \
+            static std::once_flag once;                                                         \
+            static hipError_t attr = hipSuccess;                                                \
+            std::call_once(once, [] {                                                           \
+                attr = hipFuncSetAttribute(reinterpret_cast<const void *>(qg::qgemm_fp4_kernel<S, T, K, W>), \
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)); \
+            });                                                                                 \
+            if (attr != hipSuccess) return QG_ERR_LAUNCH;                                       \
+        }                                                                                       \
+        hipLaunchKernelGGL((qg::qgemm_fp4_kernel<S, T, K, W>), grid, block, size_t(lds), stream, p); \
         return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                         \
     }
 #define QG_GEMM_SPG(S) QG_GEMM_CASE(S, 1, 1, 4) QG_GEMM_CASE(S, 2, 1, 4) QG_GEMM_CASE(S, 4, 1, 4) \

@@ -73,6 +73,11 @@ __device__ __forceinline__ void transpose4_lanes(uint4 &d) {
     sw16(d.z, d.w);
 }
 
+// Whether qgemm_fp4_kernel double-buffers its staged chunks: for 16 or 32
+// activation rows; with 64 the second buffer would halve the workgroups a CU
+// holds (measured slower).
+__host__ __device__ constexpr bool gemm_double_buffer(int tb) { return tb < 4; }
+
 // SPG = MFMA steps per scale group (group size / 32): each group's steps form
 // one straight-line chain of MFMAs from a zero accumulator, read once.
 // TB = blocks of 16 activation rows per workgroup.
@@ -94,15 +99,23 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
     constexpr int BS = 8 / TB > SPG ? 8 / TB : SPG;   // MFMA steps per batch of independent chains
     constexpr int GB = BS / SPG;                   // scale groups per batch
-    __shared__ __attribute__((aligned(16))) uint16_t xsa[KS][kTokens][kGemmKC + kGemmXPad];
-    __shared__ __attribute__((aligned(16))) uint16_t ssa[KS][kGemmKC / 32][RW];
+    // LDS (dynamic, gemm_general_lds bytes): per K slice, buffers of a
+    // chunk's activations and scales.  With two (DB), chunk i + 1 is staged
+    // into one while chunk i is multiplied from the other, one barrier per
+    // chunk; with 64 activation rows the second buffer would halve the
+    // workgroups a CU holds, so those stage into one buffer between two
+    // barriers.
+    constexpr bool DB = gemm_double_buffer(TB);
+    typedef uint16_t XBuf[kTokens][kGemmKC + kGemmXPad];
+    typedef uint16_t SBuf[kGemmKC / 32][RW];
+    extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
+    XBuf *xsa = reinterpret_cast<XBuf *>(gsmem);                      // [2][KS]
+    SBuf *ssa = reinterpret_cast<SBuf *>(gsmem + (DB ? 2 : 1) * KS * sizeof(XBuf));   // [DB ? 2 : 1][KS]
 
     const int ks = threadIdx.x / ST;               // K slice
     const int tid = threadIdx.x % ST;              // thread in the slice
     const int lane = tid & (kWave - 1);
     const int w = tid >> 6;                        // wave in the slice: rows 16w..16w+15
-    auto &xs = xsa[ks];
-    auto &ss = ssa[ks];
     const int g = lane >> 4;                       // k quarter of an MFMA step / D row quarter
     const int li = lane & 15;                      // A row / B column inside a block
     const int64_t rbase = int64_t(blockIdx.x) * RW;
@@ -165,27 +178,47 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
         load_chunk(d, d * KS + ks);
         __builtin_amdgcn_sched_barrier(0);
     }
+    // stage ring set d (chunk c of this slice) into buffer par; stored
+    // whether the chunk exists or not (a branch here would cost the compiler
+    // its count of the loads in flight: it would drain them)
+    auto stage = [&](int d, int c, int par) __attribute__((always_inline)) {
+        XBuf &xw = xsa[par * KS + ks];
+        SBuf &sw = ssa[par * KS + ks];
+#pragma unroll
+        for (int j = 0; j < kXUnits; ++j) {
+            const int u = tid + ST * j;
+            const int kk = c * kGemmKC + (u & 31) * 8;
+            // units past k are stored as zeros (the MFMA of a partial last
+            // chunk stops at a whole group, but LDS stays defined)
+            *reinterpret_cast<uint4 *>(&xw[u >> 5][(u & 31) * 8]) = kk < p.k ? xr[d][j] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + ST * j;
+            sw[e / RW][e % RW] = sr[d][j];
+        }
+    };
+    if constexpr (DB) {
+        stage(0, ks, 0);
+        __syncthreads();
+    }
     for (int c0 = 0; c0 < nit; c0 += PD) {
 #pragma unroll
         for (int d = 0; d < PD; ++d) {
-            const int c = (c0 + d) * KS + ks;                 // this slice's chunk
-            const bool active = c < nch;                       // uniform in the wave
-            // stored whether active or not: a branch here would cost the
-            // compiler its count of the loads in flight (it would drain them)
-#pragma unroll
-            for (int j = 0; j < kXUnits; ++j) {
-                const int u = tid + ST * j;
-                const int kk = c * kGemmKC + (u & 31) * 8;
-                // units past k are stored as zeros (the MFMA of a partial last
-                // chunk stops at a whole group, but LDS stays defined)
-                *reinterpret_cast<uint4 *>(&xs[u >> 5][(u & 31) * 8]) = kk < p.k ? xr[d][j] : make_uint4(0, 0, 0, 0);
+            const int i = c0 + d;                             // chunk of this slice, in order
+            const int c = i * KS + ks;                        // chunk of the row
+            const bool active = c < nch;                      // uniform in the wave
+            const int par = DB ? (i & 1) : 0;
+            if constexpr (DB) {
+                // the next chunk (ring set d + 1) into the other buffer: every
+                // wave finished reading it before the last barrier
+                stage((d + 1) % PD, (i + 1) * KS + ks, par ^ 1);
+            } else {
+                stage(d, c, 0);
+                __syncthreads();
             }
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int e = tid + ST * j;
-                ss[e / RW][e % RW] = sr[d][j];
-            }
-            __syncthreads();
+            const XBuf &xs = xsa[par * KS + ks];
+            const SBuf &ss = ssa[par * KS + ks];
             uint4 wp[2] = {wn[d][0], wn[d][1]};
             load_chunk(d, c + PD * KS);
             transpose4_lanes(wp[0]);
@@ -251,8 +284,8 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     if constexpr (KS > 1) {
         // slices 1.. leave their sums in LDS (over the staged chunks, free
         // after the loop's last barrier); slice 0 adds them in slice order
-        f32x4_t *red = reinterpret_cast<f32x4_t *>(&xsa[0][0][0]);
-        static_assert(sizeof(xsa) >= (KS - 1) * WPS * TB * 64 * sizeof(f32x4_t), "reduction space");
+        f32x4_t *red = reinterpret_cast<f32x4_t *>(gsmem);
+        static_assert((DB ? 2 : 1) * KS * sizeof(XBuf) >= (KS - 1) * WPS * TB * 64 * sizeof(f32x4_t), "reduction space");
         if (ks > 0) {
 #pragma unroll
             for (int b = 0; b < TB; ++b) red[(((ks - 1) * WPS + w) * TB + b) * 64 + lane] = acc[b];
@@ -285,6 +318,13 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
             }
         }
     }
+}
+
+// LDS bytes of qgemm_fp4_kernel<SPG, TB, KS, WPS>: one or two buffers per K
+// slice of a chunk's activations and scales
+__host__ __device__ constexpr int64_t gemm_general_lds(int tb, int ks, int wps) {
+    return (gemm_double_buffer(tb) ? 2 : 1) * int64_t(ks) *
+           (16 * tb * (kGemmKC + kGemmXPad) * 2 + (kGemmKC / 32) * 16 * wps * 2);
 }
 
 // ------------------------------------------------------------------ m <= 16
