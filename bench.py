@@ -79,8 +79,8 @@ def algorithmic_bytes(fmt, n, k, batch, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         w = q.qg_bytes_fp4(n, k, gs)
-    elif fmt in ("u4", "u8"):
-        w = q.qg_bytes_affine(n, k, 4 if fmt == "u4" else 8, gs)
+    elif fmt in ("u4", "u8", "u4q8", "u4q8mv"):
+        w = q.qg_bytes_affine(n, k, 8 if fmt == "u8" else 4, gs)
     else:
         w = q.qg_bytes_fp8(n, k)
     return w + batch * k * 2 + batch * n * 4
@@ -90,8 +90,8 @@ def quantize(fmt, w, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         return q.qg_quantize_fp4_e2m1(w, gs)
-    if fmt in ("u4", "u8"):
-        return q.qg_quantize_affine(w, 4 if fmt == "u4" else 8, gs)
+    if fmt in ("u4", "u8", "u4q8", "u4q8mv"):
+        return q.qg_quantize_affine(w, 8 if fmt == "u8" else 4, gs)
     return q.qg_quantize_fp8_e4m3_rowwise(w)
 
 
@@ -129,6 +129,10 @@ class Workload:
             self.host = None
         self.x = to_dev(self.x_host)
         self.y = torch.empty((batch, n), dtype=torch.float32, device="cuda:0")
+        if fmt in ("u4q8", "u4q8mv"):
+            # int8 activation blocks: requantized every step ("u4q8", the whole
+            # route) or once here ("u4q8mv", the matvec kernel alone)
+            self.xq, self.ds = q.qg_quantize_q8_1(self.x)
 
     def launch(self, i):
         d = self.dev[i % self.copies]
@@ -139,6 +143,10 @@ class Workload:
             q.qgemv_affine_u4(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
         elif self.fmt == "u8":
             q.qgemv_affine_u8(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
+        elif self.fmt in ("u4q8", "u4q8mv"):
+            if self.fmt == "u4q8":
+                q.qg_quantize_q8_1(self.x, self.xq, self.ds)
+            q.qgemv_affine_u4_q8(d[0], d[1], d[2], self.xq, self.ds, self.y, self.gs)
         else:
             q.qgemv_fp8_e4m3(d[0], d[1], self.x, self.y, plan=self.plan)
 
@@ -282,6 +290,11 @@ SWEEP = [
     ("u4", "mlp_up", 1, 64), ("u4", "mlp_down", 1, 64), ("u4", "llama_up", 1, 64), ("u4", "llama_down", 1, 64),
     ("u8", "mlp_up", 1, 64), ("u8", "mlp_down", 1, 64), ("u8", "llama_up", 1, 64), ("u8", "llama_down", 1, 64),
     ("fp8", "lm_head", 1, None), ("fp8", "lm_head", 4, None), ("fp4", "tiny", 1, 32),
+    # the int8 activation route for u4 (quantize + matvec, and the matvec
+    # alone) beside the bf16 route, at batch 1 and 4
+    ("u4q8", "mlp_up", 1, 64), ("u4q8mv", "mlp_up", 1, 64), ("u4q8", "mlp_down", 1, 64),
+    ("u4q8mv", "mlp_down", 1, 64), ("u4q8", "llama_up", 1, 64), ("u4q8", "llama_down", 1, 64),
+    ("u4", "mlp_up", 4, 64), ("u4q8", "mlp_up", 4, 64), ("u4", "mlp_down", 4, 64), ("u4q8", "mlp_down", 4, 64),
 ]
 
 

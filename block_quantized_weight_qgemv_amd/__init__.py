@@ -26,6 +26,7 @@ qg_plan = _b.qg_plan
 
 __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
+    "qg_quantize_q8_1", "qgemv_affine_u4_q8",
     "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
@@ -218,6 +219,52 @@ def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream, g
 def qgemv_affine_u4(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):
     """y[b, n] = sum_k (scale[n,g] * q[n,k] + bias[n,g]) * x[b,k], 4-bit u32 low-first codes [n, k/8]."""
     return _affine("qgemv_affine_u4", 4, codes, scales, biases, x, y, group_size, plan, stream)
+
+
+def qg_quantize_q8_1(x, xq=None, ds=None, stream=None):
+    """bf16 x [batch, k] -> (xq int8 [batch, k], ds float32 [batch, k/32, 2] = {d, s}) on x's device."""
+    torch = _torch()
+    xp = _dev_ptr(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (1, 2))
+    batch = 1 if x.dim() == 1 else x.shape[0]
+    k = x.shape[-1]
+    if xq is None:
+        xq = torch.empty((batch, k), dtype=torch.int8, device=x.device)
+    if ds is None:
+        ds = torch.empty((batch, k // 32, 2), dtype=torch.float32, device=x.device)
+    qp = _dev_ptr(xq, "xq", (torch.int8,), (1, 2))
+    dp = _dev_ptr(ds, "ds", (torch.float32,), (2, 3))
+    if xq.numel() != batch * k or ds.numel() != batch * (k // 32) * 2:
+        raise ValueError("xq must hold [batch=%d, k=%d], ds [batch, k/32, 2]" % (batch, k))
+    _same_device(x, xq, ds)
+    _check(_lib.qg_quantize_q8_1(xp, k, batch, qp, dp, _stream(stream, x.device)), "qg_quantize_q8_1")
+    return xq, ds
+
+
+def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=None):
+    """Affine u4 weights against int8 activation blocks from qg_quantize_q8_1:
+    y[b, n] = sum_blk scale * d * sum(u * q) + bias * s."""
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    qp = _dev_ptr(xq, "xq", (torch.int8,), (1, 2))
+    dp = _dev_ptr(ds, "ds", (torch.float32,), (2, 3))
+    yp = _dev_ptr(y, "y", (torch.float32, torch.bfloat16), (1, 2))
+    n = codes.shape[0]
+    batch = 1 if xq.dim() == 1 else xq.shape[0]
+    k = xq.shape[-1]
+    if codes.shape[1] * 8 != k or tuple(scales.shape) != (n, k // group_size) \
+            or tuple(biases.shape) != tuple(scales.shape) or ds.numel() != batch * (k // 32) * 2:
+        raise ValueError("shapes: codes %s, scales %s, biases %s, xq %s, ds %s, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), tuple(xq.shape),
+                            tuple(ds.shape), group_size))
+    if y.numel() != batch * n or (y.dim() == 2 and tuple(y.shape) != (batch, n)):
+        raise ValueError("y must be [batch=%d, n=%d], got %s" % (batch, n, tuple(y.shape)))
+    out = _b.QG_OUT_F32 if y.dtype == torch.float32 else _b.QG_OUT_BF16
+    _same_device(codes, scales, biases, xq, ds, y)
+    _check(_lib.qgemv_affine_u4_q8(cp, sp, bp, qp, dp, yp, n, k, int(group_size), batch, out,
+                                   _stream(stream, y.device)), "qgemv_affine_u4_q8")
+    return y
 
 
 def qgemv_affine_u8(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):

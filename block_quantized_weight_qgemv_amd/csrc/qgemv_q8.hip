@@ -1,0 +1,312 @@
+// The int8 activation route for affine 4-bit weights: the activation is
+// quantized in blocks of 32 to int8 codes with an fp32 pair {d, s}
+// (s = d * sum q), the weight nibbles are widened to int8 bytes and meet the
+// activation codes in 4-wide integer dots, and the affine bias is applied once
+// per block through s.
+//
+// Prior art, not the blueprint: "perf(cuda): generalize Gemma 4 batched
+// prefill + flash attn + decode graphs to dense Q4_K models", section
+// "Item C2" (int8 blocks carrying {d, s}, nibbles widened to int8, the min
+// term applied through the activation sum).  There it feeds int8 matrix
+// products and a 4-wide integer-dot matvec; here it is the matvec, on
+// gfx950's v_dot4_i32_i8.
+//
+// One 16-byte chunk of u4 codes is 32 weights, exactly one activation block,
+// so every chunk's fold is  acc += scale * (d * idot) + bias * s.
+
+#include "qgemv.h"
+#include "qgemv_kernels.hpp"
+
+#include <mutex>
+
+namespace qg {
+
+constexpr int kQ8Block = 32;
+
+// ------------------------------------------------------------------ quantize
+
+// One thread per block of 32 activations: amax, d = amax / 127, the codes
+// rne(x * (127 / amax)) and s = d * sum(q), all decided in fp32 with
+// correctly rounded operations (an all-zero block gives d = s = 0 and zero
+// codes).  Codes are written in natural column order.
+__global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t blocks,
+                                                             int8_t *__restrict__ xq, float *__restrict__ ds) {
+    const int64_t blk = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (blk >= blocks) return;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * kQ8Block);
+    float v[kQ8Block];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint4 w = src[u];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * u + 2 * i] = bf16_to_f32(ws[i] & 0xFFFFu);
+            v[8 * u + 2 * i + 1] = bf16_to_f32(ws[i] >> 16);
+        }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kQ8Block; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const float d = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 0.0f;
+    const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
+    int sum = 0;
+    uint32_t packed[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float r = fminf(fmaxf(__builtin_rintf(__fmul_rn(v[4 * w + j], inv)), -127.0f), 127.0f);
+            const int qi = int(r);
+            sum += qi;
+            word |= (uint32_t(qi) & 0xFFu) << (8 * j);
+        }
+        packed[w] = word;
+    }
+    uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * kQ8Block);
+    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+    reinterpret_cast<float2 *>(ds)[blk] = make_float2(d, __fmul_rn(d, float(sum)));
+}
+
+// ------------------------------------------------------------------ matvec
+
+struct Q8Args {
+    const int8_t *xq;       // int8 [B, k], natural order
+    const float *ds;        // {d, s} [B, k/32]
+};
+
+// Bytes 0..3 and 4..7 of an 8-column group (x0..x7) regrouped as the even
+// columns (x0, x2, x4, x6) and the odd ones (x1, x3, x5, x7): the order in
+// which the masked low and high nibbles of a code word hold their columns.
+__device__ __forceinline__ uint2 even_odd(uint32_t lo4, uint32_t hi4) {
+    return make_uint2(__builtin_amdgcn_perm(hi4, lo4, 0x06040200u), __builtin_amdgcn_perm(hi4, lo4, 0x07050301u));
+}
+
+// Integer dot of one chunk of u4 codes (word i: columns 8i..8i+7, code j at
+// bits 4j) with the chunk's activation codes, as two regrouped 16-byte pieces
+// (piece p: .x/.y even/odd of columns 16p..16p+7, .z/.w of 16p+8..16p+15).
+__device__ __forceinline__ int dot_u4_i8(const uint4 q, const uint4 (&xp)[2]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 p = xp[i >> 1];
+        const uint32_t ev = (i & 1) ? p.z : p.x;
+        const uint32_t od = (i & 1) ? p.w : p.y;
+        acc = __builtin_amdgcn_sdot4(int(w[i] & 0x0F0F0F0Fu), int(ev), acc, false);
+        acc = __builtin_amdgcn_sdot4(int((w[i] >> 4) & 0x0F0F0F0Fu), int(od), acc, false);
+    }
+    return acc;
+}
+
+__host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks) {
+    return batch * chunks * (2 * 16 + 8);
+}
+
+// Waves take contiguous row ranges (wave_rows); a step is one pass of 64
+// chunks over an R-row tile, D steps in flight.  The workgroup first stages
+// every batch row's codes (regrouped) and {d, s} pairs in LDS, piece-major so
+// that consecutive lanes read consecutive 16 bytes.
+template <int R, int B, int D>
+__global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const Q8Args a) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    struct Buf {
+        uint4 c[R];
+        uint32_t s[R], b[R];
+    };
+    const int lane = threadIdx.x & (kWave - 1);
+    const int chunks = p.chunks;
+    uint4 *xl = reinterpret_cast<uint4 *>(smem);                                   // [B][2][chunks]
+    float2 *dl = reinterpret_cast<float2 *>(smem + int64_t(B) * chunks * 32);     // [B][chunks]
+
+    int64_t r_begin, r_end;
+    wave_rows(p, r_begin, r_end);
+    const int tiles = int((r_end - r_begin + R - 1) / R);
+    const int passes = p.passes;
+    const int steps = tiles * passes;
+    const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
+    const int last_chunk = chunks - 1;
+
+    auto issue = [&](Buf &bf, int s) {
+        const int t = s / passes;
+        const int j = s - t * passes;
+        const int c = min(lane + kWave * j, last_chunk);
+        const int64_t row0 = r_begin + int64_t(t) * R;
+        const int g = c >> p.group_shift;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t row = min(row0 + i, row_hi);
+            bf.c[i] = load_code_chunk(p.codes + row * p.row_bytes + uint32_t(c) * kChunkBytes);
+            bf.s[i] = load_param(p.scales + row * p.groups + g);
+            bf.b[i] = load_param(p.biases + row * p.groups + g);
+        }
+    };
+
+    Buf buf[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+
+    // stage the activation codes and pairs while the first tiles load
+    const int units_per_row = p.k / 16;
+    for (int u = threadIdx.x; u < B * units_per_row; u += blockDim.x) {
+        const int b = u / units_per_row;
+        const int i = u - b * units_per_row;
+        const uint4 v = *reinterpret_cast<const uint4 *>(a.xq + int64_t(b) * p.k + int64_t(i) * 16);
+        const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
+        xl[(b * 2 + (i & 1)) * chunks + (i >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+    }
+    for (int u = threadIdx.x; u < B * chunks; u += blockDim.x)
+        dl[u] = reinterpret_cast<const float2 *>(a.ds)[u];
+    __syncthreads();
+
+    float acc[R][B];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.0f;
+
+    auto consume = [&](const Buf &bf, int s) {
+        const int t = s / passes;
+        const int j = s - t * passes;
+        const int c = lane + kWave * j;
+        const int64_t row0 = r_begin + int64_t(t) * R;
+        if (c < chunks) {
+            uint4 xp[B][2];
+            float2 dsv[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                xp[b][0] = xl[(b * 2) * chunks + c];
+                xp[b][1] = xl[(b * 2 + 1) * chunks + c];
+                dsv[b] = dl[b * chunks + c];
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                if (row0 + i < r_end) {
+                    const float sc = bf16_to_f32(bf.s[i]);
+                    const float bi = bf16_to_f32(bf.b[i]);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const float t_ = dsv[b].x * float(dot_u4_i8(bf.c[i], xp[b]));
+                        acc[i][b] = fmaf(bi, dsv[b].y, fmaf(sc, t_, acc[i][b]));
+                    }
+                }
+            }
+        }
+        if (j == passes - 1) reduce_store<R, B>(p, acc, row0, r_end, lane, [](int) { return 1.0f; });
+    };
+
+    run_pipeline<D>(buf, steps, issue, consume);
+}
+
+}  // namespace qg
+
+// ------------------------------------------------------------------ C ABI
+
+namespace {
+
+constexpr int64_t kQ8MaxLds = 128 * 1024;
+constexpr int kQ8Rows = 2;          // rows per tile
+constexpr int kQ8Depth = 4;         // steps in flight per wave
+constexpr int kQ8Waves = 4;         // waves per workgroup
+
+bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+qg_status q8_cus(int *cus) {
+    static std::once_flag once[64];
+    static int count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QG_ERR_DEVICE;
+    std::call_once(once[dev], [dev] {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+        count[dev] = v;
+    });
+    if (count[dev] <= 0) return QG_ERR_DEVICE;
+    *cus = count[dev];
+    return QG_OK;
+}
+
+template <int B>
+qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_t lds, hipStream_t stream) {
+    auto kern = qg::qgemv_u4_q8_kernel<kQ8Rows, B, kQ8Depth>;
+    if (lds > 64 * 1024) {
+        static std::once_flag once;
+        static hipError_t err = hipSuccess;
+        std::call_once(once, [&] {
+            err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(kQ8MaxLds));
+        });
+        if (err != hipSuccess) return QG_ERR_LAUNCH;
+    }
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kQ8Waves * qg::kWave), size_t(lds), stream, p, a);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
+                           hipStream_t stream) {
+    if (!x || !xq || !ds) return QG_ERR_NULL_POINTER;
+    if (k < 1 || k % qg::kQ8Block || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    const int64_t blocks = int64_t(batch) * k / qg::kQ8Block;
+    const int64_t grid = (blocks + 255) / 256;
+    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, blocks, xq, ds);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    if (!codes || !scales || !biases || !xq || !ds || !y) return QG_ERR_NULL_POINTER;
+    if (n < 1 || k < 1 || k % qg::kQ8Block) return QG_ERR_BAD_SHAPE;
+    if (n > (int64_t(1) << 31) || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
+    if (group_size != 32 && group_size != 64 && group_size != 128) return QG_ERR_BAD_GROUP_SIZE;
+    if (k % group_size) return QG_ERR_BAD_GROUP_SIZE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    if (out_dtype != QG_OUT_F32 && out_dtype != QG_OUT_BF16) return QG_ERR_BAD_DTYPE;
+    if (!aligned_to(codes, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    if (!aligned_to(scales, 2) || !aligned_to(biases, 2)) return QG_ERR_MISALIGNED;
+    if (!aligned_to(y, out_dtype == QG_OUT_F32 ? 4 : 2)) return QG_ERR_MISALIGNED;
+    const int64_t chunks = k / qg::kQ8Block;
+    const int64_t lds = qg::q8_lds_bytes(batch, chunks);
+    if (lds > kQ8MaxLds) return QG_ERR_TOO_LARGE;
+    int cus = 0;
+    const qg_status st = q8_cus(&cus);
+    if (st != QG_OK) return st;
+
+    qg::Params p{};
+    p.codes = reinterpret_cast<const unsigned char *>(codes);
+    p.scales = scales;
+    p.biases = biases;
+    p.y = y;
+    p.n = n;
+    p.row_bytes = k / 2;
+    p.k = int32_t(k);
+    p.chunks = int32_t(chunks);
+    p.passes = int32_t((chunks + qg::kWave - 1) / qg::kWave);
+    p.groups = int32_t(k / group_size);
+    int shift = 0;
+    while ((qg::kQ8Block << shift) < group_size) ++shift;
+    p.group_shift = shift;
+    p.out_bf16 = out_dtype == QG_OUT_BF16;
+    // two workgroups of four waves per compute unit, fewer when rows are few
+    int64_t blocks = int64_t(cus) * 2;
+    const int64_t max_blocks = (n + kQ8Waves - 1) / kQ8Waves;
+    if (blocks > max_blocks) blocks = max_blocks;
+    p.total_waves = int32_t(blocks * kQ8Waves);
+    const qg::Q8Args a{xq, ds};
+    switch (batch) {
+        case 1: return launch_q8<1>(p, a, int(blocks), lds, stream);
+        case 2: return launch_q8<2>(p, a, int(blocks), lds, stream);
+        case 3: return launch_q8<3>(p, a, int(blocks), lds, stream);
+        default: return launch_q8<4>(p, a, int(blocks), lds, stream);
+    }
+}
+
+}  // extern "C"

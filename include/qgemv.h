@@ -287,6 +287,48 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
 qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y, int64_t n,
                          int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Int8 activation route for affine 4-bit weights.
+ *
+ * The SharpInference issue ("generalize Gemma 4 batched prefill ..."),
+ * "Item C2", quantizes the activation to int8 blocks that carry a pair
+ * {d, s} with s = d * sum(q), widens the 4-bit weights to int8, and applies
+ * the affine minimum once per block through s.  The pages do not print the
+ * quantizer; this library reads it as the symmetric one below.  The route
+ * changes the result by at most sum_k |W^[n,k]| * d_blk / 2 against the bf16
+ * product (each activation moves by at most half a step).
+ *
+ * qg_quantize_q8_1: per batch row, per block of 32 consecutive activations,
+ *   amax = max |x|,  d = fp32(amax / 127),  q = rne(fp32(x * fp32(127 / amax)))
+ *   (in [-127, 127]),  s = fp32(d * sum q);  an all-zero block gives d = s = 0
+ *   and zero codes.  Every operation is a correctly rounded fp32 one, so the
+ *   codes are exact functions of x.  x must be finite.
+ *   x    bf16 [batch, k] (DEVICE), 16-byte aligned
+ *   xq   int8 [batch, k] (DEVICE, caller-owned output), 16-byte aligned,
+ *        natural column order
+ *   ds   float [batch, k/32, 2] = {d, s} (DEVICE, caller-owned output),
+ *        8-byte aligned
+ *   k >= 32, k % 32 == 0                          QG_ERR_BAD_SHAPE
+ *   1 <= batch <= 4                               QG_ERR_BAD_BATCH
+ *
+ * qgemv_affine_u4_q8: y[b, r] = sum over blocks of
+ *   scale[r,g] * d[b,blk] * sum_{k in blk} u[r,k] * q[b,k]  +  bias[r,g] * s[b,blk]
+ *   with the integer block dots exact (4-wide int8 dots) and the rest in
+ *   fp32; one block is one 16-byte chunk of codes.  Codes, scales and biases
+ *   are those of qgemv_affine_u4 (u32 low-first nibbles, bf16 [n, k/gs]).
+ *   xq, ds  as written by qg_quantize_q8_1 (DEVICE)
+ *   y       [batch, n] f32 or bf16 (DEVICE), 4- or 2-byte aligned
+ *   group_size in {32, 64, 128}, k % group_size == 0   QG_ERR_BAD_GROUP_SIZE
+ *   the activation codes and pairs are staged in LDS: batch * k * 1.25 bytes
+ *   must be at most 128 KiB                       QG_ERR_TOO_LARGE
+ *   other checks and errors as for qgemv_affine_u4.
+ * Neither call allocates device memory; both are asynchronous on `stream`. */
+qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
+                           hipStream_t stream);
+qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
+
 /* QG_ABI_VERSION of the loaded library. */
 int qg_abi_version(void);
 

@@ -1,0 +1,180 @@
+"""The int8 activation route for affine 4-bit weights on the GPU, through the
+C ABI (qg_quantize_q8_1, qgemv_affine_u4_q8), against oracle.q8.
+
+* The quantizer's codes and {d, s} pairs are integer or fp32 decisions taken
+  with correctly rounded fp32 operations on both sides: compared bit for bit.
+* The matvec gets the oracle's own quantized activations (never the GPU's)
+  and meets the parity criterion against the float64 block sum.
+* End to end (GPU quantize, then GPU matvec) equals the matvec on the
+  oracle's blocks bitwise, since the blocks are equal.
+* The full-size affine shapes run in the launch configuration the bench
+  times, checked on a seeded sample of rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_weight_qgemv_amd as q
+import synth
+from oracle import formats as F
+from oracle import quantize as Q
+from oracle import q8 as Q8
+from tests import parity
+from tests.gpu_util import dev, host_y, log, out_tensor, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _x_blocks(seed, batch, k):
+    """N(0, 1) activations with a per-block magnitude spread over 2^-10..2^10,
+    some all-zero blocks, and blocks whose products land on .5 ties."""
+    rng = np.random.default_rng([0, 55, seed, batch, k])
+    x = rng.standard_normal((batch, k)).astype(np.float32)
+    x *= np.repeat(np.exp2(rng.integers(-10, 11, (batch, k // 32))), 32, axis=1).astype(np.float32)
+    nb = k // 32
+    if nb > 2:
+        x[:, 32:64] = 0.0                                      # an all-zero block
+        # ties: amax = 127/64 makes 127/amax = 64 exactly, and x = (2m+1)/128
+        # (exact in bf16) gives x * 64 = m + 1/2, rounded to the even neighbour
+        x[0, 64] = 127.0 / 64.0
+        x[0, 65:96] = (2.0 * (np.arange(31) - 15) + 1.0) / 128.0
+    return F.f64_to_bf16_bits(x.astype(np.float64))
+
+
+def _gpu_quantize(x_bits):
+    xq, ds = q.qg_quantize_q8_1(dev(x_bits))
+    torch.cuda.synchronize()
+    return xq.cpu().numpy(), ds.cpu().numpy()
+
+
+@pytest.mark.parametrize("batch,k", [(1, 32), (1, 96), (3, 3840), (4, 4096), (2, 15360), (4, 15360)])
+def test_quantize_bitwise(batch, k):
+    log("q8 quantize batch=%d k=%d" % (batch, k))
+    x = _x_blocks(1, batch, k)
+    xq, ds = _gpu_quantize(x)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    assert np.array_equal(xq, q_ref)
+    assert np.array_equal(ds[..., 0], d_ref)
+    assert np.array_equal(ds[..., 1], s_ref)
+
+
+def _weights(seed, n, k, gs):
+    w = synth.weights(300 + seed, n, k)
+    return Q.quantize_affine(w, 4, gs)
+
+
+def _matvec(arrays, xq, ds, n, gs, bf16=False):
+    y = out_tensor(xq.shape[0], n, bf16)
+    q.qgemv_affine_u4_q8(dev(arrays[0]), dev(arrays[1]), dev(arrays[2]), dev(xq), dev(ds), y, gs)
+    return host_y(y)
+
+
+@pytest.mark.parametrize("n,k,gs,batch", [
+    (1, 32, 32, 1), (37, 128, 64, 1), (250, 3840, 64, 4), (129, 4096, 128, 3),
+    (300, 15360, 64, 2), (64, 15360, 32, 4), (1000, 512, 64, 1),
+])
+def test_matvec_parity(n, k, gs, batch):
+    log("q8 matvec n=%d k=%d gs=%d batch=%d" % (n, k, gs, batch))
+    arrays = _weights(n + k, n, k, gs)
+    x = _x_blocks(2, batch, k)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    ds = np.stack([d_ref, s_ref], axis=-1).astype(np.float32)
+    y = _matvec(arrays, q_ref, ds, n, gs)
+    y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
+    parity.assert_parity(y, y_ref, a_ref, "u4 q8 n=%d k=%d" % (n, k))
+    # bf16 output is the rounding of the same sums
+    yb = _matvec(arrays, q_ref, ds, n, gs, bf16=True)
+    yf = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yb, yf)
+
+
+def test_end_to_end_equals_oracle_blocks():
+    n, k, gs, batch = 513, 3840, 64, 4
+    log("q8 end to end n=%d k=%d batch=%d" % (n, k, batch))
+    arrays = _weights(9, n, k, gs)
+    x = _x_blocks(3, batch, k)
+    dargs = [dev(a) for a in arrays]
+    xq, ds = q.qg_quantize_q8_1(dev(x))
+    y = out_tensor(batch, n)
+    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y, gs)
+    y_gpu = host_y(y)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    y_blocks = _matvec(arrays, q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs)
+    assert np.array_equal(y_gpu, y_blocks)
+    y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
+    parity.assert_parity(y_gpu, y_ref, a_ref, "u4 q8 end to end")
+
+
+def test_all_codes_and_zero_blocks():
+    """Uniform random code words (every nibble value) and an activation with
+    all-zero blocks: the zero blocks add nothing, bias terms included."""
+    n, k, gs = 96, 1024, 64
+    log("q8 uniform codes n=%d k=%d" % (n, k))
+    codes = synth.uniform_words((n, k // 8), 21)
+    scales = synth.uniform_bf16((n, k // gs), -0.05, 0.05, 22)
+    biases = synth.uniform_bf16((n, k // gs), -0.05, 0.05, 23)
+    x = _x_blocks(4, 2, k)
+    x[1, :] = 0
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    y = _matvec((codes, scales, biases), q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs)
+    y_ref, a_ref = Q8.gemv_affine_u4_q8(codes, scales, biases, q_ref, d_ref, s_ref, gs)
+    parity.assert_parity(y, y_ref, a_ref, "u4 q8 uniform codes")
+    assert np.all(y[1] == 0)
+
+
+def test_errors_leave_y_untouched():
+    n, k, gs = 8, 64, 64
+    arrays = [dev(a) for a in _weights(1, n, k, gs)]
+    xq = torch.zeros((1, k), dtype=torch.int8, device="cuda:0")
+    ds = torch.zeros((1, k // 32, 2), dtype=torch.float32, device="cuda:0")
+    y = out_tensor(1, n, fill=7.0)
+    lib = q.lib()
+    import ctypes
+    p = lambda t: ctypes.c_void_p(t.data_ptr())   # noqa: E731
+    s = ctypes.c_void_p(0)
+    assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
+                                  n, 48, gs, 1, 0, s) != 0                       # k not a block multiple
+    assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
+                                  n, k, 48, 1, 0, s) != 0                        # bad group size
+    assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
+                                  n, k, gs, 5, 0, s) != 0                        # batch 5
+    assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
+                                  n, 65536 * 2, gs, 1, 0, s) != 0                # beyond the LDS staging
+    assert lib.qg_quantize_q8_1(p(xq), 48, 1, p(xq), p(ds), s) != 0
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+@pytest.mark.parametrize("name", ["mlp_up", "mlp_down"])
+def test_full_size_sampled(name, batch):
+    sid, n, k = synth.shape(name)
+    gs = 64
+    log("q8 full-size %s [%d x %d] batch=%d" % (name, n, k, batch))
+    w = synth.weights(sid, n, k)
+    arrays = q.qg_quantize_affine(w, 4, gs)
+    del w
+    x = synth.activations(sid, batch, k)
+    dargs = [dev(a) for a in arrays]
+    xq, ds = q.qg_quantize_q8_1(dev(x))
+    y = out_tensor(batch, n)
+    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y, gs)
+    y1 = host_y(y)
+    y2t = out_tensor(batch, n)
+    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y2t, gs)
+    y2 = host_y(y2t)
+    assert np.isfinite(y1).all() and np.array_equal(y1, y2)
+    rows = synth.sample_rows(n, 192, seed=sid)
+    ora = Q.quantize_affine(synth.weight_rows(sid, n, k, rows), 4, gs)
+    for a_lib, a_ora in zip(arrays, ora):
+        assert np.array_equal(a_lib[rows], a_ora)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    y_ref, a_ref = Q8.gemv_affine_u4_q8(ora[0], ora[1], ora[2], q_ref, d_ref, s_ref, gs)
+    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "u4 q8 %s" % name)
+    log("q8 full-size %s: %r" % (name, r))
