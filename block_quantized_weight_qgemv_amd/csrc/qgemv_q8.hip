@@ -25,49 +25,54 @@ constexpr int kQ8Block = 32;
 
 // ------------------------------------------------------------------ quantize
 
-// One thread per block of 32 activations: amax, d = amax / 127, the codes
-// rne(x * (127 / amax)) and s = d * sum(q), all decided in fp32 with
-// correctly rounded operations (an all-zero block gives d = s = 0 and zero
-// codes).  Codes are written in natural column order.
-__global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t blocks,
+// Four lanes per block of 32 activations, eight values each: amax (a max
+// over the four lanes), d = amax / 127, the codes rne(x * (127 / amax)) and
+// s = d * sum(q) (an integer sum over the four lanes), all decided in fp32
+// with correctly rounded operations, so the result does not depend on how the
+// block is split.  An all-zero block gives d = s = 0 and zero codes.  Codes
+// are written in natural column order.  Threads past the last unit compute on
+// a clamped unit and store nothing; the four lanes of a block are always in
+// range together (units come in fours).
+__global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t units,
                                                              int8_t *__restrict__ xq, float *__restrict__ ds) {
-    const int64_t blk = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (blk >= blocks) return;
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + blk * kQ8Block);
-    float v[kQ8Block];
+    const int64_t u_in = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const bool live = u_in < units;
+    const int64_t u = live ? u_in : units - 1;
+    const uint4 w = *reinterpret_cast<const uint4 *>(x + u * 8);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const uint4 w = src[u];
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[8 * u + 2 * i] = bf16_to_f32(ws[i] & 0xFFFFu);
-            v[8 * u + 2 * i + 1] = bf16_to_f32(ws[i] >> 16);
-        }
+    for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(ws[i] & 0xFFFFu);
+        v[2 * i + 1] = bf16_to_f32(ws[i] >> 16);
     }
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kQ8Block; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
     const float d = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 0.0f;
     const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
     int sum = 0;
-    uint32_t packed[8];
+    uint32_t packed[2];
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
+    for (int h = 0; h < 2; ++h) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float r = fminf(fmaxf(__builtin_rintf(__fmul_rn(v[4 * w + j], inv)), -127.0f), 127.0f);
+            const float r = fminf(fmaxf(__builtin_rintf(__fmul_rn(v[4 * h + j], inv)), -127.0f), 127.0f);
             const int qi = int(r);
             sum += qi;
             word |= (uint32_t(qi) & 0xFFu) << (8 * j);
         }
-        packed[w] = word;
+        packed[h] = word;
     }
-    uint4 *dst = reinterpret_cast<uint4 *>(xq + blk * kQ8Block);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    reinterpret_cast<float2 *>(ds)[blk] = make_float2(d, __fmul_rn(d, float(sum)));
+    sum += __shfl_xor(sum, 1, kWave);
+    sum += __shfl_xor(sum, 2, kWave);
+    if (live) {
+        *reinterpret_cast<uint2 *>(xq + u * 8) = make_uint2(packed[0], packed[1]);
+        if ((u & 3) == 0) reinterpret_cast<float2 *>(ds)[u >> 2] = make_float2(d, __fmul_rn(d, float(sum)));
+    }
 }
 
 // ------------------------------------------------------------------ matvec
@@ -144,21 +149,65 @@ __global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const 
         }
     };
 
+    // Stage the activation codes (regrouped) and pairs in LDS.  The first
+    // kSU + kSD loads per thread go out before the weight prefetch, as buffer
+    // loads whose out-of-range lanes fetch nothing: the load counter retires
+    // in order, so storing them waits for them alone.  Longer activations
+    // stage the rest in further rounds after the prefetch.
+    constexpr int kSU = 4, kSD = 2;
+    const int nt = int(blockDim.x), tid = int(threadIdx.x);
+    const int units_per_row = p.k / 16;
+    const int x_units = B * units_per_row;
+    const int d_units = B * chunks;
+    const rsrc_t rx = make_rsrc(a.xq, uint32_t(x_units) * 16u);
+    const rsrc_t rd = make_rsrc(a.ds, uint32_t(d_units) * 8u);
+    auto load_x = [&](int u) -> uint4 {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, int(u < x_units ? uint32_t(u) * 16u : kOutOfRange), 0, 0);
+        return make_uint4(v.x, v.y, v.z, v.w);
+    };
+    auto load_d = [&](int u) -> float2 {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rd, int(u < d_units ? uint32_t(u) * 8u : kOutOfRange), 0, 0);
+        return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+    };
+    auto store_x = [&](int u, const uint4 v) {
+        if (u < x_units) {
+            const int b = u / units_per_row;
+            const int e = u - b * units_per_row;
+            const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
+            xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+        }
+    };
+    uint4 xv[kSU];
+    float2 dv[kSD];
+#pragma unroll
+    for (int i = 0; i < kSU; ++i) xv[i] = load_x(i * nt + tid);
+#pragma unroll
+    for (int i = 0; i < kSD; ++i) dv[i] = load_d(i * nt + tid);
+    __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of the prefetch
+
     Buf buf[D];
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+    __builtin_amdgcn_sched_barrier(0);
 
-    // stage the activation codes and pairs while the first tiles load
-    const int units_per_row = p.k / 16;
-    for (int u = threadIdx.x; u < B * units_per_row; u += blockDim.x) {
-        const int b = u / units_per_row;
-        const int i = u - b * units_per_row;
-        const uint4 v = *reinterpret_cast<const uint4 *>(a.xq + int64_t(b) * p.k + int64_t(i) * 16);
-        const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
-        xl[(b * 2 + (i & 1)) * chunks + (i >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+#pragma unroll
+    for (int i = 0; i < kSU; ++i) store_x(i * nt + tid, xv[i]);
+#pragma unroll
+    for (int i = 0; i < kSD; ++i)
+        if (i * nt + tid < d_units) dl[i * nt + tid] = dv[i];
+    for (int base = kSU * nt; base < x_units; base += kSU * nt) {
+#pragma unroll
+        for (int i = 0; i < kSU; ++i) xv[i] = load_x(base + i * nt + tid);
+#pragma unroll
+        for (int i = 0; i < kSU; ++i) store_x(base + i * nt + tid, xv[i]);
     }
-    for (int u = threadIdx.x; u < B * chunks; u += blockDim.x)
-        dl[u] = reinterpret_cast<const float2 *>(a.ds)[u];
+    for (int base = kSD * nt; base < d_units; base += kSD * nt) {
+#pragma unroll
+        for (int i = 0; i < kSD; ++i) dv[i] = load_d(base + i * nt + tid);
+#pragma unroll
+        for (int i = 0; i < kSD; ++i)
+            if (base + i * nt + tid < d_units) dl[base + i * nt + tid] = dv[i];
+    }
     __syncthreads();
 
     float acc[R][B];
@@ -254,9 +303,9 @@ qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *
     if (k < 1 || k % qg::kQ8Block || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
     if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
     if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
-    const int64_t blocks = int64_t(batch) * k / qg::kQ8Block;
-    const int64_t grid = (blocks + 255) / 256;
-    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, blocks, xq, ds);
+    const int64_t units = int64_t(batch) * k / 8;
+    const int64_t grid = (units + 255) / 256;
+    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq, ds);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
