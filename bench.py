@@ -79,7 +79,7 @@ def algorithmic_bytes(fmt, n, k, batch, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         w = q.qg_bytes_fp4(n, k, gs)
-    elif fmt in ("u4", "u8", "u4q8", "u4q8mv"):
+    elif fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f"):
         w = q.qg_bytes_affine(n, k, 8 if fmt == "u8" else 4, gs)
     else:
         w = q.qg_bytes_fp8(n, k)
@@ -90,7 +90,7 @@ def quantize(fmt, w, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         return q.qg_quantize_fp4_e2m1(w, gs)
-    if fmt in ("u4", "u8", "u4q8", "u4q8mv"):
+    if fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f"):
         return q.qg_quantize_affine(w, 8 if fmt == "u8" else 4, gs)
     return q.qg_quantize_fp8_e4m3_rowwise(w)
 
@@ -143,6 +143,8 @@ class Workload:
             q.qgemv_affine_u4(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
         elif self.fmt == "u8":
             q.qgemv_affine_u8(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
+        elif self.fmt == "u4q8f":
+            q.qgemv_affine_u4_q8_fused(d[0], d[1], d[2], self.x, self.y, self.gs)
         elif self.fmt in ("u4q8", "u4q8mv"):
             if self.fmt == "u4q8":
                 q.qg_quantize_q8_1(self.x, self.xq, self.ds)
@@ -295,6 +297,9 @@ SWEEP = [
     ("u4q8", "mlp_up", 1, 64), ("u4q8mv", "mlp_up", 1, 64), ("u4q8", "mlp_down", 1, 64),
     ("u4q8mv", "mlp_down", 1, 64), ("u4q8", "llama_up", 1, 64), ("u4q8", "llama_down", 1, 64),
     ("u4", "mlp_up", 4, 64), ("u4q8", "mlp_up", 4, 64), ("u4", "mlp_down", 4, 64), ("u4q8", "mlp_down", 4, 64),
+    # quantization inside the matvec (one launch)
+    ("u4q8f", "mlp_up", 1, 64), ("u4q8f", "mlp_down", 1, 64), ("u4q8f", "llama_up", 1, 64),
+    ("u4q8f", "llama_down", 1, 64), ("u4q8f", "mlp_up", 4, 64), ("u4q8f", "mlp_down", 4, 64),
 ]
 
 

@@ -26,7 +26,7 @@ qg_plan = _b.qg_plan
 
 __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
-    "qg_quantize_q8_1", "qgemv_affine_u4_q8",
+    "qg_quantize_q8_1", "qgemv_affine_u4_q8", "qgemv_affine_u4_q8_fused",
     "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
@@ -264,6 +264,24 @@ def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=N
     _same_device(codes, scales, biases, xq, ds, y)
     _check(_lib.qgemv_affine_u4_q8(cp, sp, bp, qp, dp, yp, n, k, int(group_size), batch, out,
                                    _stream(stream, y.device)), "qgemv_affine_u4_q8")
+    return y
+
+
+def qgemv_affine_u4_q8_fused(codes, scales, biases, x, y, group_size=64, stream=None):
+    """qg_quantize_q8_1 then qgemv_affine_u4_q8 in one launch (bitwise the same y)."""
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 8 != k or tuple(scales.shape) != (n, k // group_size) \
+            or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("shapes: codes %s, scales %s, biases %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), k, group_size))
+    _same_device(codes, scales, biases, x, y)
+    _check(_lib.qgemv_affine_u4_q8_fused(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out,
+                                         _stream(stream, y.device)), "qgemv_affine_u4_q8_fused")
     return y
 
 

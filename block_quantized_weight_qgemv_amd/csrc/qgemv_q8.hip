@@ -22,23 +22,20 @@
 namespace qg {
 
 constexpr int kQ8Block = 32;
+constexpr int kQuadXor1 = 0xB1;      // DPP quad_perm [1, 0, 3, 2]
+constexpr int kQuadXor2 = 0x4E;      // DPP quad_perm [2, 3, 0, 1]
 
 // ------------------------------------------------------------------ quantize
 
-// Four lanes per block of 32 activations, eight values each: amax (a max
-// over the four lanes), d = amax / 127, the codes rne(x * (127 / amax)) and
-// s = d * sum(q) (an integer sum over the four lanes), all decided in fp32
-// with correctly rounded operations, so the result does not depend on how the
-// block is split.  An all-zero block gives d = s = 0 and zero codes.  Codes
-// are written in natural column order.  Threads past the last unit compute on
-// a clamped unit and store nothing; the four lanes of a block are always in
-// range together (units come in fours).
-__global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t units,
-                                                             int8_t *__restrict__ xq, float *__restrict__ ds) {
-    const int64_t u_in = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-    const bool live = u_in < units;
-    const int64_t u = live ? u_in : units - 1;
-    const uint4 w = *reinterpret_cast<const uint4 *>(x + u * 8);
+// One lane's share of a block of 32 activations: eight bf16 values w of a
+// block held by four consecutive lanes (lanes 4m..4m+3; every lane of the
+// wave calls this together).  amax is a max over the four lanes,
+// d = amax / 127, the codes rne(x * (127 / amax)) and s = d * sum(q) (an
+// integer sum over the four lanes), all decided in fp32 with correctly
+// rounded operations, so the result does not depend on how the block is
+// split.  An all-zero block gives d = s = 0 and zero codes.  packed holds the
+// lane's eight codes in column order.
+__device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[2], float &d, float &s) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float v[8];
 #pragma unroll
@@ -49,12 +46,12 @@ __global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__r
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, kWave));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, kWave));
-    const float d = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 0.0f;
+    // quad permutes (lanes l ^ 1, then l ^ 2) as DPP moves
+    amax = fmaxf(amax, dpp_f<kQuadXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kQuadXor2>(amax));
+    d = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 0.0f;
     const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
     int sum = 0;
-    uint32_t packed[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint32_t word = 0;
@@ -67,11 +64,25 @@ __global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__r
         }
         packed[h] = word;
     }
-    sum += __shfl_xor(sum, 1, kWave);
-    sum += __shfl_xor(sum, 2, kWave);
+    sum += __builtin_amdgcn_update_dpp(0, sum, kQuadXor1, 0xF, 0xF, false);
+    sum += __builtin_amdgcn_update_dpp(0, sum, kQuadXor2, 0xF, 0xF, false);
+    s = __fmul_rn(d, float(sum));
+}
+
+// One lane per 8 activations (a block is four consecutive lanes).  Threads
+// past the last unit compute on a clamped unit and store nothing; the four
+// lanes of a block are always in range together (units come in fours).
+__global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t units,
+                                                             int8_t *__restrict__ xq, float *__restrict__ ds) {
+    const int64_t u_in = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const bool live = u_in < units;
+    const int64_t u = live ? u_in : units - 1;
+    uint32_t packed[2];
+    float d, s;
+    quantize_unit(*reinterpret_cast<const uint4 *>(x + u * 8), packed, d, s);
     if (live) {
         *reinterpret_cast<uint2 *>(xq + u * 8) = make_uint2(packed[0], packed[1]);
-        if ((u & 3) == 0) reinterpret_cast<float2 *>(ds)[u >> 2] = make_float2(d, __fmul_rn(d, float(sum)));
+        if ((u & 3) == 0) reinterpret_cast<float2 *>(ds)[u >> 2] = make_float2(d, s);
     }
 }
 
@@ -80,6 +91,7 @@ __global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__r
 struct Q8Args {
     const int8_t *xq;       // int8 [B, k], natural order
     const float *ds;        // {d, s} [B, k/32]
+    const uint16_t *x;      // bf16 [B, k], quantized in the staging (kFuse)
 };
 
 // Bytes 0..3 and 4..7 of an 8-column group (x0..x7) regrouped as the even
@@ -114,7 +126,7 @@ __host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks
 // chunks over an R-row tile, D steps in flight.  The workgroup first stages
 // every batch row's codes (regrouped) and {d, s} pairs in LDS, piece-major so
 // that consecutive lanes read consecutive 16 bytes.
-template <int R, int B, int D>
+template <int R, int B, int D, bool kFuse>
 __global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const Q8Args a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     struct Buf {
@@ -149,64 +161,108 @@ __global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const 
         }
     };
 
-    // Stage the activation codes (regrouped) and pairs in LDS.  The first
-    // kSU + kSD loads per thread go out before the weight prefetch, as buffer
-    // loads whose out-of-range lanes fetch nothing: the load counter retires
-    // in order, so storing them waits for them alone.  Longer activations
-    // stage the rest in further rounds after the prefetch.
-    constexpr int kSU = 4, kSD = 2;
-    const int nt = int(blockDim.x), tid = int(threadIdx.x);
-    const int units_per_row = p.k / 16;
-    const int x_units = B * units_per_row;
-    const int d_units = B * chunks;
-    const rsrc_t rx = make_rsrc(a.xq, uint32_t(x_units) * 16u);
-    const rsrc_t rd = make_rsrc(a.ds, uint32_t(d_units) * 8u);
-    auto load_x = [&](int u) -> uint4 {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, int(u < x_units ? uint32_t(u) * 16u : kOutOfRange), 0, 0);
-        return make_uint4(v.x, v.y, v.z, v.w);
-    };
-    auto load_d = [&](int u) -> float2 {
-        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rd, int(u < d_units ? uint32_t(u) * 8u : kOutOfRange), 0, 0);
-        return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
-    };
-    auto store_x = [&](int u, const uint4 v) {
-        if (u < x_units) {
-            const int b = u / units_per_row;
-            const int e = u - b * units_per_row;
-            const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
-            xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
-        }
-    };
-    uint4 xv[kSU];
-    float2 dv[kSD];
-#pragma unroll
-    for (int i = 0; i < kSU; ++i) xv[i] = load_x(i * nt + tid);
-#pragma unroll
-    for (int i = 0; i < kSD; ++i) dv[i] = load_d(i * nt + tid);
-    __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of the prefetch
-
     Buf buf[D];
+    if constexpr (kFuse) {
+        // Quantize x into LDS: a lane per 8 activations (16 bytes of bf16),
+        // the first kSX units per thread loaded before the weight prefetch
+        // as in the other branch.  Every lane runs quantize_unit (its block's
+        // four lanes together); only in-range units are stored.
+        constexpr int kSX = 4;
+        const int nt = int(blockDim.x), tid = int(threadIdx.x);
+        const int upr = p.k / 8;
+        const int units = B * upr;
+        const rsrc_t rxb = make_rsrc(a.x, uint32_t(units) * 16u);
+        auto load_u = [&](int u) -> uint4 {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rxb, int(u < units ? uint32_t(u) * 16u : kOutOfRange), 0, 0);
+            return make_uint4(v.x, v.y, v.z, v.w);
+        };
+        auto quant_store = [&](int u, const uint4 w) {
+            uint32_t packed[2];
+            float d, sv;
+            quantize_unit(w, packed, d, sv);
+            if (u < units) {
+                const int b = u / upr;
+                const int e = u - b * upr;           // 8-column unit in the row
+                const int c = e >> 2, h = e & 3;     // chunk, 8-column group in it
+                const uint2 eo = even_odd(packed[0], packed[1]);
+                reinterpret_cast<uint2 *>(&xl[(b * 2 + (h >> 1)) * chunks + c])[h & 1] = eo;
+                if (h == 0) dl[b * chunks + c] = make_float2(d, sv);
+            }
+        };
+        uint4 xv[kSX];
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
-    __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < kSX; ++i) xv[i] = load_u(i * nt + tid);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kSX; ++i) quant_store(i * nt + tid, xv[i]);
+        for (int base = kSX * nt; base < units; base += kSX * nt) {
+#pragma unroll
+            for (int i = 0; i < kSX; ++i) xv[i] = load_u(base + i * nt + tid);
+#pragma unroll
+            for (int i = 0; i < kSX; ++i) quant_store(base + i * nt + tid, xv[i]);
+        }
+    } else {
+        // Stage the activation codes (regrouped) and pairs in LDS.  The first
+        // kSU + kSD loads per thread go out before the weight prefetch, as buffer
+        // loads whose out-of-range lanes fetch nothing: the load counter retires
+        // in order, so storing them waits for them alone.  Longer activations
+        // stage the rest in further rounds after the prefetch.
+        constexpr int kSU = 4, kSD = 2;
+        const int nt = int(blockDim.x), tid = int(threadIdx.x);
+        const int units_per_row = p.k / 16;
+        const int x_units = B * units_per_row;
+        const int d_units = B * chunks;
+        const rsrc_t rx = make_rsrc(a.xq, uint32_t(x_units) * 16u);
+        const rsrc_t rd = make_rsrc(a.ds, uint32_t(d_units) * 8u);
+        auto load_x = [&](int u) -> uint4 {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, int(u < x_units ? uint32_t(u) * 16u : kOutOfRange), 0, 0);
+            return make_uint4(v.x, v.y, v.z, v.w);
+        };
+        auto load_d = [&](int u) -> float2 {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rd, int(u < d_units ? uint32_t(u) * 8u : kOutOfRange), 0, 0);
+            return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+        };
+        auto store_x = [&](int u, const uint4 v) {
+            if (u < x_units) {
+                const int b = u / units_per_row;
+                const int e = u - b * units_per_row;
+                const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
+                xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+            }
+        };
+        uint4 xv[kSU];
+        float2 dv[kSD];
+    #pragma unroll
+        for (int i = 0; i < kSU; ++i) xv[i] = load_x(i * nt + tid);
+    #pragma unroll
+        for (int i = 0; i < kSD; ++i) dv[i] = load_d(i * nt + tid);
+        __builtin_amdgcn_sched_barrier(0);       // keep these loads ahead of the prefetch
 
-#pragma unroll
-    for (int i = 0; i < kSU; ++i) store_x(i * nt + tid, xv[i]);
-#pragma unroll
-    for (int i = 0; i < kSD; ++i)
-        if (i * nt + tid < d_units) dl[i * nt + tid] = dv[i];
-    for (int base = kSU * nt; base < x_units; base += kSU * nt) {
-#pragma unroll
-        for (int i = 0; i < kSU; ++i) xv[i] = load_x(base + i * nt + tid);
-#pragma unroll
-        for (int i = 0; i < kSU; ++i) store_x(base + i * nt + tid, xv[i]);
-    }
-    for (int base = kSD * nt; base < d_units; base += kSD * nt) {
-#pragma unroll
-        for (int i = 0; i < kSD; ++i) dv[i] = load_d(base + i * nt + tid);
-#pragma unroll
+    #pragma unroll
+        for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        __builtin_amdgcn_sched_barrier(0);
+
+    #pragma unroll
+        for (int i = 0; i < kSU; ++i) store_x(i * nt + tid, xv[i]);
+    #pragma unroll
         for (int i = 0; i < kSD; ++i)
-            if (base + i * nt + tid < d_units) dl[base + i * nt + tid] = dv[i];
+            if (i * nt + tid < d_units) dl[i * nt + tid] = dv[i];
+        for (int base = kSU * nt; base < x_units; base += kSU * nt) {
+    #pragma unroll
+            for (int i = 0; i < kSU; ++i) xv[i] = load_x(base + i * nt + tid);
+    #pragma unroll
+            for (int i = 0; i < kSU; ++i) store_x(base + i * nt + tid, xv[i]);
+        }
+        for (int base = kSD * nt; base < d_units; base += kSD * nt) {
+    #pragma unroll
+            for (int i = 0; i < kSD; ++i) dv[i] = load_d(base + i * nt + tid);
+    #pragma unroll
+            for (int i = 0; i < kSD; ++i)
+                if (base + i * nt + tid < d_units) dl[base + i * nt + tid] = dv[i];
+        }
     }
     __syncthreads();
 
@@ -277,9 +333,9 @@ qg_status q8_cus(int *cus) {
     return QG_OK;
 }
 
-template <int B>
+template <int B, bool kFuse>
 qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_t lds, hipStream_t stream) {
-    auto kern = qg::qgemv_u4_q8_kernel<kQ8Rows, B, kQ8Depth>;
+    auto kern = qg::qgemv_u4_q8_kernel<kQ8Rows, B, kQ8Depth, kFuse>;
     if (lds > 64 * 1024) {
         static std::once_flag once;
         static hipError_t err = hipSuccess;
@@ -293,33 +349,19 @@ qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
-}  // namespace
-
-extern "C" {
-
-qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
-                           hipStream_t stream) {
-    if (!x || !xq || !ds) return QG_ERR_NULL_POINTER;
-    if (k < 1 || k % qg::kQ8Block || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
-    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
-    if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
-    const int64_t units = int64_t(batch) * k / 8;
-    const int64_t grid = (units + 255) / 256;
-    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq, ds);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
-}
-
-qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
-                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
-    if (!codes || !scales || !biases || !xq || !ds || !y) return QG_ERR_NULL_POINTER;
+// Validation (complete before any HIP call) and launch of the matvec; the
+// activation side (a) is checked by the entry points.
+qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const qg::Q8Args &a,
+                 void *y, int64_t n, int64_t k, int32_t group_size, int32_t batch, qg_out_dtype out_dtype,
+                 hipStream_t stream) {
+    if (!codes || !scales || !biases || !y) return QG_ERR_NULL_POINTER;
     if (n < 1 || k < 1 || k % qg::kQ8Block) return QG_ERR_BAD_SHAPE;
     if (n > (int64_t(1) << 31) || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
     if (group_size != 32 && group_size != 64 && group_size != 128) return QG_ERR_BAD_GROUP_SIZE;
     if (k % group_size) return QG_ERR_BAD_GROUP_SIZE;
     if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
     if (out_dtype != QG_OUT_F32 && out_dtype != QG_OUT_BF16) return QG_ERR_BAD_DTYPE;
-    if (!aligned_to(codes, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    if (!aligned_to(codes, 16)) return QG_ERR_MISALIGNED;
     if (!aligned_to(scales, 2) || !aligned_to(biases, 2)) return QG_ERR_MISALIGNED;
     if (!aligned_to(y, out_dtype == QG_OUT_F32 ? 4 : 2)) return QG_ERR_MISALIGNED;
     const int64_t chunks = k / qg::kQ8Block;
@@ -349,13 +391,55 @@ qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, cons
     const int64_t max_blocks = (n + kQ8Waves - 1) / kQ8Waves;
     if (blocks > max_blocks) blocks = max_blocks;
     p.total_waves = int32_t(blocks * kQ8Waves);
-    const qg::Q8Args a{xq, ds};
-    switch (batch) {
-        case 1: return launch_q8<1>(p, a, int(blocks), lds, stream);
-        case 2: return launch_q8<2>(p, a, int(blocks), lds, stream);
-        case 3: return launch_q8<3>(p, a, int(blocks), lds, stream);
-        default: return launch_q8<4>(p, a, int(blocks), lds, stream);
+    const int nb = int(blocks);
+    if (a.x) {
+        switch (batch) {
+            case 1: return launch_q8<1, true>(p, a, nb, lds, stream);
+            case 2: return launch_q8<2, true>(p, a, nb, lds, stream);
+            case 3: return launch_q8<3, true>(p, a, nb, lds, stream);
+            default: return launch_q8<4, true>(p, a, nb, lds, stream);
+        }
     }
+    switch (batch) {
+        case 1: return launch_q8<1, false>(p, a, nb, lds, stream);
+        case 2: return launch_q8<2, false>(p, a, nb, lds, stream);
+        case 3: return launch_q8<3, false>(p, a, nb, lds, stream);
+        default: return launch_q8<4, false>(p, a, nb, lds, stream);
+    }
+}
+
+}  // namespace
+
+extern "C" {
+
+qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
+                           hipStream_t stream) {
+    if (!x || !xq || !ds) return QG_ERR_NULL_POINTER;
+    if (k < 1 || k % qg::kQ8Block || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
+    if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
+    if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    const int64_t units = int64_t(batch) * k / 8;
+    const int64_t grid = (units + 255) / 256;
+    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq, ds);
+    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+}
+
+qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    if (!xq || !ds) return QG_ERR_NULL_POINTER;
+    if (!aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    return run_q8(codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
+                  stream);
+}
+
+qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                   const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                                   int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    if (!x) return QG_ERR_NULL_POINTER;
+    if (!aligned_to(x, 16)) return QG_ERR_MISALIGNED;
+    return run_q8(codes, scales, biases, qg::Q8Args{nullptr, nullptr, x}, y, n, k, group_size, batch, out_dtype,
+                  stream);
 }
 
 }  // extern "C"

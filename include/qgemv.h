@@ -322,12 +322,23 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   the activation codes and pairs are staged in LDS: batch * k * 1.25 bytes
  *   must be at most 128 KiB                       QG_ERR_TOO_LARGE
  *   other checks and errors as for qgemv_affine_u4.
- * Neither call allocates device memory; both are asynchronous on `stream`. */
+ * qgemv_affine_u4_q8_fused: the same product with the quantization of x
+ *   done inside the matvec (each workgroup quantizes x as it stages it, with
+ *   the arithmetic of qg_quantize_q8_1), so one launch replaces two and no
+ *   int8 copy of x goes to memory.  Returns bitwise what qg_quantize_q8_1
+ *   followed by qgemv_affine_u4_q8 returns.
+ *   x       bf16 [batch, k] (DEVICE), 16-byte aligned, finite
+ *   other arguments, checks and errors as for qgemv_affine_u4_q8.
+ * None of these calls allocates device memory; all are asynchronous on
+ * `stream`. */
 qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
                            hipStream_t stream);
 qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                              const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
+qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                   const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                                   int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 
 /* QG_ABI_VERSION of the loaded library. */
 int qg_abi_version(void);

@@ -111,6 +111,30 @@ def test_end_to_end_equals_oracle_blocks():
     parity.assert_parity(y_gpu, y_ref, a_ref, "u4 q8 end to end")
 
 
+@pytest.mark.parametrize("n,k,gs,batch", [
+    (1, 32, 32, 1), (37, 128, 64, 2), (513, 3840, 64, 4), (129, 4096, 128, 3), (300, 15360, 64, 1),
+    (64, 15360, 32, 4), (1000, 8192, 64, 1),
+])
+def test_fused_equals_separate_bitwise(n, k, gs, batch):
+    """The in-kernel quantization stages the same blocks as qg_quantize_q8_1,
+    so the fused call returns the two-launch result bit for bit."""
+    log("q8 fused n=%d k=%d gs=%d batch=%d" % (n, k, gs, batch))
+    arrays = _weights(7 * n + k, n, k, gs)
+    x = _x_blocks(5, batch, k)
+    dargs = [dev(a) for a in arrays]
+    xd = dev(x)
+    xq, ds = q.qg_quantize_q8_1(xd)
+    y_sep = out_tensor(batch, n)
+    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y_sep, gs)
+    y_fused = out_tensor(batch, n)
+    q.qgemv_affine_u4_q8_fused(dargs[0], dargs[1], dargs[2], xd, y_fused, gs)
+    a, b = host_y(y_sep), host_y(y_fused)
+    assert np.array_equal(a, b)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
+    parity.assert_parity(b, y_ref, a_ref, "u4 q8 fused n=%d k=%d" % (n, k))
+
+
 def test_all_codes_and_zero_blocks():
     """Uniform random code words (every nibble value) and an activation with
     all-zero blocks: the zero blocks add nothing, bias terms included."""
@@ -147,6 +171,11 @@ def test_errors_leave_y_untouched():
     assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
                                   n, 65536 * 2, gs, 1, 0, s) != 0                # beyond the LDS staging
     assert lib.qg_quantize_q8_1(p(xq), 48, 1, p(xq), p(ds), s) != 0
+    xb = torch.zeros((1, k), dtype=torch.bfloat16, device="cuda:0")
+    assert lib.qgemv_affine_u4_q8_fused(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xb), p(y),
+                                        n, k, gs, 0, 0, s) != 0                  # batch 0
+    assert lib.qgemv_affine_u4_q8_fused(p(arrays[0]), p(arrays[1]), p(arrays[2]), None, p(y),
+                                        n, k, gs, 1, 0, s) != 0                  # null x
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
 
