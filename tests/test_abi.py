@@ -170,3 +170,39 @@ def test_qgemm_argument_errors():
     assert fn(ODD, A2, A3, A4, 64, 256, 32, 8, 0, None) == MIS              # codes 8-byte aligned only
     assert fn(A, A2, ODD, A4, 64, 256, 32, 8, 0, None) == MIS               # x
     assert fn(A, A2, A3, ctypes.c_void_p(0x400002), 64, 256, 32, 8, 0, None) == MIS   # f32 y 2-byte aligned
+
+
+def _q8(codes=A, scales=A2, biases=A2, xq=A3, ds=A4, y=A4, n=8, k=128, gs=64, b=1, out=0):
+    return LIB.qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, n, k, gs, b, out, None)
+
+
+def _q8f(codes=A, scales=A2, biases=A2, x=A3, y=A4, n=8, k=128, gs=64, b=1, out=0):
+    return LIB.qgemv_affine_u4_q8_fused(codes, scales, biases, x, y, n, k, gs, b, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"codes": None}, NULL), ({"biases": None}, NULL), ({"xq": None}, NULL), ({"ds": None}, NULL),
+    ({"n": 0}, SHAPE), ({"k": 48}, SHAPE), ({"k": 0}, SHAPE), ({"gs": 16}, GROUP), ({"k": 96, "gs": 64}, GROUP),
+    ({"codes": ODD}, MIS), ({"xq": ODD}, MIS), ({"ds": ctypes.c_void_p(0x200004)}, MIS),
+    ({"b": 0}, BATCH), ({"b": 5}, BATCH), ({"out": 2}, DTYPE), ({"k": 1 << 17, "b": 1}, LARGE),
+])
+def test_int8_route_validation(kw, status):
+    # every argument error is returned before any device call
+    assert _q8(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"x": None}, NULL), ({"x": ODD}, MIS), ({"k": 40}, SHAPE), ({"gs": 256}, GROUP), ({"b": 6}, BATCH),
+    ({"k": 32768, "b": 4}, LARGE),
+])
+def test_int8_route_fused_validation(kw, status):
+    assert _q8f(**kw) == status
+
+
+def test_int8_quantize_validation():
+    fn = LIB.qg_quantize_q8_1
+    assert fn(None, 64, 1, A3, A4, None) == NULL
+    assert fn(A3, 48, 1, A3, A4, None) == SHAPE
+    assert fn(A3, 0, 1, A3, A4, None) == SHAPE
+    assert fn(A3, 64, 0, A3, A4, None) == BATCH
+    assert fn(A3, 64, 1, ODD, A4, None) == MIS
