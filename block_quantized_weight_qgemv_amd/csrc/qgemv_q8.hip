@@ -312,8 +312,10 @@ __global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const 
 namespace {
 
 constexpr int64_t kQ8MaxLds = 128 * 1024;
-constexpr int kQ8Rows = 2;          // rows per tile
-constexpr int kQ8Depth = 4;         // steps in flight per wave
+// rows per tile and steps in flight per wave: 8 code chunks in flight per
+// lane either way; 4-row tiles halve the LDS activation reads per weight
+// where the batch is 3-4 and every wave has at least 4 rows
+constexpr int q8_depth(int r) { return 8 / r; }
 constexpr int kQ8Waves = 4;         // waves per workgroup
 
 bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -333,9 +335,9 @@ qg_status q8_cus(int *cus) {
     return QG_OK;
 }
 
-template <int B, bool kFuse>
+template <int R, int B, bool kFuse>
 qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_t lds, hipStream_t stream) {
-    auto kern = qg::qgemv_u4_q8_kernel<kQ8Rows, B, kQ8Depth, kFuse>;
+    auto kern = qg::qgemv_u4_q8_kernel<R, B, q8_depth(R), kFuse>;
     if (lds > 64 * 1024) {
         static std::once_flag once;
         static hipError_t err = hipSuccess;
@@ -392,19 +394,24 @@ qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *
     if (blocks > max_blocks) blocks = max_blocks;
     p.total_waves = int32_t(blocks * kQ8Waves);
     const int nb = int(blocks);
+    const bool wide = batch >= 3 && n >= int64_t(4) * p.total_waves;
     if (a.x) {
         switch (batch) {
-            case 1: return launch_q8<1, true>(p, a, nb, lds, stream);
-            case 2: return launch_q8<2, true>(p, a, nb, lds, stream);
-            case 3: return launch_q8<3, true>(p, a, nb, lds, stream);
-            default: return launch_q8<4, true>(p, a, nb, lds, stream);
+            case 1: return launch_q8<2, 1, true>(p, a, nb, lds, stream);
+            case 2: return launch_q8<2, 2, true>(p, a, nb, lds, stream);
+            case 3: return wide ? launch_q8<4, 3, true>(p, a, nb, lds, stream)
+                                : launch_q8<2, 3, true>(p, a, nb, lds, stream);
+            default: return wide ? launch_q8<4, 4, true>(p, a, nb, lds, stream)
+                                 : launch_q8<2, 4, true>(p, a, nb, lds, stream);
         }
     }
     switch (batch) {
-        case 1: return launch_q8<1, false>(p, a, nb, lds, stream);
-        case 2: return launch_q8<2, false>(p, a, nb, lds, stream);
-        case 3: return launch_q8<3, false>(p, a, nb, lds, stream);
-        default: return launch_q8<4, false>(p, a, nb, lds, stream);
+        case 1: return launch_q8<2, 1, false>(p, a, nb, lds, stream);
+        case 2: return launch_q8<2, 2, false>(p, a, nb, lds, stream);
+        case 3: return wide ? launch_q8<4, 3, false>(p, a, nb, lds, stream)
+                            : launch_q8<2, 3, false>(p, a, nb, lds, stream);
+        default: return wide ? launch_q8<4, 4, false>(p, a, nb, lds, stream)
+                             : launch_q8<2, 4, false>(p, a, nb, lds, stream);
     }
 }
 

@@ -135,3 +135,65 @@ def test_graph_replay_with_norms_matches_eager_bitwise():
         for (name, *_, y_f, y_s), (f, s) in zip(mats, eager):
             assert np.array_equal(y_f.cpu().numpy(), f), (rep, name, "fused")
             assert np.array_equal(y_s.cpu().numpy(), s), (rep, name, "separate")
+
+
+def test_graph_replay_int8_route_matches_eager_bitwise():
+    """The int8 activation route in one graph: a quantize launch whose blocks
+    feed two matvecs (as one x feeds gate and up), and the fused launch,
+    over affine u4 shapes at batch 1 and 4.  Every replay equals the eager
+    launches bitwise (the quantized blocks and pairs included)."""
+    cases = []
+    for ci, (n, k, b) in enumerate([(1024, 3840, 1), (480, 15360, 4), (768, 4096, 4)]):
+        w1 = synth.weights(230 + ci, n, k)
+        w2 = synth.weights(240 + ci, n, k)
+        a1 = [dev(a) for a in q.qg_quantize_affine(w1, 4, 64)]
+        a2 = [dev(a) for a in q.qg_quantize_affine(w2, 4, 64)]
+        x = dev(synth.activations(230 + ci, b, k))
+        xq = torch.empty((b, k), dtype=torch.int8, device="cuda:0")
+        ds = torch.empty((b, k // 32, 2), dtype=torch.float32, device="cuda:0")
+        ys = [torch.empty((b, n), dtype=torch.float32, device="cuda:0") for _ in range(3)]
+        cases.append((a1, a2, x, xq, ds, ys))
+
+    def step():
+        for a1, a2, x, xq, ds, ys in cases:
+            q.qg_quantize_q8_1(x, xq, ds)
+            q.qgemv_affine_u4_q8(a1[0], a1[1], a1[2], xq, ds, ys[0], 64)
+            q.qgemv_affine_u4_q8(a2[0], a2[1], a2[2], xq, ds, ys[1], 64)
+            q.qgemv_affine_u4_q8_fused(a1[0], a1[1], a1[2], x, ys[2], 64)
+
+    def outputs():
+        return [[t.cpu().numpy().copy() for t in (xq, ds, *ys)] for _, _, _, xq, ds, ys in cases]
+
+    log("graph int8: eager step")
+    step()
+    torch.cuda.synchronize()
+    eager = outputs()
+    for e in eager:
+        assert np.isfinite(e[3]).all() and np.array_equal(e[2], e[4])   # fused equals two launches
+
+    log("graph int8: capture")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+
+    scratch = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(3):
+        for _, _, _, xq, ds, ys in cases:
+            xq.zero_()
+            ds.zero_()
+            for t in ys:
+                t.zero_()
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        log("graph int8: replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for ci, (got, want) in enumerate(zip(outputs(), eager)):
+            for j, (a, b) in enumerate(zip(got, want)):
+                assert np.array_equal(a, b), (rep, ci, j)
