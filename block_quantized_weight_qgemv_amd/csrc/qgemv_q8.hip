@@ -127,7 +127,7 @@ __host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks
 // every batch row's codes (regrouped) and {d, s} pairs in LDS, piece-major so
 // that consecutive lanes read consecutive 16 bytes.
 template <int R, int B, int D, bool kFuse>
-__global__ void __launch_bounds__(256) qgemv_u4_q8_kernel(const Params p, const Q8Args a) {
+__global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const Q8Args a) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     struct Buf {
         uint4 c[R];
@@ -316,7 +316,13 @@ constexpr int64_t kQ8MaxLds = 128 * 1024;
 // lane either way; 4-row tiles halve the LDS activation reads per weight
 // where the batch is 3-4 and every wave has at least 4 rows
 constexpr int q8_depth(int r) { return 8 / r; }
-constexpr int kQ8Waves = 4;         // waves per workgroup
+// Eight waves per compute unit: two workgroups of four, or one workgroup of
+// eight where staging costs more than the second workgroup brings, so each CU
+// stages the activations once: beyond 32 KiB of them, and beyond 16 KiB when
+// the staging also quantizes x or the batch is 3-4 (measured on the affine
+// shapes of the decode step).
+constexpr int64_t kQ8WideStage = 32 * 1024;
+constexpr int64_t kQ8WideStageHeavy = 16 * 1024;
 
 bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -336,7 +342,8 @@ qg_status q8_cus(int *cus) {
 }
 
 template <int R, int B, bool kFuse>
-qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_t lds, hipStream_t stream) {
+qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int waves, int64_t lds,
+                    hipStream_t stream) {
     auto kern = qg::qgemv_u4_q8_kernel<R, B, q8_depth(R), kFuse>;
     if (lds > 64 * 1024) {
         static std::once_flag once;
@@ -347,7 +354,7 @@ qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int64_
         });
         if (err != hipSuccess) return QG_ERR_LAUNCH;
     }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kQ8Waves * qg::kWave), size_t(lds), stream, p, a);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * qg::kWave), size_t(lds), stream, p, a);
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
@@ -388,30 +395,31 @@ qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *
     while ((qg::kQ8Block << shift) < group_size) ++shift;
     p.group_shift = shift;
     p.out_bf16 = out_dtype == QG_OUT_BF16;
-    // two workgroups of four waves per compute unit, fewer when rows are few
-    int64_t blocks = int64_t(cus) * 2;
-    const int64_t max_blocks = (n + kQ8Waves - 1) / kQ8Waves;
+    const bool heavy = a.x != nullptr || batch >= 3;
+    const int waves = (lds > kQ8WideStage || (heavy && lds > kQ8WideStageHeavy)) ? 8 : 4;
+    int64_t blocks = int64_t(cus) * 8 / waves;          // fewer when rows are few
+    const int64_t max_blocks = (n + waves - 1) / waves;
     if (blocks > max_blocks) blocks = max_blocks;
-    p.total_waves = int32_t(blocks * kQ8Waves);
+    p.total_waves = int32_t(blocks * waves);
     const int nb = int(blocks);
     const bool wide = batch >= 3 && n >= int64_t(4) * p.total_waves;
     if (a.x) {
         switch (batch) {
-            case 1: return launch_q8<2, 1, true>(p, a, nb, lds, stream);
-            case 2: return launch_q8<2, 2, true>(p, a, nb, lds, stream);
-            case 3: return wide ? launch_q8<4, 3, true>(p, a, nb, lds, stream)
-                                : launch_q8<2, 3, true>(p, a, nb, lds, stream);
-            default: return wide ? launch_q8<4, 4, true>(p, a, nb, lds, stream)
-                                 : launch_q8<2, 4, true>(p, a, nb, lds, stream);
+            case 1: return launch_q8<2, 1, true>(p, a, nb, waves, lds, stream);
+            case 2: return launch_q8<2, 2, true>(p, a, nb, waves, lds, stream);
+            case 3: return wide ? launch_q8<4, 3, true>(p, a, nb, waves, lds, stream)
+                                : launch_q8<2, 3, true>(p, a, nb, waves, lds, stream);
+            default: return wide ? launch_q8<4, 4, true>(p, a, nb, waves, lds, stream)
+                                 : launch_q8<2, 4, true>(p, a, nb, waves, lds, stream);
         }
     }
     switch (batch) {
-        case 1: return launch_q8<2, 1, false>(p, a, nb, lds, stream);
-        case 2: return launch_q8<2, 2, false>(p, a, nb, lds, stream);
-        case 3: return wide ? launch_q8<4, 3, false>(p, a, nb, lds, stream)
-                            : launch_q8<2, 3, false>(p, a, nb, lds, stream);
-        default: return wide ? launch_q8<4, 4, false>(p, a, nb, lds, stream)
-                             : launch_q8<2, 4, false>(p, a, nb, lds, stream);
+        case 1: return launch_q8<2, 1, false>(p, a, nb, waves, lds, stream);
+        case 2: return launch_q8<2, 2, false>(p, a, nb, waves, lds, stream);
+        case 3: return wide ? launch_q8<4, 3, false>(p, a, nb, waves, lds, stream)
+                            : launch_q8<2, 3, false>(p, a, nb, waves, lds, stream);
+        default: return wide ? launch_q8<4, 4, false>(p, a, nb, waves, lds, stream)
+                             : launch_q8<2, 4, false>(p, a, nb, waves, lds, stream);
     }
 }
 
