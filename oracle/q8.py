@@ -1,4 +1,4 @@
-"""Int8 activation route for affine 4-bit weights.  Test infrastructure.
+"""Int8 activation route for affine 4-bit and 8-bit weights.  Test infrastructure.
 
 Source: "perf(cuda): generalize Gemma 4 batched prefill + flash attn + decode
 graphs to dense Q4_K models", sections "Item C2" (the activation is
@@ -26,7 +26,7 @@ The matvec on those blocks then computes, in float64,
   y[b, r] = sum_blocks  scale[r, g] * d_blk * sum_{k in blk} u[r, k] * q[b, k]
                       + bias[r, g] * s_blk
 
-with u the 4-bit codes and g the block's scale group.  Mathematically this is
+with u the 4-bit or 8-bit codes and g the block's scale group.  Mathematically this is
 sum_k (scale*u + bias)[r, k] * (d * q)[b, k] with the block's activation sum
 rounded once to fp32 (s); tests pin it against the dequantized weights of
 oracle.gemv applied to the dequantized activations d * q.
@@ -70,8 +70,18 @@ def gemv_affine_u4_q8(codes, scales, biases, q, d, s, group_size):
     with W^ the dequantized weight and x^ = d * q, the conditioning mass of
     the parity criterion.
     """
+    return gemv_affine_q8(codes, scales, biases, q, d, s, 4, group_size)
+
+
+def gemv_affine_u8_q8(codes, scales, biases, q, d, s, group_size):
+    """As gemv_affine_u4_q8 for 8-bit codes, uint32 [N, K/4] low-first bytes."""
+    return gemv_affine_q8(codes, scales, biases, q, d, s, 8, group_size)
+
+
+def gemv_affine_q8(codes, scales, biases, q, d, s, bits, group_size):
+    """The block sum for affine codes of `bits` (4 or 8) bits."""
     codes = np.asarray(codes, dtype=np.uint32)
-    n, k = codes.shape[0], codes.shape[1] * 8
+    n, k = codes.shape[0], codes.shape[1] * (32 // bits)
     q = np.atleast_2d(np.asarray(q, dtype=np.int8))
     d = np.atleast_2d(np.asarray(d, dtype=np.float32)).astype(np.float64)
     s = np.atleast_2d(np.asarray(s, dtype=np.float32)).astype(np.float64)
@@ -90,7 +100,7 @@ def gemv_affine_u4_q8(codes, scales, biases, q, d, s, group_size):
     xhat = (d[:, :, None] * qb).reshape(bsz, k)                        # d * q, exact in float64
     for r0 in range(0, n, 1024):
         r1 = min(n, r0 + 1024)
-        u = unpack_u32(codes[r0:r1], k, 4).astype(np.int64).reshape(r1 - r0, nblk, BLOCK)
+        u = unpack_u32(codes[r0:r1], k, bits).astype(np.int64).reshape(r1 - r0, nblk, BLOCK)
         s_blk = sc[r0:r1][:, grp]                                      # [rows, nblk]
         b_blk = bi[r0:r1][:, grp]
         for b in range(bsz):

@@ -15,6 +15,7 @@ import os
 from fractions import Fraction
 
 import numpy as np
+import pytest
 
 from oracle import formats as F
 from oracle import gemv as G
@@ -83,22 +84,31 @@ def test_degenerate_blocks():
     assert np.array_equal(q1, q2) and np.array_equal(d1 * 64, d2) and np.array_equal(s1 * 64, s2)
 
 
-def _affine_u4(rng, n, k, gs):
+def _affine(rng, n, k, gs, bits=4):
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
-    codes, scales, biases = Q.quantize_affine(w, 4, gs)
+    codes, scales, biases = Q.quantize_affine(w, bits, gs)
     return codes, scales, biases
 
 
-def test_matvec_matches_dequantized_product():
+def _affine_u4(rng, n, k, gs):
+    return _affine(rng, n, k, gs, 4)
+
+
+def _q8_matvec(bits):
+    return Q8.gemv_affine_u4_q8 if bits == 4 else Q8.gemv_affine_u8_q8
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matvec_matches_dequantized_product(bits):
     """y equals W^ (oracle.gemv's dequantized weights) times x^ = d * q, up to
     the one fp32 rounding of s per block."""
-    rng = _rng(7)
+    rng = _rng(7 + bits)
     for n, k, gs, bsz in [(37, 128, 64, 1), (16, 256, 32, 3), (9, 384, 128, 4)]:
-        codes, scales, biases = _affine_u4(rng, n, k, gs)
+        codes, scales, biases = _affine(rng, n, k, gs, bits)
         x = _bits(rng.standard_normal((bsz, k)))
         q, d, s = Q8.quantize_q8_1(x)
-        y, a = Q8.gemv_affine_u4_q8(codes, scales, biases, q, d, s, gs)
-        w_hat = G.dequant_affine(codes, scales, biases, k, 4, gs)
+        y, a = _q8_matvec(bits)(codes, scales, biases, q, d, s, gs)
+        w_hat = G.dequant_affine(codes, scales, biases, k, bits, gs)
         xhat = np.repeat(d.astype(np.float64), 32, axis=1) * q.astype(np.float64)
         y_ref = xhat @ w_hat.T
         bi = np.repeat(F.bf16_bits_to_f64(biases), gs, axis=1)
@@ -108,20 +118,21 @@ def test_matvec_matches_dequantized_product():
         assert np.allclose(a, np.abs(xhat) @ np.abs(w_hat).T, rtol=1e-12)
 
 
-def test_matvec_integer_brute_force():
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matvec_integer_brute_force(bits):
     """x integer in [-127, 127] with a block maximum of 127: d = 1, q = x, s =
     sum x, and y is an exact rational sum computed term by term."""
-    rng = _rng(3)
+    rng = _rng(3 + bits)
     n, k, gs = 5, 64, 32
-    codes_u = rng.integers(0, 16, (n, k))
-    codes = L.pack_u32(codes_u.astype(np.uint8), 4)
+    codes_u = rng.integers(0, 1 << bits, (n, k))
+    codes = L.pack_u32(codes_u.astype(np.uint8), bits)
     scales = _bits(rng.uniform(-1, 1, (n, k // gs)))
     biases = _bits(rng.uniform(-1, 1, (n, k // gs)))
     xi = rng.integers(-127, 128, (1, k))
     xi[0, ::32] = 127
     q, d, s = Q8.quantize_q8_1(_bits(xi.astype(np.float64)))
     assert np.array_equal(q.astype(np.int64), xi) and np.all(d == 1)
-    y, _ = Q8.gemv_affine_u4_q8(codes, scales, biases, q, d, s, gs)
+    y, _ = _q8_matvec(bits)(codes, scales, biases, q, d, s, gs)
     sc = F.bf16_bits_to_f64(scales)
     bi = F.bf16_bits_to_f64(biases)
     for r in range(n):
@@ -132,17 +143,18 @@ def test_matvec_integer_brute_force():
         assert abs(Fraction(y[0, r]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 60)
 
 
-def test_route_error_bound_against_bf16_product():
+@pytest.mark.parametrize("bits", [4, 8])
+def test_route_error_bound_against_bf16_product(bits):
     """The int8 route differs from the bf16 product by at most
     sum_k |W^| * d / 2 (each activation moves by at most half a step)."""
-    rng = _rng(9)
+    rng = _rng(9 + bits)
     n, k, gs = 64, 512, 64
-    codes, scales, biases = _affine_u4(rng, n, k, gs)
+    codes, scales, biases = _affine(rng, n, k, gs, bits)
     x = _bits(rng.standard_normal((2, k)))
     q, d, s = Q8.quantize_q8_1(x)
-    y, _ = Q8.gemv_affine_u4_q8(codes, scales, biases, q, d, s, gs)
-    y_bf16, _ = G.gemv_affine(codes, scales, biases, x, 4, gs)
-    w_abs = np.abs(G.dequant_affine(codes, scales, biases, k, 4, gs))
+    y, _ = _q8_matvec(bits)(codes, scales, biases, q, d, s, gs)
+    y_bf16, _ = G.gemv_affine(codes, scales, biases, x, bits, gs)
+    w_abs = np.abs(G.dequant_affine(codes, scales, biases, k, bits, gs))
     half_step = np.repeat(d.astype(np.float64), 32, axis=1) * (0.5 + 1e-5)
     bound = half_step @ w_abs.T
     assert np.all(np.abs(y - y_bf16) <= bound * (1 + 1e-9))
