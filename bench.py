@@ -79,8 +79,8 @@ def algorithmic_bytes(fmt, n, k, batch, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         w = q.qg_bytes_fp4(n, k, gs)
-    elif fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f"):
-        w = q.qg_bytes_affine(n, k, 8 if fmt == "u8" else 4, gs)
+    elif fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f", "u8q8", "u8q8f"):
+        w = q.qg_bytes_affine(n, k, 8 if fmt.startswith("u8") else 4, gs)
     else:
         w = q.qg_bytes_fp8(n, k)
     return w + batch * k * 2 + batch * n * 4
@@ -90,8 +90,8 @@ def quantize(fmt, w, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         return q.qg_quantize_fp4_e2m1(w, gs)
-    if fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f"):
-        return q.qg_quantize_affine(w, 8 if fmt == "u8" else 4, gs)
+    if fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f", "u8q8", "u8q8f"):
+        return q.qg_quantize_affine(w, 8 if fmt.startswith("u8") else 4, gs)
     return q.qg_quantize_fp8_e4m3_rowwise(w)
 
 
@@ -129,7 +129,7 @@ class Workload:
             self.host = None
         self.x = to_dev(self.x_host)
         self.y = torch.empty((batch, n), dtype=torch.float32, device="cuda:0")
-        if fmt in ("u4q8", "u4q8mv"):
+        if fmt in ("u4q8", "u4q8mv", "u8q8"):
             # int8 activation blocks: requantized every step ("u4q8", the whole
             # route) or once here ("u4q8mv", the matvec kernel alone)
             self.xq, self.ds = q.qg_quantize_q8_1(self.x)
@@ -145,6 +145,11 @@ class Workload:
             q.qgemv_affine_u8(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
         elif self.fmt == "u4q8f":
             q.qgemv_affine_u4_q8_fused(d[0], d[1], d[2], self.x, self.y, self.gs)
+        elif self.fmt == "u8q8f":
+            q.qgemv_affine_u8_q8_fused(d[0], d[1], d[2], self.x, self.y, self.gs)
+        elif self.fmt == "u8q8":
+            q.qg_quantize_q8_1(self.x, self.xq, self.ds)
+            q.qgemv_affine_u8_q8(d[0], d[1], d[2], self.xq, self.ds, self.y, self.gs)
         elif self.fmt in ("u4q8", "u4q8mv"):
             if self.fmt == "u4q8":
                 q.qg_quantize_q8_1(self.x, self.xq, self.ds)
@@ -300,6 +305,12 @@ SWEEP = [
     # quantization inside the matvec (one launch)
     ("u4q8f", "mlp_up", 1, 64), ("u4q8f", "mlp_down", 1, 64), ("u4q8f", "llama_up", 1, 64),
     ("u4q8f", "llama_down", 1, 64), ("u4q8f", "mlp_up", 4, 64), ("u4q8f", "mlp_down", 4, 64),
+    # the int8 route for 8-bit codes beside the bf16 route (which cannot
+    # stage 3840x15360's x at batch 4: fp32 activations exceed its LDS limit)
+    ("u8", "mlp_up", 4, 64),
+    ("u8q8", "mlp_up", 1, 64), ("u8q8", "mlp_down", 1, 64), ("u8q8", "mlp_up", 4, 64), ("u8q8", "mlp_down", 4, 64),
+    ("u8q8f", "mlp_up", 1, 64), ("u8q8f", "mlp_down", 1, 64), ("u8q8f", "mlp_up", 4, 64),
+    ("u8q8f", "mlp_down", 4, 64),
 ]
 
 

@@ -26,7 +26,8 @@ qg_plan = _b.qg_plan
 
 __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
-    "qg_quantize_q8_1", "qgemv_affine_u4_q8", "qgemv_affine_u4_q8_fused",
+    "qg_quantize_q8_1", "qgemv_affine_u4_q8", "qgemv_affine_u4_q8_fused", "qgemv_affine_u8_q8",
+    "qgemv_affine_u8_q8_fused",
     "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
@@ -240,9 +241,7 @@ def qg_quantize_q8_1(x, xq=None, ds=None, stream=None):
     return xq, ds
 
 
-def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=None):
-    """Affine u4 weights against int8 activation blocks from qg_quantize_q8_1:
-    y[b, n] = sum_blk scale * d * sum(u * q) + bias * s."""
+def _affine_q8(name, bits, codes, scales, biases, xq, ds, y, group_size, stream):
     torch = _torch()
     cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
     sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
@@ -253,7 +252,7 @@ def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=N
     n = codes.shape[0]
     batch = 1 if xq.dim() == 1 else xq.shape[0]
     k = xq.shape[-1]
-    if codes.shape[1] * 8 != k or tuple(scales.shape) != (n, k // group_size) \
+    if codes.shape[1] * (32 // bits) != k or tuple(scales.shape) != (n, k // group_size) \
             or tuple(biases.shape) != tuple(scales.shape) or ds.numel() != batch * (k // 32) * 2:
         raise ValueError("shapes: codes %s, scales %s, biases %s, xq %s, ds %s, group_size=%d"
                          % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), tuple(xq.shape),
@@ -262,27 +261,47 @@ def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=N
         raise ValueError("y must be [batch=%d, n=%d], got %s" % (batch, n, tuple(y.shape)))
     out = _b.QG_OUT_F32 if y.dtype == torch.float32 else _b.QG_OUT_BF16
     _same_device(codes, scales, biases, xq, ds, y)
-    _check(_lib.qgemv_affine_u4_q8(cp, sp, bp, qp, dp, yp, n, k, int(group_size), batch, out,
-                                   _stream(stream, y.device)), "qgemv_affine_u4_q8")
+    _check(getattr(_lib, name)(cp, sp, bp, qp, dp, yp, n, k, int(group_size), batch, out,
+                               _stream(stream, y.device)), name)
     return y
 
 
-def qgemv_affine_u4_q8_fused(codes, scales, biases, x, y, group_size=64, stream=None):
-    """qg_quantize_q8_1 then qgemv_affine_u4_q8 in one launch (bitwise the same y)."""
+def _affine_q8_fused(name, bits, codes, scales, biases, x, y, group_size, stream):
     torch = _torch()
     cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
     sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
     bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
     n = codes.shape[0]
     xp, yp, batch, k, out = _x_y(x, y, n)
-    if codes.shape[1] * 8 != k or tuple(scales.shape) != (n, k // group_size) \
+    if codes.shape[1] * (32 // bits) != k or tuple(scales.shape) != (n, k // group_size) \
             or tuple(biases.shape) != tuple(scales.shape):
         raise ValueError("shapes: codes %s, scales %s, biases %s, k=%d, group_size=%d"
                          % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), k, group_size))
     _same_device(codes, scales, biases, x, y)
-    _check(_lib.qgemv_affine_u4_q8_fused(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out,
-                                         _stream(stream, y.device)), "qgemv_affine_u4_q8_fused")
+    _check(getattr(_lib, name)(cp, sp, bp, xp, yp, n, k, int(group_size), batch, out,
+                               _stream(stream, y.device)), name)
     return y
+
+
+def qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=None):
+    """Affine u4 weights against int8 activation blocks from qg_quantize_q8_1:
+    y[b, n] = sum_blk scale * d * sum(u * q) + bias * s."""
+    return _affine_q8("qgemv_affine_u4_q8", 4, codes, scales, biases, xq, ds, y, group_size, stream)
+
+
+def qgemv_affine_u4_q8_fused(codes, scales, biases, x, y, group_size=64, stream=None):
+    """qg_quantize_q8_1 then qgemv_affine_u4_q8 in one launch (bitwise the same y)."""
+    return _affine_q8_fused("qgemv_affine_u4_q8_fused", 4, codes, scales, biases, x, y, group_size, stream)
+
+
+def qgemv_affine_u8_q8(codes, scales, biases, xq, ds, y, group_size=64, stream=None):
+    """As qgemv_affine_u4_q8 for 8-bit codes, u32 low-first [n, k/4]."""
+    return _affine_q8("qgemv_affine_u8_q8", 8, codes, scales, biases, xq, ds, y, group_size, stream)
+
+
+def qgemv_affine_u8_q8_fused(codes, scales, biases, x, y, group_size=64, stream=None):
+    """qg_quantize_q8_1 then qgemv_affine_u8_q8 in one launch (bitwise the same y)."""
+    return _affine_q8_fused("qgemv_affine_u8_q8_fused", 8, codes, scales, biases, x, y, group_size, stream)
 
 
 def qgemv_affine_u8(codes, scales, biases, x, y, group_size=64, plan=None, stream=None):

@@ -60,6 +60,8 @@ SIGNATURES = {
     "qg_quantize_q8_1": (_st, [_p, _i64, _i32, _p, _p, _p]),
     "qgemv_affine_u4_q8": (_st, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qgemv_affine_u4_q8_fused": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
+    "qgemv_affine_u8_q8": (_st, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
+    "qgemv_affine_u8_q8_fused": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qg_plan_query": (_st, [_i32, _i64, _i64, _i32, _p]),
     "qg_stream_probe": (_st, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "qg_status_string": (ctypes.c_char_p, [_st]),

@@ -118,16 +118,34 @@ __device__ __forceinline__ int dot_u4_i8(const uint4 q, const uint4 (&xp)[2]) {
     return acc;
 }
 
+// Integer dot of one 16-byte piece of 8-bit codes (half a block; word i:
+// columns 4i..4i+3 of the piece, one byte each) with the matching 16
+// activation codes in natural order.  Flipping a byte's top bit turns code c
+// into the signed byte c - 128; the caller adds 128 * scale * s back.
+__device__ __forceinline__ int dot_u8_i8(const uint4 q, const uint4 xp) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    const uint32_t x[4] = {xp.x, xp.y, xp.z, xp.w};
+    int acc = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(int(w[i] ^ 0x80808080u), int(x[i]), acc, false);
+    return acc;
+}
+
 __host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks) {
     return batch * chunks * (2 * 16 + 8);
 }
 
 // Waves take contiguous row ranges (wave_rows); a step is one pass of 64
-// chunks over an R-row tile, D steps in flight.  The workgroup first stages
-// every batch row's codes (regrouped) and {d, s} pairs in LDS, piece-major so
-// that consecutive lanes read consecutive 16 bytes.
-template <int R, int B, int D, bool kFuse>
-__global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const Q8Args a) {
+// 16-byte code pieces (one per lane, so every load is contiguous) over an
+// R-row tile, D steps in flight.  Bits is the code width, 4 or 8: a block of
+// 32 weights is one piece or two, and with two the lanes of a pair share the
+// block's {d, s} and only the first adds the bias term.  The workgroup first
+// stages every batch row's activation codes (for 4-bit weights regrouped into
+// even and odd columns) and {d, s} pairs in LDS, piece-major so that
+// consecutive lanes read consecutive 16 bytes.
+template <int Bits, int R, int B, int D, bool kFuse>
+__global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, const Q8Args a) {
+    constexpr int PPB = Bits / 4;            // 16-byte code pieces per block
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     struct Buf {
         uint4 c[R];
@@ -144,18 +162,18 @@ __global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const 
     const int passes = p.passes;
     const int steps = tiles * passes;
     const int64_t row_hi = r_end > r_begin ? r_end - 1 : min(r_begin, p.n - 1);
-    const int last_chunk = chunks - 1;
+    const int pieces = chunks * PPB;         // code pieces per row
 
     auto issue = [&](Buf &bf, int s) {
         const int t = s / passes;
         const int j = s - t * passes;
-        const int c = min(lane + kWave * j, last_chunk);
+        const int pc = min(lane + kWave * j, pieces - 1);
         const int64_t row0 = r_begin + int64_t(t) * R;
-        const int g = c >> p.group_shift;
+        const int g = (pc / PPB) >> p.group_shift;
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int64_t row = min(row0 + i, row_hi);
-            bf.c[i] = load_code_chunk(p.codes + row * p.row_bytes + uint32_t(c) * kChunkBytes);
+            bf.c[i] = load_code_chunk(p.codes + row * p.row_bytes + uint32_t(pc) * kChunkBytes);
             bf.s[i] = load_param(p.scales + row * p.groups + g);
             bf.b[i] = load_param(p.biases + row * p.groups + g);
         }
@@ -184,7 +202,7 @@ __global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const 
                 const int b = u / upr;
                 const int e = u - b * upr;           // 8-column unit in the row
                 const int c = e >> 2, h = e & 3;     // chunk, 8-column group in it
-                const uint2 eo = even_odd(packed[0], packed[1]);
+                const uint2 eo = Bits == 4 ? even_odd(packed[0], packed[1]) : make_uint2(packed[0], packed[1]);
                 reinterpret_cast<uint2 *>(&xl[(b * 2 + (h >> 1)) * chunks + c])[h & 1] = eo;
                 if (h == 0) dl[b * chunks + c] = make_float2(d, sv);
             }
@@ -229,8 +247,12 @@ __global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const 
             if (u < x_units) {
                 const int b = u / units_per_row;
                 const int e = u - b * units_per_row;
-                const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
-                xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+                if constexpr (Bits == 4) {
+                    const uint2 e0 = even_odd(v.x, v.y), e1 = even_odd(v.z, v.w);
+                    xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = make_uint4(e0.x, e0.y, e1.x, e1.y);
+                } else {
+                    xl[(b * 2 + (e & 1)) * chunks + (e >> 1)] = v;
+                }
             }
         };
         uint4 xv[kSU];
@@ -275,25 +297,36 @@ __global__ void __launch_bounds__(512) qgemv_u4_q8_kernel(const Params p, const 
     auto consume = [&](const Buf &bf, int s) {
         const int t = s / passes;
         const int j = s - t * passes;
-        const int c = lane + kWave * j;
+        const int pc = lane + kWave * j;
         const int64_t row0 = r_begin + int64_t(t) * R;
-        if (c < chunks) {
+        if (pc < pieces) {
+            const int c = pc / PPB, h = pc % PPB;    // block, half of it
             uint4 xp[B][2];
             float2 dsv[B];
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                xp[b][0] = xl[(b * 2) * chunks + c];
-                xp[b][1] = xl[(b * 2 + 1) * chunks + c];
+                if constexpr (Bits == 4) {
+                    xp[b][0] = xl[(b * 2) * chunks + c];
+                    xp[b][1] = xl[(b * 2 + 1) * chunks + c];
+                } else {
+                    xp[b][0] = xl[(b * 2 + h) * chunks + c];
+                }
                 dsv[b] = dl[b * chunks + c];
             }
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 if (row0 + i < r_end) {
                     const float sc = bf16_to_f32(bf.s[i]);
-                    const float bi = bf16_to_f32(bf.b[i]);
+                    // 8-bit codes enter the dot as c - 128: the bias takes
+                    // 128 * scale, once per block (on its first half)
+                    const float bi = Bits == 4 ? bf16_to_f32(bf.b[i])
+                                               : (h == 0 ? fmaf(128.0f, sc, bf16_to_f32(bf.b[i])) : 0.0f);
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
-                        const float t_ = dsv[b].x * float(dot_u4_i8(bf.c[i], xp[b]));
+                        int idot;
+                        if constexpr (Bits == 4) idot = dot_u4_i8(bf.c[i], xp[b]);
+                        else idot = dot_u8_i8(bf.c[i], xp[b][0]);
+                        const float t_ = dsv[b].x * float(idot);
                         acc[i][b] = fmaf(bi, dsv[b].y, fmaf(sc, t_, acc[i][b]));
                     }
                 }
@@ -341,10 +374,10 @@ qg_status q8_cus(int *cus) {
     return QG_OK;
 }
 
-template <int R, int B, bool kFuse>
+template <int Bits, int R, int B, bool kFuse>
 qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int waves, int64_t lds,
                     hipStream_t stream) {
-    auto kern = qg::qgemv_u4_q8_kernel<R, B, q8_depth(R), kFuse>;
+    auto kern = qg::qgemv_affine_q8_kernel<Bits, R, B, q8_depth(R), kFuse>;
     if (lds > 64 * 1024) {
         static std::once_flag once;
         static hipError_t err = hipSuccess;
@@ -358,11 +391,37 @@ qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int wa
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
-// Validation (complete before any HIP call) and launch of the matvec; the
-// activation side (a) is checked by the entry points.
-qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const qg::Q8Args &a,
-                 void *y, int64_t n, int64_t k, int32_t group_size, int32_t batch, qg_out_dtype out_dtype,
-                 hipStream_t stream) {
+// The instance for a code width, batch size, tile shape and activation side
+// (4-row tiles at batch 3-4 where every wave has at least 4 rows).
+template <int Bits>
+qg_status dispatch_q8(const qg::Params &p, const qg::Q8Args &a, int32_t batch, bool wide, int nb, int waves,
+                      int64_t lds, hipStream_t stream) {
+    if (a.x) {
+        switch (batch) {
+            case 1: return launch_q8<Bits, 2, 1, true>(p, a, nb, waves, lds, stream);
+            case 2: return launch_q8<Bits, 2, 2, true>(p, a, nb, waves, lds, stream);
+            case 3: return wide ? launch_q8<Bits, 4, 3, true>(p, a, nb, waves, lds, stream)
+                                : launch_q8<Bits, 2, 3, true>(p, a, nb, waves, lds, stream);
+            default: return wide ? launch_q8<Bits, 4, 4, true>(p, a, nb, waves, lds, stream)
+                                 : launch_q8<Bits, 2, 4, true>(p, a, nb, waves, lds, stream);
+        }
+    }
+    switch (batch) {
+        case 1: return launch_q8<Bits, 2, 1, false>(p, a, nb, waves, lds, stream);
+        case 2: return launch_q8<Bits, 2, 2, false>(p, a, nb, waves, lds, stream);
+        case 3: return wide ? launch_q8<Bits, 4, 3, false>(p, a, nb, waves, lds, stream)
+                            : launch_q8<Bits, 2, 3, false>(p, a, nb, waves, lds, stream);
+        default: return wide ? launch_q8<Bits, 4, 4, false>(p, a, nb, waves, lds, stream)
+                             : launch_q8<Bits, 2, 4, false>(p, a, nb, waves, lds, stream);
+    }
+}
+
+// Validation (complete before any HIP call) and launch of the matvec for
+// affine codes of `bits` bits; the activation side (a) is checked by the
+// entry points.
+qg_status run_q8(int bits, const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                 const qg::Q8Args &a, void *y, int64_t n, int64_t k, int32_t group_size, int32_t batch,
+                 qg_out_dtype out_dtype, hipStream_t stream) {
     if (!codes || !scales || !biases || !y) return QG_ERR_NULL_POINTER;
     if (n < 1 || k < 1 || k % qg::kQ8Block) return QG_ERR_BAD_SHAPE;
     if (n > (int64_t(1) << 31) || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
@@ -386,10 +445,10 @@ qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *
     p.biases = biases;
     p.y = y;
     p.n = n;
-    p.row_bytes = k / 2;
+    p.row_bytes = k * bits / 8;
     p.k = int32_t(k);
     p.chunks = int32_t(chunks);
-    p.passes = int32_t((chunks + qg::kWave - 1) / qg::kWave);
+    p.passes = int32_t((chunks * (bits / 4) + qg::kWave - 1) / qg::kWave);   // 16-byte code pieces per lane
     p.groups = int32_t(k / group_size);
     int shift = 0;
     while ((qg::kQ8Block << shift) < group_size) ++shift;
@@ -403,24 +462,8 @@ qg_status run_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *
     p.total_waves = int32_t(blocks * waves);
     const int nb = int(blocks);
     const bool wide = batch >= 3 && n >= int64_t(4) * p.total_waves;
-    if (a.x) {
-        switch (batch) {
-            case 1: return launch_q8<2, 1, true>(p, a, nb, waves, lds, stream);
-            case 2: return launch_q8<2, 2, true>(p, a, nb, waves, lds, stream);
-            case 3: return wide ? launch_q8<4, 3, true>(p, a, nb, waves, lds, stream)
-                                : launch_q8<2, 3, true>(p, a, nb, waves, lds, stream);
-            default: return wide ? launch_q8<4, 4, true>(p, a, nb, waves, lds, stream)
-                                 : launch_q8<2, 4, true>(p, a, nb, waves, lds, stream);
-        }
-    }
-    switch (batch) {
-        case 1: return launch_q8<2, 1, false>(p, a, nb, waves, lds, stream);
-        case 2: return launch_q8<2, 2, false>(p, a, nb, waves, lds, stream);
-        case 3: return wide ? launch_q8<4, 3, false>(p, a, nb, waves, lds, stream)
-                            : launch_q8<2, 3, false>(p, a, nb, waves, lds, stream);
-        default: return wide ? launch_q8<4, 4, false>(p, a, nb, waves, lds, stream)
-                             : launch_q8<2, 4, false>(p, a, nb, waves, lds, stream);
-    }
+    return bits == 4 ? dispatch_q8<4>(p, a, batch, wide, nb, waves, lds, stream)
+                     : dispatch_q8<8>(p, a, batch, wide, nb, waves, lds, stream);
 }
 
 }  // namespace
@@ -444,7 +487,7 @@ qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, cons
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     if (!xq || !ds) return QG_ERR_NULL_POINTER;
     if (!aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
-    return run_q8(codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
+    return run_q8(4, codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
                   stream);
 }
 
@@ -453,8 +496,26 @@ qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales
                                    int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     if (!x) return QG_ERR_NULL_POINTER;
     if (!aligned_to(x, 16)) return QG_ERR_MISALIGNED;
-    return run_q8(codes, scales, biases, qg::Q8Args{nullptr, nullptr, x}, y, n, k, group_size, batch, out_dtype,
+    return run_q8(4, codes, scales, biases, qg::Q8Args{nullptr, nullptr, x}, y, n, k, group_size, batch,
+                  out_dtype, stream);
+}
+
+qg_status qgemv_affine_u8_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    if (!xq || !ds) return QG_ERR_NULL_POINTER;
+    if (!aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    return run_q8(8, codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
                   stream);
+}
+
+qg_status qgemv_affine_u8_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                   const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                                   int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    if (!x) return QG_ERR_NULL_POINTER;
+    if (!aligned_to(x, 16)) return QG_ERR_MISALIGNED;
+    return run_q8(8, codes, scales, biases, qg::Q8Args{nullptr, nullptr, x}, y, n, k, group_size, batch,
+                  out_dtype, stream);
 }
 
 }  // extern "C"

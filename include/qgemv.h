@@ -288,7 +288,7 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
                          int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Int8 activation route for affine 4-bit weights.
+ * Int8 activation route for affine 4-bit and 8-bit weights.
  *
  * The SharpInference issue ("generalize Gemma 4 batched prefill ..."),
  * "Item C2", quantizes the activation to int8 blocks that carry a pair
@@ -329,6 +329,13 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   followed by qgemv_affine_u4_q8 returns.
  *   x       bf16 [batch, k] (DEVICE), 16-byte aligned, finite
  *   other arguments, checks and errors as for qgemv_affine_u4_q8.
+ * qgemv_affine_u8_q8, qgemv_affine_u8_q8_fused: the same for the 8-bit
+ *   codes of qgemv_affine_u8 (codes uint32 [n, k/4], code j of a word in
+ *   bits [8j, 8j+8)).  One block is two 16-byte chunks of codes; a code c
+ *   enters the 4-wide dot as the signed byte c - 128 (its top bit flipped)
+ *   and the block adds 128 * scale * s back with the bias, so that
+ *   y[b, r] = sum over blocks of scale*d*sum(c*q) + bias*s as for u4 (up to
+ *   the fp32 rounding of s).
  * None of these calls allocates device memory; all are asynchronous on
  * `stream`. */
 qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
@@ -337,6 +344,12 @@ qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, cons
                              const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                                   const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
+                                   int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
+qg_status qgemv_affine_u8_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
+                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
+qg_status qgemv_affine_u8_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                                    const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
                                    int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 

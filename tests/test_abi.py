@@ -206,3 +206,21 @@ def test_int8_quantize_validation():
     assert fn(A3, 0, 1, A3, A4, None) == SHAPE
     assert fn(A3, 64, 0, A3, A4, None) == BATCH
     assert fn(A3, 64, 1, ODD, A4, None) == MIS
+
+
+@pytest.mark.parametrize("name", ["qgemv_affine_u8_q8", "qgemv_affine_u8_q8_fused"])
+def test_int8_route_u8_validation(name):
+    fn = getattr(LIB, name)
+    if name.endswith("fused"):
+        call = lambda **kw: fn(kw.get("codes", A), A2, A2, kw.get("x", A3), A4, 8, kw.get("k", 128),   # noqa: E731
+                               kw.get("gs", 64), kw.get("b", 1), 0, None)
+    else:
+        call = lambda **kw: fn(kw.get("codes", A), A2, A2, kw.get("x", A3), A4, A4, 8, kw.get("k", 128),  # noqa: E731
+                               kw.get("gs", 64), kw.get("b", 1), 0, None)
+    assert call(codes=None) == NULL
+    assert call(x=None) == NULL
+    assert call(k=48) == SHAPE
+    assert call(gs=16) == GROUP
+    assert call(b=5) == BATCH
+    assert call(codes=ODD) == MIS
+    assert call(k=1 << 17) == LARGE

@@ -1,5 +1,6 @@
-"""The int8 activation route for affine 4-bit weights on the GPU, through the
-C ABI (qg_quantize_q8_1, qgemv_affine_u4_q8), against oracle.q8.
+"""The int8 activation route for affine 4-bit and 8-bit weights on the GPU,
+through the C ABI (qg_quantize_q8_1, qgemv_affine_u{4,8}_q8 and their fused
+forms), against oracle.q8.
 
 * The quantizer's codes and {d, s} pairs are integer or fp32 decisions taken
   with correctly rounded fp32 operations on both sides: compared bit for bit.
@@ -64,14 +65,20 @@ def test_quantize_bitwise(batch, k):
     assert np.array_equal(ds[..., 1], s_ref)
 
 
-def _weights(seed, n, k, gs):
+def _weights(seed, n, k, gs, bits=4):
     w = synth.weights(300 + seed, n, k)
-    return Q.quantize_affine(w, 4, gs)
+    return Q.quantize_affine(w, bits, gs)
 
 
-def _matvec(arrays, xq, ds, n, gs, bf16=False):
+def _fns(bits):
+    if bits == 4:
+        return q.qgemv_affine_u4_q8, q.qgemv_affine_u4_q8_fused
+    return q.qgemv_affine_u8_q8, q.qgemv_affine_u8_q8_fused
+
+
+def _matvec(arrays, xq, ds, n, gs, bf16=False, bits=4):
     y = out_tensor(xq.shape[0], n, bf16)
-    q.qgemv_affine_u4_q8(dev(arrays[0]), dev(arrays[1]), dev(arrays[2]), dev(xq), dev(ds), y, gs)
+    _fns(bits)[0](dev(arrays[0]), dev(arrays[1]), dev(arrays[2]), dev(xq), dev(ds), y, gs)
     return host_y(y)
 
 
@@ -81,17 +88,18 @@ def _matvec(arrays, xq, ds, n, gs, bf16=False):
     # at least 4 rows per wave: batch 3-4 take 4-row tiles (8200, 9001: ragged)
     (8200, 512, 64, 3), (9001, 256, 32, 4),
 ])
-def test_matvec_parity(n, k, gs, batch):
-    log("q8 matvec n=%d k=%d gs=%d batch=%d" % (n, k, gs, batch))
-    arrays = _weights(n + k, n, k, gs)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matvec_parity(bits, n, k, gs, batch):
+    log("q8 matvec u%d n=%d k=%d gs=%d batch=%d" % (bits, n, k, gs, batch))
+    arrays = _weights(n + k, n, k, gs, bits)
     x = _x_blocks(2, batch, k)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
     ds = np.stack([d_ref, s_ref], axis=-1).astype(np.float32)
-    y = _matvec(arrays, q_ref, ds, n, gs)
-    y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
-    parity.assert_parity(y, y_ref, a_ref, "u4 q8 n=%d k=%d" % (n, k))
+    y = _matvec(arrays, q_ref, ds, n, gs, bits=bits)
+    y_ref, a_ref = Q8.gemv_affine_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, bits, gs)
+    parity.assert_parity(y, y_ref, a_ref, "u%d q8 n=%d k=%d" % (bits, n, k))
     # bf16 output is the rounding of the same sums
-    yb = _matvec(arrays, q_ref, ds, n, gs, bf16=True)
+    yb = _matvec(arrays, q_ref, ds, n, gs, bf16=True, bits=bits)
     yf = torch.from_numpy(y).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(yb, yf)
 
@@ -117,40 +125,44 @@ def test_end_to_end_equals_oracle_blocks():
     (1, 32, 32, 1), (37, 128, 64, 2), (513, 3840, 64, 4), (129, 4096, 128, 3), (300, 15360, 64, 1),
     (64, 15360, 32, 4), (1000, 8192, 64, 1), (8200, 512, 64, 3), (9001, 1024, 128, 4),
 ])
-def test_fused_equals_separate_bitwise(n, k, gs, batch):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_fused_equals_separate_bitwise(bits, n, k, gs, batch):
     """The in-kernel quantization stages the same blocks as qg_quantize_q8_1,
     so the fused call returns the two-launch result bit for bit."""
-    log("q8 fused n=%d k=%d gs=%d batch=%d" % (n, k, gs, batch))
-    arrays = _weights(7 * n + k, n, k, gs)
+    log("q8 fused u%d n=%d k=%d gs=%d batch=%d" % (bits, n, k, gs, batch))
+    arrays = _weights(7 * n + k, n, k, gs, bits)
+    sep, fused = _fns(bits)
     x = _x_blocks(5, batch, k)
     dargs = [dev(a) for a in arrays]
     xd = dev(x)
     xq, ds = q.qg_quantize_q8_1(xd)
     y_sep = out_tensor(batch, n)
-    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y_sep, gs)
+    sep(dargs[0], dargs[1], dargs[2], xq, ds, y_sep, gs)
     y_fused = out_tensor(batch, n)
-    q.qgemv_affine_u4_q8_fused(dargs[0], dargs[1], dargs[2], xd, y_fused, gs)
+    fused(dargs[0], dargs[1], dargs[2], xd, y_fused, gs)
     a, b = host_y(y_sep), host_y(y_fused)
     assert np.array_equal(a, b)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
-    parity.assert_parity(b, y_ref, a_ref, "u4 q8 fused n=%d k=%d" % (n, k))
+    y_ref, a_ref = Q8.gemv_affine_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, bits, gs)
+    parity.assert_parity(b, y_ref, a_ref, "u%d q8 fused n=%d k=%d" % (bits, n, k))
 
 
-def test_all_codes_and_zero_blocks():
-    """Uniform random code words (every nibble value) and an activation with
+@pytest.mark.parametrize("bits", [4, 8])
+def test_all_codes_and_zero_blocks(bits):
+    """Uniform random code words (every code value) and an activation with
     all-zero blocks: the zero blocks add nothing, bias terms included."""
     n, k, gs = 96, 1024, 64
-    log("q8 uniform codes n=%d k=%d" % (n, k))
-    codes = synth.uniform_words((n, k // 8), 21)
+    log("q8 uniform codes u%d n=%d k=%d" % (bits, n, k))
+    codes = synth.uniform_words((n, k * bits // 32), 21)
     scales = synth.uniform_bf16((n, k // gs), -0.05, 0.05, 22)
     biases = synth.uniform_bf16((n, k // gs), -0.05, 0.05, 23)
     x = _x_blocks(4, 2, k)
     x[1, :] = 0
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    y = _matvec((codes, scales, biases), q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs)
-    y_ref, a_ref = Q8.gemv_affine_u4_q8(codes, scales, biases, q_ref, d_ref, s_ref, gs)
-    parity.assert_parity(y, y_ref, a_ref, "u4 q8 uniform codes")
+    y = _matvec((codes, scales, biases), q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs,
+                bits=bits)
+    y_ref, a_ref = Q8.gemv_affine_q8(codes, scales, biases, q_ref, d_ref, s_ref, bits, gs)
+    parity.assert_parity(y, y_ref, a_ref, "u%d q8 uniform codes" % bits)
     assert np.all(y[1] == 0)
 
 
@@ -173,7 +185,11 @@ def test_errors_leave_y_untouched():
     assert lib.qgemv_affine_u4_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
                                   n, 65536 * 2, gs, 1, 0, s) != 0                # beyond the LDS staging
     assert lib.qg_quantize_q8_1(p(xq), 48, 1, p(xq), p(ds), s) != 0
+    assert lib.qgemv_affine_u8_q8(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xq), p(ds), p(y),
+                                  n, k, gs, 5, 0, s) != 0                        # batch 5
     xb = torch.zeros((1, k), dtype=torch.bfloat16, device="cuda:0")
+    assert lib.qgemv_affine_u8_q8_fused(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xb), p(y),
+                                        n, 48, gs, 1, 0, s) != 0                 # k not a block multiple
     assert lib.qgemv_affine_u4_q8_fused(p(arrays[0]), p(arrays[1]), p(arrays[2]), p(xb), p(y),
                                         n, k, gs, 0, 0, s) != 0                  # batch 0
     assert lib.qgemv_affine_u4_q8_fused(p(arrays[0]), p(arrays[1]), p(arrays[2]), None, p(y),
@@ -184,28 +200,30 @@ def test_errors_leave_y_untouched():
 
 @pytest.mark.parametrize("batch", [1, 4])
 @pytest.mark.parametrize("name", ["mlp_up", "mlp_down"])
-def test_full_size_sampled(name, batch):
+@pytest.mark.parametrize("bits", [4, 8])
+def test_full_size_sampled(bits, name, batch):
     sid, n, k = synth.shape(name)
     gs = 64
-    log("q8 full-size %s [%d x %d] batch=%d" % (name, n, k, batch))
+    log("q8 full-size u%d %s [%d x %d] batch=%d" % (bits, name, n, k, batch))
     w = synth.weights(sid, n, k)
-    arrays = q.qg_quantize_affine(w, 4, gs)
+    arrays = q.qg_quantize_affine(w, bits, gs)
+    sep = _fns(bits)[0]
     del w
     x = synth.activations(sid, batch, k)
     dargs = [dev(a) for a in arrays]
     xq, ds = q.qg_quantize_q8_1(dev(x))
     y = out_tensor(batch, n)
-    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y, gs)
+    sep(dargs[0], dargs[1], dargs[2], xq, ds, y, gs)
     y1 = host_y(y)
     y2t = out_tensor(batch, n)
-    q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y2t, gs)
+    sep(dargs[0], dargs[1], dargs[2], xq, ds, y2t, gs)
     y2 = host_y(y2t)
     assert np.isfinite(y1).all() and np.array_equal(y1, y2)
     rows = synth.sample_rows(n, 192, seed=sid)
-    ora = Q.quantize_affine(synth.weight_rows(sid, n, k, rows), 4, gs)
+    ora = Q.quantize_affine(synth.weight_rows(sid, n, k, rows), bits, gs)
     for a_lib, a_ora in zip(arrays, ora):
         assert np.array_equal(a_lib[rows], a_ora)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    y_ref, a_ref = Q8.gemv_affine_u4_q8(ora[0], ora[1], ora[2], q_ref, d_ref, s_ref, gs)
-    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "u4 q8 %s" % name)
-    log("q8 full-size %s: %r" % (name, r))
+    y_ref, a_ref = Q8.gemv_affine_q8(ora[0], ora[1], ora[2], q_ref, d_ref, s_ref, bits, gs)
+    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "u%d q8 %s" % (bits, name))
+    log("q8 full-size u%d %s: %r" % (bits, name, r))
