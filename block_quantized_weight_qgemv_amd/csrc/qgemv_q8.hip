@@ -1,8 +1,9 @@
-// The int8 activation route for affine 4-bit weights: the activation is
-// quantized in blocks of 32 to int8 codes with an fp32 pair {d, s}
-// (s = d * sum q), the weight nibbles are widened to int8 bytes and meet the
-// activation codes in 4-wide integer dots, and the affine bias is applied once
-// per block through s.
+// The int8 activation route for affine 4-bit and 8-bit weights: the
+// activation is quantized in blocks of 32 to int8 codes with an fp32 pair
+// {d, s} (s = d * sum q), the weight codes are widened to int8 bytes (4-bit:
+// nibble masks; 8-bit: c - 128 by flipping the top bit) and meet the
+// activation codes in 4-wide integer dots, and the affine bias is applied
+// once per block through s.
 //
 // Prior art, not the blueprint: "perf(cuda): generalize Gemma 4 batched
 // prefill + flash attn + decode graphs to dense Q4_K models", section
@@ -11,8 +12,9 @@
 // products and a 4-wide integer-dot matvec; here it is the matvec, on
 // gfx950's v_dot4_i32_i8.
 //
-// One 16-byte chunk of u4 codes is 32 weights, exactly one activation block,
-// so every chunk's fold is  acc += scale * (d * idot) + bias * s.
+// A block of 32 weights is one 16-byte chunk of 4-bit codes or two of 8-bit
+// codes, and its fold is  acc += scale * (d * idot) + bias * s  (8-bit:
+// bias + 128 * scale in place of bias).
 
 #include "qgemv.h"
 #include "qgemv_kernels.hpp"
