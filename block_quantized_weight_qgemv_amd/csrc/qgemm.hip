@@ -4,28 +4,16 @@
 
 #include "qgemv.h"
 #include "qgemm_kernels.hpp"
+#include "qgemv_device.hpp"
 
 #include <mutex>
 
 namespace {
 
-bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+using qgl::aligned_to;
 
-// compute units of the current device, read once per device
-constexpr int kMaxDevices = 64;
-std::once_flag g_cu_once[kMaxDevices];
-int g_cu_count[kMaxDevices];
-
-int device_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-    std::call_once(g_cu_once[dev], [dev] {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
-        g_cu_count[dev] = v;
-    });
-    return g_cu_count[dev];
-}
+// compute units of the current device (cached per device), 0 if unknown
+int device_cus() { return qgl::device_cu_count(); }
 
 }  // namespace
 

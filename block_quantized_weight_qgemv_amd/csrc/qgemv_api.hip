@@ -12,6 +12,7 @@
 #include "qgemv_kernels.hpp"
 #include "qgemv_fp8_mfma.hpp"
 #include "stream_probe.hpp"
+#include "qgemv_device.hpp"
 
 #include <atomic>
 #include <mutex>
@@ -48,7 +49,7 @@ int64_t lds_bytes(qg_format f, int64_t k, int32_t batch) {
            qg::kLdsSink;
 }
 
-bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool aligned(const void *p, uintptr_t a) { return qgl::aligned_to(p, a); }
 
 qg_status check_common(qg_format f, const void *codes, const void *x, const void *y, int64_t n,
                        int64_t k, int32_t batch, qg_out_dtype out) {
@@ -82,19 +83,10 @@ int log2i(int v) {
 
 // ---------------------------------------------------------------- device info
 
-std::once_flag g_cu_once[kMaxDevices];
-int g_cu_count[kMaxDevices];
-
 qg_status device_cus(int *cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return QG_ERR_DEVICE;
-    std::call_once(g_cu_once[dev], [dev] {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
-        g_cu_count[dev] = v;
-    });
-    if (g_cu_count[dev] <= 0) return QG_ERR_DEVICE;
-    *cus = g_cu_count[dev];
+    const int v = qgl::device_cu_count();
+    if (v <= 0) return QG_ERR_DEVICE;
+    *cus = v;
     return QG_OK;
 }
 
@@ -411,6 +403,26 @@ qg_status fp8_entry(const uint8_t *codes, const float *row_scale, const uint16_t
 }
 
 }  // namespace
+
+namespace qgl {
+
+namespace {
+std::once_flag g_cu_once[kMaxDevices];
+int g_cu_count[kMaxDevices];
+}  // namespace
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    std::call_once(g_cu_once[dev], [dev] {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
+        g_cu_count[dev] = v;
+    });
+    return g_cu_count[dev];
+}
+
+}  // namespace qgl
 
 extern "C" {
 

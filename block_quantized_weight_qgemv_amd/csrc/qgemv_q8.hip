@@ -18,6 +18,7 @@
 
 #include "qgemv.h"
 #include "qgemv_kernels.hpp"
+#include "qgemv_device.hpp"
 
 #include <mutex>
 
@@ -359,20 +360,12 @@ constexpr int q8_depth(int r) { return 8 / r; }
 constexpr int64_t kQ8WideStage = 32 * 1024;
 constexpr int64_t kQ8WideStageHeavy = 16 * 1024;
 
-bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+using qgl::aligned_to;
 
 qg_status q8_cus(int *cus) {
-    static std::once_flag once[64];
-    static int count[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return QG_ERR_DEVICE;
-    std::call_once(once[dev], [dev] {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) v = 0;
-        count[dev] = v;
-    });
-    if (count[dev] <= 0) return QG_ERR_DEVICE;
-    *cus = count[dev];
+    const int v = qgl::device_cu_count();
+    if (v <= 0) return QG_ERR_DEVICE;
+    *cus = v;
     return QG_OK;
 }
 
