@@ -572,16 +572,19 @@ def run_summarize_pmc(args):
     """FETCH_SIZE and WRITE_SIZE per matvec launch, scaled by the counters of a
     plain copy of COPY_BYTES (read COPY_BYTES, wrote COPY_BYTES)."""
     fetch_dir, write_dir, copy_fetch_dir, copy_write_dir = args.summarize_pmc
-    k_fetch, n1 = _pmc_median(fetch_dir, "FETCH_SIZE", "qgemv")
-    k_write, n2 = _pmc_median(write_dir, "WRITE_SIZE", "qgemv")
+    k_fetch, n1 = _pmc_median(fetch_dir, "FETCH_SIZE", args.pmc_kernel)
+    k_write, n2 = _pmc_median(write_dir, "WRITE_SIZE", args.pmc_kernel)
     c_fetch, _ = _pmc_median(copy_fetch_dir, "FETCH_SIZE", "copyBuffer")
     c_write, _ = _pmc_median(copy_write_dir, "WRITE_SIZE", "copyBuffer")
     f_scale = COPY_BYTES / (c_fetch * 1024.0)
     w_scale = COPY_BYTES / (c_write * 1024.0)
     fetch_b = k_fetch * 1024.0 * f_scale
     write_b = k_write * 1024.0 * w_scale
+    default = args.pmc_workload == ""
     out = {
-        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)",
+        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)" if default
+        else args.pmc_workload,
+        "kernel": args.pmc_kernel,
         "kernel_source_sha256": kernel_source_hash(),
         "fetch_size_kib_median": k_fetch, "write_size_kib_median": k_write, "dispatches": [n1, n2],
         "copy_bytes": COPY_BYTES, "copy_fetch_size_kib": c_fetch, "copy_write_size_kib": c_write,
@@ -589,7 +592,8 @@ def run_summarize_pmc(args):
         "hbm_bytes_per_launch": int(round(fetch_b + write_b)),
         "hbm_read_bytes_per_launch": int(round(fetch_b)),
         "hbm_write_bytes_per_launch": int(round(write_b)),
-        "algorithmic_bytes_per_launch": algorithmic_bytes("fp4", 30720, 3840, 1, 32),
+        "algorithmic_bytes_per_launch": algorithmic_bytes("fp4", 30720, 3840, 1, 32) if default
+        else int(args.pmc_bytes),
         "commands": args.commands or "",
     }
     with open(args.out or TRAFFIC_FILE, "w") as f:
@@ -616,8 +620,11 @@ def run_summarize_busy(args):
     for c in BUSY_COUNTERS:
         med[c], n = _pmc_median(run_dir, c, "qgemv")
     gui_per_xcd = med["GRBM_GUI_ACTIVE"] / 8.0
+    default = args.pmc_workload == ""
     out = {
-        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)",
+        "workload": "FP4-E2M1 gate_up W[30720x3840] group 32, batch 1 (bench.py default)" if default
+        else args.pmc_workload,
+        "kernel": args.pmc_kernel,
         "kernel_source_sha256": kernel_source_hash(),
         "dispatches": n,
         "counters_median": med,
@@ -694,6 +701,9 @@ def main(argv=None):
                     help="stream probe at each sweep workload's byte count, beside the workload")
     ap.add_argument("--summarize-pmc", nargs=4, metavar="DIR",
                     help="fetch, write, copy-fetch and copy-write rocprofv3 --pmc output dirs")
+    ap.add_argument("--pmc-kernel", default="qgemv", help="with --summarize-pmc: kernel name substring")
+    ap.add_argument("--pmc-workload", default="", help="with --summarize-pmc: workload label (default: the bench line's)")
+    ap.add_argument("--pmc-bytes", default="0", help="with --summarize-pmc and --pmc-workload: algorithmic bytes")
     ap.add_argument("--summarize-trace", metavar="DIR", help="rocprofv3 --kernel-trace --stats output dir")
     ap.add_argument("--summarize-busy", metavar="DIR",
                     help="rocprofv3 --pmc output dir holding BUSY_COUNTERS (VALU and memory-unit busy)")
