@@ -305,6 +305,7 @@ SWEEP = [
     # quantization inside the matvec (one launch)
     ("u4q8f", "mlp_up", 1, 64), ("u4q8f", "mlp_down", 1, 64), ("u4q8f", "llama_up", 1, 64),
     ("u4q8f", "llama_down", 1, 64), ("u4q8f", "mlp_up", 4, 64), ("u4q8f", "mlp_down", 4, 64),
+    ("u4", "mlp_up", 2, 64), ("u4q8f", "mlp_up", 2, 64),
     # the int8 route for 8-bit codes beside the bf16 route (which cannot
     # stage 3840x15360's x at batch 4: fp32 activations exceed its LDS limit)
     ("u8", "mlp_up", 4, 64),

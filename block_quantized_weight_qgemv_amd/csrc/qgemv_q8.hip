@@ -350,7 +350,7 @@ namespace {
 constexpr int64_t kQ8MaxLds = 128 * 1024;
 // rows per tile and steps in flight per wave: 8 code chunks in flight per
 // lane either way; 4-row tiles halve the LDS activation reads per weight
-// where the batch is 3-4 and every wave has at least 4 rows
+// and are taken where every wave has at least 4 rows
 constexpr int q8_depth(int r) { return 8 / r; }
 // Eight waves per compute unit: two workgroups of four, or one workgroup of
 // eight where staging costs more than the second workgroup brings, so each CU
@@ -387,14 +387,16 @@ qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int wa
 }
 
 // The instance for a code width, batch size, tile shape and activation side
-// (4-row tiles at batch 3-4 where every wave has at least 4 rows).
+// (4-row tiles where every wave has at least 4 rows).
 template <int Bits>
 qg_status dispatch_q8(const qg::Params &p, const qg::Q8Args &a, int32_t batch, bool wide, int nb, int waves,
                       int64_t lds, hipStream_t stream) {
     if (a.x) {
         switch (batch) {
-            case 1: return launch_q8<Bits, 2, 1, true>(p, a, nb, waves, lds, stream);
-            case 2: return launch_q8<Bits, 2, 2, true>(p, a, nb, waves, lds, stream);
+            case 1: return wide ? launch_q8<Bits, 4, 1, true>(p, a, nb, waves, lds, stream)
+                                : launch_q8<Bits, 2, 1, true>(p, a, nb, waves, lds, stream);
+            case 2: return wide ? launch_q8<Bits, 4, 2, true>(p, a, nb, waves, lds, stream)
+                                : launch_q8<Bits, 2, 2, true>(p, a, nb, waves, lds, stream);
             case 3: return wide ? launch_q8<Bits, 4, 3, true>(p, a, nb, waves, lds, stream)
                                 : launch_q8<Bits, 2, 3, true>(p, a, nb, waves, lds, stream);
             default: return wide ? launch_q8<Bits, 4, 4, true>(p, a, nb, waves, lds, stream)
@@ -402,8 +404,10 @@ qg_status dispatch_q8(const qg::Params &p, const qg::Q8Args &a, int32_t batch, b
         }
     }
     switch (batch) {
-        case 1: return launch_q8<Bits, 2, 1, false>(p, a, nb, waves, lds, stream);
-        case 2: return launch_q8<Bits, 2, 2, false>(p, a, nb, waves, lds, stream);
+        case 1: return wide ? launch_q8<Bits, 4, 1, false>(p, a, nb, waves, lds, stream)
+                            : launch_q8<Bits, 2, 1, false>(p, a, nb, waves, lds, stream);
+        case 2: return wide ? launch_q8<Bits, 4, 2, false>(p, a, nb, waves, lds, stream)
+                            : launch_q8<Bits, 2, 2, false>(p, a, nb, waves, lds, stream);
         case 3: return wide ? launch_q8<Bits, 4, 3, false>(p, a, nb, waves, lds, stream)
                             : launch_q8<Bits, 2, 3, false>(p, a, nb, waves, lds, stream);
         default: return wide ? launch_q8<Bits, 4, 4, false>(p, a, nb, waves, lds, stream)
@@ -456,7 +460,7 @@ qg_status run_q8(int bits, const uint32_t *codes, const uint16_t *scales, const 
     if (blocks > max_blocks) blocks = max_blocks;
     p.total_waves = int32_t(blocks * waves);
     const int nb = int(blocks);
-    const bool wide = batch >= 3 && n >= int64_t(4) * p.total_waves;
+    const bool wide = n >= int64_t(4) * p.total_waves;
     return bits == 4 ? dispatch_q8<4>(p, a, batch, wide, nb, waves, lds, stream)
                      : dispatch_q8<8>(p, a, batch, wide, nb, waves, lds, stream);
 }

@@ -85,8 +85,8 @@ def _matvec(arrays, xq, ds, n, gs, bf16=False, bits=4):
 @pytest.mark.parametrize("n,k,gs,batch", [
     (1, 32, 32, 1), (37, 128, 64, 1), (250, 3840, 64, 4), (129, 4096, 128, 3),
     (300, 15360, 64, 2), (64, 15360, 32, 4), (1000, 512, 64, 1),
-    # at least 4 rows per wave: batch 3-4 take 4-row tiles (8200, 9001: ragged)
-    (8200, 512, 64, 3), (9001, 256, 32, 4),
+    # at least 4 rows per wave: 4-row tiles (8200, 9001: ragged)
+    (8200, 512, 64, 3), (9001, 256, 32, 4), (8200, 256, 64, 1), (9001, 512, 128, 2),
 ])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_matvec_parity(bits, n, k, gs, batch):
@@ -123,7 +123,8 @@ def test_end_to_end_equals_oracle_blocks():
 
 @pytest.mark.parametrize("n,k,gs,batch", [
     (1, 32, 32, 1), (37, 128, 64, 2), (513, 3840, 64, 4), (129, 4096, 128, 3), (300, 15360, 64, 1),
-    (64, 15360, 32, 4), (1000, 8192, 64, 1), (8200, 512, 64, 3), (9001, 1024, 128, 4),
+    (64, 15360, 32, 4), (1000, 8192, 64, 1), (8200, 512, 64, 3), (9001, 1024, 128, 4), (8200, 256, 32, 1),
+    (9001, 512, 64, 2),
 ])
 @pytest.mark.parametrize("bits", [4, 8])
 def test_fused_equals_separate_bitwise(bits, n, k, gs, batch):
