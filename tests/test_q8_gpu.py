@@ -228,3 +228,44 @@ def test_full_size_sampled(bits, name, batch):
     y_ref, a_ref = Q8.gemv_affine_q8(ora[0], ora[1], ora[2], q_ref, d_ref, s_ref, bits, gs)
     r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "u%d q8 %s" % (bits, name))
     log("q8 full-size u%d %s: %r" % (bits, name, r))
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_largest_staged_k(bits):
+    """batch 4 at the largest k whose int8 blocks fit the 128 KiB staging
+    (4 * k * 1.25 bytes: k = 26208 with groups of 32), plain and fused, and
+    the next block multiple is refused before any launch."""
+    n, k, gs, batch = 70, 26208, 32, 4
+    log("q8 largest k u%d n=%d k=%d batch=%d" % (bits, n, k, batch))
+    arrays = _weights(11 + bits, n, k, gs, bits)
+    x = _x_blocks(6, batch, k)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    y_ref, a_ref = Q8.gemv_affine_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, bits, gs)
+    sep, fused = _fns(bits)
+    dargs = [dev(a) for a in arrays]
+    y = out_tensor(batch, n)
+    sep(dargs[0], dargs[1], dargs[2], dev(q_ref), dev(np.stack([d_ref, s_ref], axis=-1).astype(np.float32)), y, gs)
+    parity.assert_parity(host_y(y), y_ref, a_ref, "u%d q8 largest k" % bits)
+    yf = out_tensor(batch, n)
+    fused(dargs[0], dargs[1], dargs[2], dev(x), yf, gs)
+    parity.assert_parity(host_y(yf), y_ref, a_ref, "u%d q8 fused largest k" % bits)
+    # k + 32 no longer fits: QG_ERR_TOO_LARGE, y untouched
+    k2 = k + 32
+    arrays2 = [dev(a) for a in _weights(12 + bits, n, k2, gs, bits)]
+    y2 = out_tensor(batch, n, fill=3.0)
+    with pytest.raises(q.QgError) as err:
+        fused(arrays2[0], arrays2[1], arrays2[2], dev(_x_blocks(7, batch, k2)), y2, gs)
+    assert err.value.status == 9
+    torch.cuda.synchronize()
+    assert torch.all(y2 == 3.0)
+
+
+def test_quantize_long_rows_bitwise():
+    """The standalone quantizer has no staging limit: 4 rows of 2^18."""
+    batch, k = 4, 1 << 18
+    log("q8 quantize long rows batch=%d k=%d" % (batch, k))
+    x = _x_blocks(8, batch, k)
+    xq, ds = _gpu_quantize(x)
+    q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
+    assert np.array_equal(xq, q_ref)
+    assert np.array_equal(ds[..., 0], d_ref) and np.array_equal(ds[..., 1], s_ref)
