@@ -331,7 +331,7 @@ def run_sweep(args):
         if only and name not in only and "%s:%s" % (fmt, name) not in only:
             continue
         wl = Workload(fmt, name, batch=batch, gs=gs, plan=parse_plan(args.plan))
-        steps = timed_steps(wl.launch, args.mode)
+        steps = args.sweep_steps or timed_steps(wl.launch, args.mode)
         ms = time_steps(wl.launch, steps, max(1, steps // 10), args.mode)
         us = ms / steps * 1e3
         gbs = wl.bytes / (us * 1e-6) / 1e9
@@ -619,7 +619,7 @@ def run_summarize_busy(args):
     run_dir = args.summarize_busy
     med = {}
     for c in BUSY_COUNTERS:
-        med[c], n = _pmc_median(run_dir, c, "qgemv")
+        med[c], n = _pmc_median(run_dir, c, args.pmc_kernel)
     gui_per_xcd = med["GRBM_GUI_ACTIVE"] / 8.0
     default = args.pmc_workload == ""
     out = {
@@ -695,6 +695,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--only", default="", help="with --sweep: comma list of shape names or fmt:shape")
+    ap.add_argument("--sweep-steps", type=int, default=0,
+                    help="with --sweep: this many timed steps per workload (default: about 25 ms of them)")
     ap.add_argument("--out", default="")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--probe", action="store_true", help="stream-probe read bandwidth sweep")

@@ -223,7 +223,7 @@ def qgemv_affine_u4(codes, scales, biases, x, y, group_size=64, plan=None, strea
 
 
 def qg_quantize_q8_1(x, xq=None, ds=None, stream=None):
-    """bf16 x [batch, k] -> (xq int8 [batch, k], ds float32 [batch, k/32, 2] = {d, s}) on x's device."""
+    """bf16 x [batch, k] -> (xq int8 [batch, k], ds fp16 bits int16 [batch, k/32, 2] = {d, s}) on x's device."""
     torch = _torch()
     xp = _dev_ptr(x, "x", (torch.bfloat16, torch.int16, torch.uint16), (1, 2))
     batch = 1 if x.dim() == 1 else x.shape[0]
@@ -231,9 +231,9 @@ def qg_quantize_q8_1(x, xq=None, ds=None, stream=None):
     if xq is None:
         xq = torch.empty((batch, k), dtype=torch.int8, device=x.device)
     if ds is None:
-        ds = torch.empty((batch, k // 32, 2), dtype=torch.float32, device=x.device)
+        ds = torch.empty((batch, k // 32, 2), dtype=torch.int16, device=x.device)
     qp = _dev_ptr(xq, "xq", (torch.int8,), (1, 2))
-    dp = _dev_ptr(ds, "ds", (torch.float32,), (2, 3))
+    dp = _dev_ptr(ds, "ds", (torch.int16, torch.uint16, torch.float16), (2, 3))
     if xq.numel() != batch * k or ds.numel() != batch * (k // 32) * 2:
         raise ValueError("xq must hold [batch=%d, k=%d], ds [batch, k/32, 2]" % (batch, k))
     _same_device(x, xq, ds)
@@ -247,7 +247,7 @@ def _affine_q8(name, bits, codes, scales, biases, xq, ds, y, group_size, stream)
     sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
     bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
     qp = _dev_ptr(xq, "xq", (torch.int8,), (1, 2))
-    dp = _dev_ptr(ds, "ds", (torch.float32,), (2, 3))
+    dp = _dev_ptr(ds, "ds", (torch.int16, torch.uint16, torch.float16), (2, 3))
     yp = _dev_ptr(y, "y", (torch.float32, torch.bfloat16), (1, 2))
     n = codes.shape[0]
     batch = 1 if xq.dim() == 1 else xq.shape[0]

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 # QG_ABI_VERSION of include/qgemv.h that these declarations follow; a
 # library that reports another version is refused at load.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 QG_OK = 0
 QG_OUT_F32 = 0

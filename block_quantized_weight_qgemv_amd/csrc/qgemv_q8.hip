@@ -1,16 +1,18 @@
 // The int8 activation route for affine 4-bit and 8-bit weights: the
-// activation is quantized in blocks of 32 to int8 codes with an fp32 pair
-// {d, s} (s = d * sum q), the weight codes are widened to int8 bytes (4-bit:
-// nibble masks; 8-bit: c - 128 by flipping the top bit) and meet the
-// activation codes in 4-wide integer dots, and the affine bias is applied
-// once per block through s.
+// activation is quantized in blocks of 32 to int8 codes with an fp16 pair
+// {d, s} in one 32-bit word (d in the low half, s = d * sum q in the high
+// half), the weight codes are widened to int8 bytes (4-bit: nibble masks;
+// 8-bit: c - 128 by flipping the top bit) and meet the activation codes in
+// 4-wide integer dots, and the affine bias is applied once per block
+// through s.
 //
 // Prior art, not the blueprint: "perf(cuda): generalize Gemma 4 batched
 // prefill + flash attn + decode graphs to dense Q4_K models", section
-// "Item C2" (int8 blocks carrying {d, s}, nibbles widened to int8, the min
-// term applied through the activation sum).  There it feeds int8 matrix
-// products and a 4-wide integer-dot matvec; here it is the matvec, on
-// gfx950's v_dot4_i32_i8.
+// "Item C2" (int8 q8_1 blocks whose ds word carries d and, in its high half,
+// the fp16 activation sum s; nibbles widened to int8; the min term applied
+// through the activation sum).  There it feeds int8 matrix products and a
+// 4-wide integer-dot matvec; here it is the matvec, on gfx950's
+// v_dot4_i32_i8.
 //
 // A block of 32 weights is one 16-byte chunk of 4-bit codes or two of 8-bit
 // codes, and its fold is  acc += scale * (d * idot) + bias * s  (8-bit:
@@ -30,15 +32,27 @@ constexpr int kQuadXor2 = 0x4E;      // DPP quad_perm [2, 3, 0, 1]
 
 // ------------------------------------------------------------------ quantize
 
+// fp32 -> fp16 bits, round to nearest even (the hardware conversion in the
+// default rounding mode; overflow gives infinity), and back (exact).
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
 // One lane's share of a block of 32 activations: eight bf16 values w of a
 // block held by four consecutive lanes (lanes 4m..4m+3; every lane of the
-// wave calls this together).  amax is a max over the four lanes,
-// d = amax / 127, the codes rne(x * (127 / amax)) and s = d * sum(q) (an
-// integer sum over the four lanes), all decided in fp32 with correctly
-// rounded operations, so the result does not depend on how the block is
-// split.  An all-zero block gives d = s = 0 and zero codes.  packed holds the
-// lane's eight codes in column order.
-__device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[2], float &d, float &s) {
+// wave calls this together).  amax is a max over the four lanes; the block
+// stores d = fp16_rne(amax / 127), its codes are rne(x / d) with that stored
+// d, clamped to +-127 (0 when d is 0), and s = fp16_rne(d * sum(q)) (an
+// integer sum over the four lanes; d * sum is exact in fp32).  The quotients
+// are correctly rounded fp32 divisions: a quotient of a bf16 by 127 or by an
+// fp16 value is never within fp32 rounding of an fp16 or integer midpoint
+// unless it lies on it, so these are the exact-arithmetic decisions, and the
+// result does not depend on how the block is split.  packed holds the lane's
+// eight codes in column order; ds is the block's {d, s} word.
+__device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[2], uint32_t &ds) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float v[8];
 #pragma unroll
@@ -52,15 +66,16 @@ __device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[
     // quad permutes (lanes l ^ 1, then l ^ 2) as DPP moves
     amax = fmaxf(amax, dpp_f<kQuadXor1>(amax));
     amax = fmaxf(amax, dpp_f<kQuadXor2>(amax));
-    d = amax > 0.0f ? __fdiv_rn(amax, 127.0f) : 0.0f;
-    const float inv = amax > 0.0f ? __fdiv_rn(127.0f, amax) : 0.0f;
+    const uint32_t dh = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
+    const float d = f16_bits_to_f32(dh);
+    const bool live = d > 0.0f;
     int sum = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float r = fminf(fmaxf(__builtin_rintf(__fmul_rn(v[4 * h + j], inv)), -127.0f), 127.0f);
+            const float r = live ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(v[4 * h + j], d)), -127.0f), 127.0f) : 0.0f;
             const int qi = int(r);
             sum += qi;
             word |= (uint32_t(qi) & 0xFFu) << (8 * j);
@@ -69,23 +84,22 @@ __device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[
     }
     sum += __builtin_amdgcn_update_dpp(0, sum, kQuadXor1, 0xF, 0xF, false);
     sum += __builtin_amdgcn_update_dpp(0, sum, kQuadXor2, 0xF, 0xF, false);
-    s = __fmul_rn(d, float(sum));
+    ds = dh | (f32_to_f16_bits(d * float(sum)) << 16);
 }
 
 // One lane per 8 activations (a block is four consecutive lanes).  Threads
 // past the last unit compute on a clamped unit and store nothing; the four
 // lanes of a block are always in range together (units come in fours).
 __global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__restrict__ x, int64_t units,
-                                                             int8_t *__restrict__ xq, float *__restrict__ ds) {
+                                                             int8_t *__restrict__ xq, uint32_t *__restrict__ ds) {
     const int64_t u_in = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
     const bool live = u_in < units;
     const int64_t u = live ? u_in : units - 1;
-    uint32_t packed[2];
-    float d, s;
-    quantize_unit(*reinterpret_cast<const uint4 *>(x + u * 8), packed, d, s);
+    uint32_t packed[2], dsw;
+    quantize_unit(*reinterpret_cast<const uint4 *>(x + u * 8), packed, dsw);
     if (live) {
         *reinterpret_cast<uint2 *>(xq + u * 8) = make_uint2(packed[0], packed[1]);
-        if ((u & 3) == 0) reinterpret_cast<float2 *>(ds)[u >> 2] = make_float2(d, s);
+        if ((u & 3) == 0) ds[u >> 2] = dsw;
     }
 }
 
@@ -93,7 +107,7 @@ __global__ void __launch_bounds__(256) qg_quantize_q8_kernel(const uint16_t *__r
 
 struct Q8Args {
     const int8_t *xq;       // int8 [B, k], natural order
-    const float *ds;        // {d, s} [B, k/32]
+    const uint32_t *ds;     // {d, s} fp16 pairs [B, k/32], d in the low half
     const uint16_t *x;      // bf16 [B, k], quantized in the staging (kFuse)
 };
 
@@ -135,7 +149,7 @@ __device__ __forceinline__ int dot_u8_i8(const uint4 q, const uint4 xp) {
 }
 
 __host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks) {
-    return batch * chunks * (2 * 16 + 8);
+    return batch * chunks * (2 * 16 + 4);
 }
 
 // Waves take contiguous row ranges (wave_rows); a step is one pass of 64
@@ -157,7 +171,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
     const int lane = threadIdx.x & (kWave - 1);
     const int chunks = p.chunks;
     uint4 *xl = reinterpret_cast<uint4 *>(smem);                                   // [B][2][chunks]
-    float2 *dl = reinterpret_cast<float2 *>(smem + int64_t(B) * chunks * 32);     // [B][chunks]
+    uint32_t *dl = reinterpret_cast<uint32_t *>(smem + int64_t(B) * chunks * 32); // [B][chunks]
 
     int64_t r_begin, r_end;
     wave_rows(p, r_begin, r_end);
@@ -198,16 +212,15 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
             return make_uint4(v.x, v.y, v.z, v.w);
         };
         auto quant_store = [&](int u, const uint4 w) {
-            uint32_t packed[2];
-            float d, sv;
-            quantize_unit(w, packed, d, sv);
+            uint32_t packed[2], dsw;
+            quantize_unit(w, packed, dsw);
             if (u < units) {
                 const int b = u / upr;
                 const int e = u - b * upr;           // 8-column unit in the row
                 const int c = e >> 2, h = e & 3;     // chunk, 8-column group in it
                 const uint2 eo = Bits == 4 ? even_odd(packed[0], packed[1]) : make_uint2(packed[0], packed[1]);
                 reinterpret_cast<uint2 *>(&xl[(b * 2 + (h >> 1)) * chunks + c])[h & 1] = eo;
-                if (h == 0) dl[b * chunks + c] = make_float2(d, sv);
+                if (h == 0) dl[b * chunks + c] = dsw;
             }
         };
         uint4 xv[kSX];
@@ -237,14 +250,13 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
         const int x_units = B * units_per_row;
         const int d_units = B * chunks;
         const rsrc_t rx = make_rsrc(a.xq, uint32_t(x_units) * 16u);
-        const rsrc_t rd = make_rsrc(a.ds, uint32_t(d_units) * 8u);
+        const rsrc_t rd = make_rsrc(a.ds, uint32_t(d_units) * 4u);
         auto load_x = [&](int u) -> uint4 {
             const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rx, int(u < x_units ? uint32_t(u) * 16u : kOutOfRange), 0, 0);
             return make_uint4(v.x, v.y, v.z, v.w);
         };
-        auto load_d = [&](int u) -> float2 {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rd, int(u < d_units ? uint32_t(u) * 8u : kOutOfRange), 0, 0);
-            return make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+        auto load_d = [&](int u) -> uint32_t {
+            return __builtin_amdgcn_raw_buffer_load_b32(rd, int(u < d_units ? uint32_t(u) * 4u : kOutOfRange), 0, 0);
         };
         auto store_x = [&](int u, const uint4 v) {
             if (u < x_units) {
@@ -259,7 +271,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
             }
         };
         uint4 xv[kSU];
-        float2 dv[kSD];
+        uint32_t dv[kSD];
     #pragma unroll
         for (int i = 0; i < kSU; ++i) xv[i] = load_x(i * nt + tid);
     #pragma unroll
@@ -305,7 +317,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
         if (pc < pieces) {
             const int c = pc / PPB, h = pc % PPB;    // block, half of it
             uint4 xp[B][2];
-            float2 dsv[B];
+            float dv[B], sv[B];
 #pragma unroll
             for (int b = 0; b < B; ++b) {
                 if constexpr (Bits == 4) {
@@ -314,7 +326,9 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
                 } else {
                     xp[b][0] = xl[(b * 2 + h) * chunks + c];
                 }
-                dsv[b] = dl[b * chunks + c];
+                const uint32_t dsw = dl[b * chunks + c];
+                dv[b] = f16_bits_to_f32(dsw & 0xFFFFu);
+                sv[b] = f16_bits_to_f32(dsw >> 16);
             }
 #pragma unroll
             for (int i = 0; i < R; ++i) {
@@ -329,8 +343,8 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
                         int idot;
                         if constexpr (Bits == 4) idot = dot_u4_i8(bf.c[i], xp[b]);
                         else idot = dot_u8_i8(bf.c[i], xp[b][0]);
-                        const float t_ = dsv[b].x * float(idot);
-                        acc[i][b] = fmaf(bi, dsv[b].y, fmaf(sc, t_, acc[i][b]));
+                        const float t_ = dv[b] * float(idot);
+                        acc[i][b] = fmaf(bi, sv[b], fmaf(sc, t_, acc[i][b]));
                     }
                 }
             }
@@ -469,24 +483,25 @@ qg_status run_q8(int bits, const uint32_t *codes, const uint16_t *scales, const 
 
 extern "C" {
 
-qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
+qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, uint16_t *ds,
                            hipStream_t stream) {
     if (!x || !xq || !ds) return QG_ERR_NULL_POINTER;
     if (k < 1 || k % qg::kQ8Block || k > (int64_t(1) << 30)) return QG_ERR_BAD_SHAPE;
     if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
-    if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
+    if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 4)) return QG_ERR_MISALIGNED;
     const int64_t units = int64_t(batch) * k / 8;
     const int64_t grid = (units + 255) / 256;
-    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq, ds);
+    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq,
+                       reinterpret_cast<uint32_t *>(ds));
     return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
 qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             const int8_t *xq, const uint16_t *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     if (!xq || !ds) return QG_ERR_NULL_POINTER;
-    if (!aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
-    return run_q8(4, codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
+    if (!aligned_to(xq, 16) || !aligned_to(ds, 4)) return QG_ERR_MISALIGNED;
+    return run_q8(4, codes, scales, biases, qg::Q8Args{xq, reinterpret_cast<const uint32_t *>(ds), nullptr}, y, n, k, group_size, batch, out_dtype,
                   stream);
 }
 
@@ -500,11 +515,11 @@ qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales
 }
 
 qg_status qgemv_affine_u8_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             const int8_t *xq, const uint16_t *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
     if (!xq || !ds) return QG_ERR_NULL_POINTER;
-    if (!aligned_to(xq, 16) || !aligned_to(ds, 8)) return QG_ERR_MISALIGNED;
-    return run_q8(8, codes, scales, biases, qg::Q8Args{xq, ds, nullptr}, y, n, k, group_size, batch, out_dtype,
+    if (!aligned_to(xq, 16) || !aligned_to(ds, 4)) return QG_ERR_MISALIGNED;
+    return run_q8(8, codes, scales, biases, qg::Q8Args{xq, reinterpret_cast<const uint32_t *>(ds), nullptr}, y, n, k, group_size, batch, out_dtype,
                   stream);
 }
 

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 3
+#define QG_ABI_VERSION 4
 
 typedef enum qg_status {
     QG_OK = 0,
@@ -291,23 +291,30 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  * Int8 activation route for affine 4-bit and 8-bit weights.
  *
  * The SharpInference issue ("generalize Gemma 4 batched prefill ..."),
- * "Item C2", quantizes the activation to int8 blocks that carry a pair
- * {d, s} with s = d * sum(q), widens the 4-bit weights to int8, and applies
- * the affine minimum once per block through s.  The pages do not print the
- * quantizer; this library reads it as the symmetric one below.  The route
- * changes the result by at most sum_k |W^[n,k]| * d_blk / 2 against the bf16
- * product (each activation moves by at most half a step).
+ * "Item C2", quantizes the activation to int8 q8_1 blocks whose 32-bit ds
+ * word carries an fp16 pair: d in the low half and, in the high half, the
+ * block's activation sum s = d * sum(q); it widens the 4-bit weights to int8
+ * and applies the affine minimum once per block through s.  The pages do not
+ * print the quantizer; this library reads it as the symmetric one below,
+ * with the codes chosen against the d the block stores.  The route changes
+ * the result by at most sum_k |W^[n,k]| * d_blk / 2 against the bf16
+ * product (each activation moves by at most half a step), plus the fp16
+ * rounding of s times the bias.
  *
  * qg_quantize_q8_1: per batch row, per block of 32 consecutive activations,
- *   amax = max |x|,  d = fp32(amax / 127),  q = rne(fp32(x * fp32(127 / amax)))
- *   (in [-127, 127]),  s = fp32(d * sum q);  an all-zero block gives d = s = 0
- *   and zero codes.  Every operation is a correctly rounded fp32 one, so the
- *   codes are exact functions of x.  x must be finite.
+ *   amax = max |x|,  d = fp16_rne(amax / 127),
+ *   q = clamp(rne(x / d), -127, 127)  (q = 0 when d is 0: an all-zero block,
+ *   or amax / 127 below half the smallest fp16 subnormal),
+ *   s = fp16_rne(d * sum q).
+ *   The decisions are those of exact arithmetic (correctly rounded fp32
+ *   quotients, which never reach an fp16 or integer midpoint they are not
+ *   on), so the codes and pairs are exact functions of x.  x must be finite;
+ *   block maxima of 65520 * 127 or more make d infinite (unspecified result).
  *   x    bf16 [batch, k] (DEVICE), 16-byte aligned
  *   xq   int8 [batch, k] (DEVICE, caller-owned output), 16-byte aligned,
  *        natural column order
- *   ds   float [batch, k/32, 2] = {d, s} (DEVICE, caller-owned output),
- *        8-byte aligned
+ *   ds   fp16 bits [batch, k/32, 2] = {d, s} (DEVICE, caller-owned output),
+ *        4-byte aligned: one little-endian 32-bit word per block, d low
  *   k >= 32, k % 32 == 0                          QG_ERR_BAD_SHAPE
  *   1 <= batch <= 4                               QG_ERR_BAD_BATCH
  *
@@ -319,8 +326,8 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   xq, ds  as written by qg_quantize_q8_1 (DEVICE)
  *   y       [batch, n] f32 or bf16 (DEVICE), 4- or 2-byte aligned
  *   group_size in {32, 64, 128}, k % group_size == 0   QG_ERR_BAD_GROUP_SIZE
- *   the activation codes and pairs are staged in LDS: batch * k * 1.25 bytes
- *   must be at most 128 KiB                       QG_ERR_TOO_LARGE
+ *   the activation codes and pairs are staged in LDS: batch * k * 1.125
+ *   bytes must be at most 128 KiB                 QG_ERR_TOO_LARGE
  *   other checks and errors as for qgemv_affine_u4.
  * qgemv_affine_u4_q8_fused: the same product with the quantization of x
  *   done inside the matvec (each workgroup quantizes x as it stages it, with
@@ -335,19 +342,19 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   enters the 4-wide dot as the signed byte c - 128 (its top bit flipped)
  *   and the block adds 128 * scale * s back with the bias, so that
  *   y[b, r] = sum over blocks of scale*d*sum(c*q) + bias*s as for u4 (up to
- *   the fp32 rounding of s).
+ *   the fp32 rounding of 128 * scale + bias).
  * None of these calls allocates device memory; all are asynchronous on
  * `stream`. */
-qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, float *ds,
+qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, uint16_t *ds,
                            hipStream_t stream);
 qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             const int8_t *xq, const uint16_t *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 qg_status qgemv_affine_u4_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                                    const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,
                                    int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 qg_status qgemv_affine_u8_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
-                             const int8_t *xq, const float *ds, void *y, int64_t n, int64_t k,
+                             const int8_t *xq, const uint16_t *ds, void *y, int64_t n, int64_t k,
                              int32_t group_size, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
 qg_status qgemv_affine_u8_q8_fused(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,
                                    const uint16_t *x, void *y, int64_t n, int64_t k, int32_t group_size,

@@ -183,7 +183,7 @@ def _q8f(codes=A, scales=A2, biases=A2, x=A3, y=A4, n=8, k=128, gs=64, b=1, out=
 @pytest.mark.parametrize("kw,status", [
     ({"codes": None}, NULL), ({"biases": None}, NULL), ({"xq": None}, NULL), ({"ds": None}, NULL),
     ({"n": 0}, SHAPE), ({"k": 48}, SHAPE), ({"k": 0}, SHAPE), ({"gs": 16}, GROUP), ({"k": 96, "gs": 64}, GROUP),
-    ({"codes": ODD}, MIS), ({"xq": ODD}, MIS), ({"ds": ctypes.c_void_p(0x200004)}, MIS),
+    ({"codes": ODD}, MIS), ({"xq": ODD}, MIS), ({"ds": ctypes.c_void_p(0x200002)}, MIS),
     ({"b": 0}, BATCH), ({"b": 5}, BATCH), ({"out": 2}, DTYPE), ({"k": 1 << 17, "b": 1}, LARGE),
 ])
 def test_int8_route_validation(kw, status):

@@ -2,8 +2,9 @@
 through the C ABI (qg_quantize_q8_1, qgemv_affine_u{4,8}_q8 and their fused
 forms), against oracle.q8.
 
-* The quantizer's codes and {d, s} pairs are integer or fp32 decisions taken
-  with correctly rounded fp32 operations on both sides: compared bit for bit.
+* The quantizer's codes and fp16 {d, s} pairs are the decisions of exact
+  arithmetic on both sides (float64 in the oracle, correctly rounded fp32
+  quotients on the GPU): compared bit for bit.
 * The matvec gets the oracle's own quantized activations (never the GPU's)
   and meets the parity criterion against the float64 block sum.
 * End to end (GPU quantize, then GPU matvec) equals the matvec on the
@@ -33,19 +34,27 @@ def _gpu():
 
 
 def _x_blocks(seed, batch, k):
-    """N(0, 1) activations with a per-block magnitude spread over 2^-10..2^10,
-    some all-zero blocks, and blocks whose products land on .5 ties."""
+    """N(0, 1) activations with a per-block magnitude spread over 2^-14..2^6
+    (the small blocks have fp16-subnormal d), some all-zero blocks, a block
+    whose d underflows to zero, and a block whose quotients land on .5 ties."""
     rng = np.random.default_rng([0, 55, seed, batch, k])
     x = rng.standard_normal((batch, k)).astype(np.float32)
-    x *= np.repeat(np.exp2(rng.integers(-10, 11, (batch, k // 32))), 32, axis=1).astype(np.float32)
+    x *= np.repeat(np.exp2(rng.integers(-14, 7, (batch, k // 32))), 32, axis=1).astype(np.float32)
     nb = k // 32
     if nb > 2:
         x[:, 32:64] = 0.0                                      # an all-zero block
-        # ties: amax = 127/64 makes 127/amax = 64 exactly, and x = (2m+1)/128
-        # (exact in bf16) gives x * 64 = m + 1/2, rounded to the even neighbour
+        # ties: amax = 127/64 gives d = 2^-6 exactly, and x = (2m+1)/128
+        # (exact in bf16) gives x / d = m + 1/2, rounded to the even neighbour
         x[0, 64] = 127.0 / 64.0
         x[0, 65:96] = (2.0 * (np.arange(31) - 15) + 1.0) / 128.0
+    if nb > 3:
+        x[-1, 96:128] = 2.0 ** -27                             # amax / 127 below fp16: d = 0
     return F.f64_to_bf16_bits(x.astype(np.float64))
+
+
+def _ds(d_ref, s_ref):
+    """The oracle's pairs in the library's layout (fp16 bits, d then s)."""
+    return Q8.pack_ds(d_ref, s_ref)
 
 
 def _gpu_quantize(x_bits):
@@ -61,8 +70,7 @@ def test_quantize_bitwise(batch, k):
     xq, ds = _gpu_quantize(x)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
     assert np.array_equal(xq, q_ref)
-    assert np.array_equal(ds[..., 0], d_ref)
-    assert np.array_equal(ds[..., 1], s_ref)
+    assert np.array_equal(ds.view(np.uint16), _ds(d_ref, s_ref))
 
 
 def _weights(seed, n, k, gs, bits=4):
@@ -94,7 +102,7 @@ def test_matvec_parity(bits, n, k, gs, batch):
     arrays = _weights(n + k, n, k, gs, bits)
     x = _x_blocks(2, batch, k)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    ds = np.stack([d_ref, s_ref], axis=-1).astype(np.float32)
+    ds = _ds(d_ref, s_ref)
     y = _matvec(arrays, q_ref, ds, n, gs, bits=bits)
     y_ref, a_ref = Q8.gemv_affine_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, bits, gs)
     parity.assert_parity(y, y_ref, a_ref, "u%d q8 n=%d k=%d" % (bits, n, k))
@@ -115,7 +123,7 @@ def test_end_to_end_equals_oracle_blocks():
     q.qgemv_affine_u4_q8(dargs[0], dargs[1], dargs[2], xq, ds, y, gs)
     y_gpu = host_y(y)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    y_blocks = _matvec(arrays, q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs)
+    y_blocks = _matvec(arrays, q_ref, _ds(d_ref, s_ref), n, gs)
     assert np.array_equal(y_gpu, y_blocks)
     y_ref, a_ref = Q8.gemv_affine_u4_q8(arrays[0], arrays[1], arrays[2], q_ref, d_ref, s_ref, gs)
     parity.assert_parity(y_gpu, y_ref, a_ref, "u4 q8 end to end")
@@ -160,8 +168,7 @@ def test_all_codes_and_zero_blocks(bits):
     x = _x_blocks(4, 2, k)
     x[1, :] = 0
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
-    y = _matvec((codes, scales, biases), q_ref, np.stack([d_ref, s_ref], axis=-1).astype(np.float32), n, gs,
-                bits=bits)
+    y = _matvec((codes, scales, biases), q_ref, _ds(d_ref, s_ref), n, gs, bits=bits)
     y_ref, a_ref = Q8.gemv_affine_q8(codes, scales, biases, q_ref, d_ref, s_ref, bits, gs)
     parity.assert_parity(y, y_ref, a_ref, "u%d q8 uniform codes" % bits)
     assert np.all(y[1] == 0)
@@ -171,7 +178,7 @@ def test_errors_leave_y_untouched():
     n, k, gs = 8, 64, 64
     arrays = [dev(a) for a in _weights(1, n, k, gs)]
     xq = torch.zeros((1, k), dtype=torch.int8, device="cuda:0")
-    ds = torch.zeros((1, k // 32, 2), dtype=torch.float32, device="cuda:0")
+    ds = torch.zeros((1, k // 32, 2), dtype=torch.int16, device="cuda:0")
     y = out_tensor(1, n, fill=7.0)
     lib = q.lib()
     import ctypes
@@ -233,9 +240,9 @@ def test_full_size_sampled(bits, name, batch):
 @pytest.mark.parametrize("bits", [4, 8])
 def test_largest_staged_k(bits):
     """batch 4 at the largest k whose int8 blocks fit the 128 KiB staging
-    (4 * k * 1.25 bytes: k = 26208 with groups of 32), plain and fused, and
+    (4 * k * 1.125 bytes: k = 29120 with groups of 32), plain and fused, and
     the next block multiple is refused before any launch."""
-    n, k, gs, batch = 70, 26208, 32, 4
+    n, k, gs, batch = 70, 29120, 32, 4
     log("q8 largest k u%d n=%d k=%d batch=%d" % (bits, n, k, batch))
     arrays = _weights(11 + bits, n, k, gs, bits)
     x = _x_blocks(6, batch, k)
@@ -244,7 +251,7 @@ def test_largest_staged_k(bits):
     sep, fused = _fns(bits)
     dargs = [dev(a) for a in arrays]
     y = out_tensor(batch, n)
-    sep(dargs[0], dargs[1], dargs[2], dev(q_ref), dev(np.stack([d_ref, s_ref], axis=-1).astype(np.float32)), y, gs)
+    sep(dargs[0], dargs[1], dargs[2], dev(q_ref), dev(_ds(d_ref, s_ref)), y, gs)
     parity.assert_parity(host_y(y), y_ref, a_ref, "u%d q8 largest k" % bits)
     yf = out_tensor(batch, n)
     fused(dargs[0], dargs[1], dargs[2], dev(x), yf, gs)
@@ -268,4 +275,4 @@ def test_quantize_long_rows_bitwise():
     xq, ds = _gpu_quantize(x)
     q_ref, d_ref, s_ref = Q8.quantize_q8_1(x)
     assert np.array_equal(xq, q_ref)
-    assert np.array_equal(ds[..., 0], d_ref) and np.array_equal(ds[..., 1], s_ref)
+    assert np.array_equal(ds.view(np.uint16), _ds(d_ref, s_ref))
