@@ -28,7 +28,7 @@ __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
     "qg_quantize_q8_1", "qgemv_affine_u4_q8", "qgemv_affine_u4_q8_fused", "qgemv_affine_u8_q8",
     "qgemv_affine_u8_q8_fused",
-    "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version", "qg_max_k",
+    "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version",
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
     "qg_bytes_fp4", "qg_bytes_affine", "qg_bytes_fp8", "lib",
@@ -58,10 +58,6 @@ def qg_status_string(status):
 
 def qg_abi_version():
     return int(_lib.qg_abi_version())
-
-
-def qg_max_k(fmt, batch):
-    return int(_lib.qg_max_k(int(fmt), int(batch)))
 
 
 # ------------------------------------------------------------------ device entry points

@@ -66,7 +66,6 @@ SIGNATURES = {
     "qg_stream_probe": (_st, [_p, _i64, _i32, _i32, _i32, _i32, _p, _p]),
     "qg_status_string": (ctypes.c_char_p, [_st]),
     "qg_abi_version": (ctypes.c_int, []),
-    "qg_max_k": (_i64, [_i32, _i32]),
     "qg_quantize_fp4_e2m1": (_st, [_p, _i64, _i64, _i32, _p, _p]),
     "qg_quantize_affine": (_st, [_p, _i64, _i64, _i32, _i32, _p, _p, _p]),
     "qg_quantize_fp8_e4m3_rowwise": (_st, [_p, _i64, _i64, _p, _p]),

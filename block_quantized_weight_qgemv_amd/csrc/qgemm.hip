@@ -81,8 +81,8 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);      \
             });                                                                                         \
             if (attr != hipSuccess) return QG_ERR_LAUNCH;                                               \
-            hipLaunchKernelGGL((qg::qgemm_fp4_small_kernel<S, K, V>), sgrid, sblock, size_t(small_lds), stream, p); \
-            return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                             \
+            return qgl::launch_kernel(qg::qgemm_fp4_small_kernel<S, K, V>, sgrid, sblock, size_t(small_lds), \
+                                      stream, p);                                                       \
         }
 #define QG_GEMM_SMALL_V(S, K) QG_GEMM_SMALL(S, K, true) QG_GEMM_SMALL(S, K, false)
         QG_GEMM_SMALL_V(1, 1) QG_GEMM_SMALL_V(1, 2) QG_GEMM_SMALL_V(1, 4)
@@ -117,8 +117,7 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
             });                                                                                 \
             if (attr != hipSuccess) return QG_ERR_LAUNCH;                                       \
         }                                                                                       \
-        hipLaunchKernelGGL((qg::qgemm_fp4_kernel<S, T, K, W>), grid, block, size_t(lds), stream, p); \
-        return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;                         \
+        return qgl::launch_kernel(qg::qgemm_fp4_kernel<S, T, K, W>, grid, block, size_t(lds), stream, p); \
     }
 #define QG_GEMM_SPG(S) QG_GEMM_CASE(S, 1, 1, 4) QG_GEMM_CASE(S, 2, 1, 4) QG_GEMM_CASE(S, 4, 1, 4) \
     QG_GEMM_CASE(S, 1, 2, 4) QG_GEMM_CASE(S, 2, 2, 4) QG_GEMM_CASE(S, 1, 4, 4)                   \

@@ -62,7 +62,6 @@ qg_status check_common(qg_format f, const void *codes, const void *x, const void
     if (out != QG_OUT_F32 && out != QG_OUT_BF16) return QG_ERR_BAD_DTYPE;
     if (!aligned(codes, 16) || !aligned(x, 16)) return QG_ERR_MISALIGNED;
     if (!aligned(y, out == QG_OUT_F32 ? 4 : 2)) return QG_ERR_MISALIGNED;
-    if (lds_bytes(f, k, batch) > kMaxLds) return QG_ERR_TOO_LARGE;
     return QG_OK;
 }
 
@@ -108,7 +107,7 @@ struct Split {
 Split split_of(qg_format f, const Params &p) {
     const FmtInfo fi = fmt_info(f);
     Split sp{1, p.chunks, p.groups, 0, false};
-    const int jmax = fi.pieces >= 4 ? 2 : 4;
+    const int jmax = qgl::row_max_passes(fi.pieces);
     int need = int((p.chunks + 64 * jmax - 1) / (64 * jmax));
     int segs = 1;
     while (segs < need) segs <<= 1;
@@ -173,7 +172,8 @@ Plan default_plan(qg_format f, const Params &p, int32_t batch, int cus) {
 template <class Fmt>
 bool row_instance_exists(int r, int b, int j) {
     const int pcs = Fmt::kPieces;
-    return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= (Fmt::kSums ? 1 : 2)) && !(r == 4 && j == 4);
+    return b * j * pcs <= 32 && (b * j * pcs <= 16 || r <= (Fmt::kSums ? 1 : 2)) && !(r == 4 && j == 4) &&
+           j <= qgl::row_max_passes(pcs);
 }
 
 qg_status check_plan(const qg_plan *plan) {
@@ -195,11 +195,21 @@ bool row_instance_for(qg_format f, int r, int b, int j) {
 }
 
 // FP8 with three or four activation rows runs on the matrix-core kernel
-// (qgemv_fp8_mfma.hpp) for every shape: 4-row tiles, x in LDS.  Its default launch is one workgroup of 8
-// waves per CU (fewer workgroups when tiles are few); rows_per_tile is fixed.
+// (qgemv_fp8_mfma.hpp): 4-row tiles, x in LDS.  Its default launch is one
+// workgroup of 8 waves per CU (fewer workgroups when tiles are few);
+// rows_per_tile is fixed.  It takes every k whose batch-4 activations fit its
+// LDS (k <= 16368), at batch 3 as at batch 4, so that both batch sizes of
+// the group add a row's terms in the same order; longer rows take the vector
+// kernels, as batch 1 and 2 do.
+bool fp8_mfma_takes(const Params &p) {
+    const int64_t norm_bytes = p.norm ? int64_t(4) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
+    return int64_t(4) * p.k * 2 + qg::kLdsSink + norm_bytes <= kMaxLds;
+}
+
 Plan fp8_default_plan(const Params &p, int cus) {
     Plan pl;
     pl.row_kernel = false;
+    pl.fp8_mfma = true;
     pl.passes = p.passes;
     pl.rows_per_tile = qg::kFp8TileRows;
     pl.waves_per_block = 8;
@@ -241,11 +251,36 @@ qg_status run_fp8(Params p, int32_t batch, const qg_plan *override_plan, hipStre
     return qgl::launch_fp8(p, pl, batch, lds, stream);
 }
 
+// Whether the fused norm's row kernel fits its LDS (x, gamma, the tile
+// counters, one row's split-K partials, the norm's group sums).
+bool norm_row_fits(const Params &p, int32_t batch) {
+    const int64_t b = batch;
+    const int64_t norm_bytes = b * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4;
+    return (b + 1) * p.k * 2 + kCounterBytes + int64_t(p.segs) * b * 4 + norm_bytes <= kMaxLds;
+}
+
+// Launch plan for the LDS kernel: the plan's rows per tile and waves, x
+// staged in LDS when it fits beside the norm's sums, read from memory with
+// the weights (one-row tiles) otherwise.
+void lds_kernel_setup(qg_format f, Params &p, Plan &pl, int32_t batch, int64_t norm_bytes, int64_t &lds) {
+    pl.row_kernel = false;
+    p.passes = passes_of(p.chunks);               // the LDS kernel walks whole rows
+    lds = lds_bytes(f, p.k, batch);
+    p.x_global = lds + norm_bytes > kMaxLds ? 1 : 0;
+    if (p.x_global) {
+        lds = 0;
+        pl.rows_per_tile = 1;
+    }
+    p.norm_offset = int32_t(lds);
+    lds += norm_bytes;
+}
+
 qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream) {
     int cus = 0;
     qg_status st = device_cus(&cus);
     if (st != QG_OK) return st;
-    if (f == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch) return run_fp8(p, batch, override_plan, stream, cus);
+    if (f == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch && fp8_mfma_takes(p))
+        return run_fp8(p, batch, override_plan, stream, cus);
     const Split sp = split_of(f, p);
     if (sp.ok) {
         p.segs = sp.segs;
@@ -256,17 +291,25 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         p.segs = 0;                               // the row kernel does not apply
         p.passes = passes_of(p.chunks);
     }
+    // The fused norm's row kernel holds x and gamma in LDS.  Where they do not
+    // fit ((batch + 1) * k * 2 bytes beside the split-K partials and the
+    // norm's sums) the LDS kernel takes the call: the same bound, but its own
+    // order of additions, so such a call is not bitwise the plain call on
+    // the separately normalized x.
+    if (p.norm && p.segs && !norm_row_fits(p, batch)) p.segs = 0;
     Plan pl = default_plan(f, p, batch, cus);
-    if (override_plan) {
-        if (override_plan->rows_per_tile) pl.rows_per_tile = override_plan->rows_per_tile;
-        if (override_plan->waves_per_block) pl.waves_per_block = override_plan->waves_per_block;
-        if (override_plan->blocks) pl.blocks = override_plan->blocks;
+    auto apply_override = [&](Plan &q) {
+        if (!override_plan) return;
+        if (override_plan->rows_per_tile) q.rows_per_tile = override_plan->rows_per_tile;
+        if (override_plan->waves_per_block) q.waves_per_block = override_plan->waves_per_block;
+        if (override_plan->blocks) q.blocks = override_plan->blocks;
         else {
-            const int64_t max_blocks = (p.n + pl.waves_per_block - 1) / pl.waves_per_block;
-            int64_t b = int64_t(cus) * 8 / pl.waves_per_block;
-            pl.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
+            const int64_t max_blocks = (p.n + q.waves_per_block - 1) / q.waves_per_block;
+            int64_t b = int64_t(cus) * 8 / q.waves_per_block;
+            q.blocks = int(b > max_blocks ? max_blocks : (b < 1 ? 1 : b));
         }
-    }
+    };
+    apply_override(pl);
     // fused RMSNorm: one float per group of 64 activation units per batch row
     const int64_t norm_bytes = p.norm ? int64_t(batch) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
     int64_t lds = 0;
@@ -294,7 +337,6 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         p.gamma_offset = int32_t(x_bytes);
         p.counter_offset = int32_t(x_bytes + g_bytes);
         p.part_offset = int32_t(x_bytes + g_bytes + (via_lds ? kCounterBytes : 0));
-        if (p.part_offset + norm_bytes > kMaxLds) return QG_ERR_TOO_LARGE;
         lds = p.part_offset + row_lds_bytes(p, pl.blocks, batch);
         if (lds + norm_bytes > kMaxLds) {
             // more, smaller workgroups until the split-K partials fit
@@ -306,11 +348,7 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         p.norm_offset = int32_t(lds);
         lds += norm_bytes;
     } else {
-        p.passes = passes_of(p.chunks);           // the LDS kernel walks whole rows
-        lds = lds_bytes(f, p.k, batch);
-        p.norm_offset = int32_t(lds);
-        lds += norm_bytes;
-        if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
+        lds_kernel_setup(f, p, pl, batch, norm_bytes, lds);
     }
     p.total_waves = pl.blocks * pl.waves_per_block;
     switch (f) {
@@ -531,10 +569,9 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
     const int64_t sums = qg::rmsnorm_sums_bytes(k);
     if (sums > 64 * 1024) return QG_ERR_TOO_LARGE;      // k > 2^23
     if (sums + 4 * k <= 64 * 1024)
-        hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<true>, dim3(batch), dim3(256), size_t(sums + 4 * k), stream, p, out);
-    else
-        hipLaunchKernelGGL(qg::qg_rmsnorm_kernel<false>, dim3(batch), dim3(256), size_t(sums), stream, p, out);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+        return qgl::launch_kernel(qg::qg_rmsnorm_kernel<true>, dim3(batch), dim3(256), size_t(sums + 4 * k), stream,
+                                  p, out);
+    return qgl::launch_kernel(qg::qg_rmsnorm_kernel<false>, dim3(batch), dim3(256), size_t(sums), stream, p, out);
 }
 
 qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out) {
@@ -551,7 +588,7 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     p.groups = gs ? int32_t(k / gs) : 0;
     p.group_shift = gs ? log2i(gs / fmt_info(format).wpc) : 0;
     p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));
-    if (format == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch) {
+    if (format == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch && fp8_mfma_takes(p)) {
         p.passes = (p.chunks + qg::kFp8Slots - 1) / qg::kFp8Slots;
         const Plan pl = fp8_default_plan(p, cus);
         out->rows_per_tile = pl.rows_per_tile;
@@ -583,7 +620,7 @@ const char *qg_status_string(qg_status status) {
         case QG_ERR_BAD_DTYPE: return "unknown output dtype or format";
         case QG_ERR_BAD_BITS: return "bits must be 4 or 8";
         case QG_ERR_BAD_VALUE: return "non-finite weight, out-of-range code, or eps negative or not finite";
-        case QG_ERR_TOO_LARGE: return "k * batch exceeds the activation staging limit (qg_max_k)";
+        case QG_ERR_TOO_LARGE: return "the activations exceed the LDS staging limit of this call";
         case QG_ERR_DEVICE: return "no usable HIP device";
         case QG_ERR_LAUNCH: return "kernel launch failed";
     }
@@ -605,22 +642,14 @@ qg_status qg_stream_probe(const void *buf, int64_t bytes, int32_t pattern, int32
     const int64_t units = bytes / 16;
     const dim3 g(blocks), t(threads_per_block);
     switch (unroll) {
-        case 1: hipLaunchKernelGGL(qg::stream_probe_kernel<1>, g, t, 0, stream, b, units, pattern, out); break;
-        case 2: hipLaunchKernelGGL(qg::stream_probe_kernel<2>, g, t, 0, stream, b, units, pattern, out); break;
-        case 4: hipLaunchKernelGGL(qg::stream_probe_kernel<4>, g, t, 0, stream, b, units, pattern, out); break;
-        case 8: hipLaunchKernelGGL(qg::stream_probe_kernel<8>, g, t, 0, stream, b, units, pattern, out); break;
-        case 16: hipLaunchKernelGGL(qg::stream_probe_kernel<16>, g, t, 0, stream, b, units, pattern, out); break;
+        case 1: return qgl::launch_kernel(qg::stream_probe_kernel<1>, g, t, 0, stream, b, units, pattern, out);
+        case 2: return qgl::launch_kernel(qg::stream_probe_kernel<2>, g, t, 0, stream, b, units, pattern, out);
+        case 4: return qgl::launch_kernel(qg::stream_probe_kernel<4>, g, t, 0, stream, b, units, pattern, out);
+        case 8: return qgl::launch_kernel(qg::stream_probe_kernel<8>, g, t, 0, stream, b, units, pattern, out);
+        case 16: return qgl::launch_kernel(qg::stream_probe_kernel<16>, g, t, 0, stream, b, units, pattern, out);
         default: return QG_ERR_BAD_SHAPE;
     }
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
 }
 
-int64_t qg_max_k(qg_format format, int32_t batch) {
-    if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_FP8_E4M3) return 0;
-    if (batch < 1 || batch > 4) return 0;
-    const FmtInfo fi = fmt_info(format);
-    const int64_t per_chunk = int64_t(batch) * (fi.pieces * 16 + (fi.sums ? 4 : 0));
-    return ((kMaxLds - qg::kLdsSink) / per_chunk) * fi.wpc;
-}
 
 }  // extern "C"

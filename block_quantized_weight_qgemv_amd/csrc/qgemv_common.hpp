@@ -50,6 +50,7 @@ struct Params {
     int32_t norm;                   // 1: x is RMS-normalized inside the kernel
     int32_t norm_offset;            // LDS byte offset of the norm's group sums
     int32_t gamma_offset;           // row kernel: LDS byte offset of gamma (fused norm)
+    int32_t x_global;               // LDS kernel: x too large for LDS, read from memory with the weights
 };
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }

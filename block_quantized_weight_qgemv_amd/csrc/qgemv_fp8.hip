@@ -1,6 +1,7 @@
 // Kernel instances of the FP8-E4M3 format (compiled on their own, in parallel
 // with the other formats): the row and LDS kernels for one or two activation
-// rows, the matrix-core kernel (qgemv_fp8_mfma.hpp) for three or four.
+// rows, the matrix-core kernel (qgemv_fp8_mfma.hpp) for three or four where
+// the planner chose it (rows whose batch-4 activations fit its LDS).
 #include "qgemv_launch.hpp"
 #include "qgemv_fp8_mfma.hpp"
 
@@ -33,7 +34,7 @@ qg_status launch_fp8_n(const Params &p, const Plan &pl, int32_t batch, int64_t l
 }  // namespace
 
 qg_status launch_fp8(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
-    if (batch < qg::kFp8MfmaMinBatch) return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, s);
+    if (!pl.fp8_mfma || batch < qg::kFp8MfmaMinBatch) return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, s);
     return p.norm ? launch_fp8_n<true>(p, pl, batch, lds, s) : launch_fp8_n<false>(p, pl, batch, lds, s);
 }
 

@@ -27,7 +27,11 @@
 //    sums meet in LDS once, at the end.
 // qgemv_lds_kernel (any shape the row kernel does not take): one step is one
 //    pass of a tile, x (and its per-chunk sums) is staged once per workgroup
-//    in LDS, and each lane loads its own group parameter.
+//    in LDS, and each lane loads its own group parameter.  Where x does not
+//    fit in LDS (kXGlobal), each step instead brings the lane's activation
+//    units for its chunk from memory with the weights (they stay in the
+//    caches: every wave reads the same x) and forms the pieces and sums from
+//    them with the same arithmetic, so the bits are those of the staged form.
 #pragma once
 
 #include "qgemv_common.hpp"
@@ -417,13 +421,18 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 
 // ------------------------------------------------------------------ long rows
 
-template <class Fmt, int R, int B, int D>
+template <class Fmt, int R, int B, int D, bool kXGlobal = false, bool kNorm = false>
 struct LdsKernel {
     static constexpr int NA = Fmt::kAuxArrays > 0 ? Fmt::kAuxArrays : 1;
+    static constexpr int XB = kXGlobal ? B : 1;                   // activation units carried by a step
+    static constexpr int XU = kXGlobal ? Fmt::kRawUnits : 1;
+    static constexpr int GU = kXGlobal && kNorm ? Fmt::kRawUnits : 1;
     struct Buf {
         uint4 c[R];
         uint32_t a[R][NA];     // this lane's group parameter of each row
         float rs[R];
+        uint4 xr[XB][XU];      // kXGlobal: the lane's raw activation units for this step's chunk
+        uint4 gr[GU];          // kXGlobal with the fused norm: gamma's units for the chunk
     };
     // bytes of dynamic LDS: activation pieces, per-chunk sums, and a 32-byte
     // sink for the stores of out-of-range staging lanes
@@ -432,10 +441,11 @@ struct LdsKernel {
     }
 };
 
-template <class Fmt, int R, int B, int D, bool kNorm>
+template <class Fmt, int R, int B, int D, bool kNorm, bool kXGlobal = false>
 __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    using Buf = typename LdsKernel<Fmt, R, B, D>::Buf;
+    using LK = LdsKernel<Fmt, R, B, D, kXGlobal, kNorm>;
+    using Buf = typename LK::Buf;
     const int lane = threadIdx.x & (kWave - 1);
     // fused RMSNorm: every batch row's factor, before any weight load
     float rn[B];
@@ -466,6 +476,18 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
             if constexpr (Fmt::kAuxArrays >= 1) b.a[i][0] = load_param(p.scales + row * p.groups + g);
             if constexpr (Fmt::kAuxArrays >= 2) b.a[i][1] = load_param(p.biases + row * p.groups + g);
             if constexpr (Fmt::kRowScale) b.rs[i] = p.row_scale[row];
+        }
+        if constexpr (kXGlobal) {
+#pragma unroll
+            for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+                for (int u = 0; u < Fmt::kRawUnits; ++u)
+                    b.xr[bb][u] = load_x_unit(p.x + int64_t(bb) * p.k + int64_t(c) * Fmt::kWpc + 8 * u);
+            if constexpr (norm) {
+#pragma unroll
+                for (int u = 0; u < Fmt::kRawUnits; ++u)
+                    b.gr[u] = load_x_unit(p.gamma + int64_t(c) * Fmt::kWpc + 8 * u);
+            }
         }
     };
 
@@ -514,35 +536,42 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
             *((st && ru == 0) ? &xsum[b * chunks + c] : sink_f) = sm;
         }
     };
-    constexpr int kXU = 8;
-    uint4 xr[kXU], gr[kXU];
-#pragma unroll
-    for (int i = 0; i < kXU; ++i) xr[i] = x_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
-    if (norm) {
-#pragma unroll
-        for (int i = 0; i < kXU; ++i) gr[i] = gamma_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
-    } else {
-#pragma unroll
-        for (int i = 0; i < kXU; ++i) gr[i] = make_uint4(0, 0, 0, 0);
-    }
 
-    // step 0 right behind the activations, the rest once they are in (as in
-    // the row kernel)
     Buf buf[D];
-    issue(buf[0], 0);
-    wait_vm_loads<R + R * Fmt::kAuxArrays + (Fmt::kRowScale ? R : 0)>();
+    if constexpr (kXGlobal) {
+        // nothing to stage: the steps carry their activations
 #pragma unroll
-    for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+    } else {
+        constexpr int kXU = 8;
+        uint4 xr[kXU], gr[kXU];
+#pragma unroll
+        for (int i = 0; i < kXU; ++i) xr[i] = x_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
+        if (norm) {
+#pragma unroll
+            for (int i = 0; i < kXU; ++i) gr[i] = gamma_unit(min(int(threadIdx.x) + i * int(blockDim.x), x_units - 1));
+        } else {
+#pragma unroll
+            for (int i = 0; i < kXU; ++i) gr[i] = make_uint4(0, 0, 0, 0);
+        }
+
+        // step 0 right behind the activations, the rest once they are in (as
+        // in the row kernel)
+        issue(buf[0], 0);
+        wait_vm_loads<R + R * Fmt::kAuxArrays + (Fmt::kRowScale ? R : 0)>();
+#pragma unroll
+        for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
 
 #pragma unroll
-    for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i], gr[i]);
-    // activations beyond kXU units per thread; the trip count is the same for
-    // every lane of a wave
-    for (int base = kXU * blockDim.x; base < x_units; base += blockDim.x) {
-        const int u = min(base + int(threadIdx.x), x_units - 1);
-        stage_unit(base + threadIdx.x, x_unit(u), norm ? gamma_unit(u) : make_uint4(0, 0, 0, 0));
+        for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i], gr[i]);
+        // activations beyond kXU units per thread; the trip count is the same
+        // for every lane of a wave
+        for (int base = kXU * blockDim.x; base < x_units; base += blockDim.x) {
+            const int u = min(base + int(threadIdx.x), x_units - 1);
+            stage_unit(base + threadIdx.x, x_unit(u), norm ? gamma_unit(u) : make_uint4(0, 0, 0, 0));
+        }
+        __syncthreads();
     }
-    __syncthreads();
 
     float acc[R][B];
 #pragma unroll
@@ -556,23 +585,42 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         const int c = lane + kWave * j;
         const int64_t row0 = r_begin + int64_t(t) * R;
         if (c < chunks) {
-            uint4 xp[B][Fmt::kPieces];
-            float xsv[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-#pragma unroll
-                for (int q = 0; q < Fmt::kPieces; ++q) xp[b][q] = xs[(b * Fmt::kPieces + q) * chunks + c];
-                xsv[b] = Fmt::kSums ? xsum[b * chunks + c] : 0.0f;
-            }
+            float s_[R], b_[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                if (row0 + i < r_end) {
-                    const float s_ = Fmt::kAuxArrays >= 1 ? bf16_to_f32(bf.a[i][0]) : 0.0f;
-                    const float b_ = Fmt::kAuxArrays >= 2 ? bf16_to_f32(bf.a[i][LdsKernel<Fmt, R, B, D>::NA - 1]) : 0.0f;
+                s_[i] = Fmt::kAuxArrays >= 1 ? bf16_to_f32(bf.a[i][0]) : 0.0f;
+                b_[i] = Fmt::kAuxArrays >= 2 ? bf16_to_f32(bf.a[i][LK::NA - 1]) : 0.0f;
+            }
+            // one batch row at a time: its pieces are live only for its own
+            // dots (each accumulator's order of additions is unchanged)
 #pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const float raw = Fmt::dot(bf.c[i], xp[b], 0.0f);
-                        acc[i][b] = Fmt::fold(acc[i][b], raw, s_, b_, xsv[b]);
+            for (int b = 0; b < B; ++b) {
+                uint4 xp[Fmt::kPieces];
+                float xsv;
+                if constexpr (kXGlobal) {
+                    // the staged form's arithmetic: normalize, split into
+                    // pieces, sum with chunk_sum's tree
+                    uint4 v[Fmt::kRawUnits];
+#pragma unroll
+                    for (int u = 0; u < Fmt::kRawUnits; ++u) {
+                        if constexpr (norm) v[u] = norm_unit(bf.xr[b][u], bf.gr[u], pick_uniform(rn, b));
+                        else v[u] = bf.xr[b][u];
+                        uint4 pc[Fmt::kPpu];
+                        Fmt::unit_pieces(v[u], pc);
+#pragma unroll
+                        for (int m = 0; m < Fmt::kPpu; ++m) xp[u * Fmt::kPpu + m] = pc[m];
+                    }
+                    xsv = Fmt::kSums ? chunk_sum(v) : 0.0f;
+                } else {
+#pragma unroll
+                    for (int q = 0; q < Fmt::kPieces; ++q) xp[q] = xs[(b * Fmt::kPieces + q) * chunks + c];
+                    xsv = Fmt::kSums ? xsum[b * chunks + c] : 0.0f;
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    if (row0 + i < r_end) {
+                        const float raw = Fmt::dot(bf.c[i], xp, 0.0f);
+                        acc[i][b] = Fmt::fold(acc[i][b], raw, s_[i], b_[i], xsv);
                     }
                 }
             }

@@ -5,6 +5,7 @@
 #pragma once
 
 #include "qgemv.h"
+#include "qgemv_device.hpp"
 #include "qgemv_kernels.hpp"
 
 #include <mutex>
@@ -24,6 +25,7 @@ struct Plan {
     int blocks;
     bool row_kernel;       // x in registers (row kernel) or staged in LDS
     int passes;            // row kernel: passes per K segment (1, 2 or 4)
+    bool fp8_mfma = false; // FP8 at batch 3-4 on the matrix-core kernel
 };
 
 
@@ -40,8 +42,7 @@ inline qg_status launch(const Params &p, const Plan &pl, int64_t lds, hipStream_
         });
         if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
     }
-    hipLaunchKernelGGL(Kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    return launch_kernel(Kern, dim3(pl.blocks), dim3(pl.waves_per_block * qg::kWave), size_t(lds), stream, p);
 }
 
 // prefetch depth: about 8 code loads in flight per lane
@@ -49,13 +50,17 @@ inline qg_status launch(const Params &p, const Plan &pl, int64_t lds, hipStream_
 constexpr int row_depth(int r, int j, int pieces) { return pieces > 16 ? 2 : (8 / (r * j) > 2 ? 8 / (r * j) : 2); }
 constexpr int lds_depth(int r) { return r == 1 ? 8 : 4; }
 
+// passes per K segment the planner gives a format: two for 16-byte-wide
+// activation pieces (4-bit formats, u8), four for FP8's (half as wide)
+constexpr int row_max_passes(int pieces) { return pieces >= 4 ? 2 : 4; }
+
 // register budget of the row kernel: at most 32 activation pieces per lane,
 // and fewer rows per tile when they are many (one row for the affine formats,
 // whose chunk sums and biases take further registers); no instance spills
 template <class Fmt, int R, int B, int J>
 constexpr bool row_instance() {
     return B * J * Fmt::kPieces <= 32 && (B * J * Fmt::kPieces <= 16 || R <= (Fmt::kSums ? 1 : 2)) &&
-           !(R == 4 && J == 4);
+           !(R == 4 && J == 4) && J <= row_max_passes(Fmt::kPieces);
 }
 
 template <class Fmt, int R, int B, bool kNorm>
@@ -78,14 +83,18 @@ qg_status launch_row_j(const Params &p, const Plan &pl, int64_t lds, hipStream_t
 }
 
 // The fused-norm variants run their own instances (kNorm), so the plain
-// instances carry none of that code.
+// instances carry none of that code.  The LDS kernel's form for activations
+// too large for LDS (p.x_global) always takes one-row tiles, two steps in
+// flight (each step carries the lane's activation units as well).
 template <class Fmt, int R, int B>
 qg_status launch_rb(const Params &p, const Plan &pl, int64_t lds, hipStream_t s) {
     if (p.norm) {
         if (pl.row_kernel) return launch_row_j<Fmt, R, B, true>(p, pl, lds, s);
+        if (p.x_global) return launch<qg::qgemv_lds_kernel<Fmt, 1, B, 2, true, true>>(p, pl, lds, s);
         return launch<qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), true>>(p, pl, lds, s);
     }
     if (pl.row_kernel) return launch_row_j<Fmt, R, B, false>(p, pl, lds, s);
+    if (p.x_global) return launch<qg::qgemv_lds_kernel<Fmt, 1, B, 2, false, true>>(p, pl, lds, s);
     return launch<qg::qgemv_lds_kernel<Fmt, R, B, lds_depth(R), false>>(p, pl, lds, s);
 }
 

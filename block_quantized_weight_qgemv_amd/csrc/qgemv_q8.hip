@@ -15,8 +15,9 @@
 // v_dot4_i32_i8.
 //
 // A block of 32 weights is one 16-byte chunk of 4-bit codes or two of 8-bit
-// codes, and its fold is  acc += scale * (d * idot) + bias * s  (8-bit:
-// bias + 128 * scale in place of bias).
+// codes, and its fold is  acc += scale * (d * idot) + bias * s, with idot the
+// exact integer sum of code times activation code (8-bit: two halves, each
+// taken as a dot of c - 128 plus 128 times the half's activation-code sum).
 
 #include "qgemv.h"
 #include "qgemv_kernels.hpp"
@@ -138,7 +139,7 @@ __device__ __forceinline__ int dot_u4_i8(const uint4 q, const uint4 (&xp)[2]) {
 // Integer dot of one 16-byte piece of 8-bit codes (half a block; word i:
 // columns 4i..4i+3 of the piece, one byte each) with the matching 16
 // activation codes in natural order.  Flipping a byte's top bit turns code c
-// into the signed byte c - 128; the caller adds 128 * scale * s back.
+// into the signed byte c - 128; the caller adds 128 * sum(q) back.
 __device__ __forceinline__ int dot_u8_i8(const uint4 q, const uint4 xp) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     const uint32_t x[4] = {xp.x, xp.y, xp.z, xp.w};
@@ -146,6 +147,14 @@ __device__ __forceinline__ int dot_u8_i8(const uint4 q, const uint4 xp) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_sdot4(int(w[i] ^ 0x80808080u), int(x[i]), acc, false);
     return acc;
+}
+
+// Sum of the 16 signed activation codes of a piece (4-wide dots with ones).
+__device__ __forceinline__ int code_sum_i8(const uint4 xp) {
+    int acc = __builtin_amdgcn_sdot4(int(xp.x), 0x01010101, 0, false);
+    acc = __builtin_amdgcn_sdot4(int(xp.y), 0x01010101, acc, false);
+    acc = __builtin_amdgcn_sdot4(int(xp.z), 0x01010101, acc, false);
+    return __builtin_amdgcn_sdot4(int(xp.w), 0x01010101, acc, false);
 }
 
 __host__ __device__ constexpr int64_t q8_lds_bytes(int64_t batch, int64_t chunks) {
@@ -330,19 +339,24 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
                 dv[b] = f16_bits_to_f32(dsw & 0xFFFFu);
                 sv[b] = f16_bits_to_f32(dsw >> 16);
             }
+            // 8-bit codes enter the dot as c - 128; 128 times the sum of the
+            // piece's activation codes puts the difference back in the
+            // integer sum, exactly (once per piece and batch row, shared by
+            // the tile's rows)
+            int qsum[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) qsum[b] = Bits == 8 ? 128 * code_sum_i8(xp[b][0]) : 0;
 #pragma unroll
             for (int i = 0; i < R; ++i) {
                 if (row0 + i < r_end) {
                     const float sc = bf16_to_f32(bf.s[i]);
-                    // 8-bit codes enter the dot as c - 128: the bias takes
-                    // 128 * scale, once per block (on its first half)
-                    const float bi = Bits == 4 ? bf16_to_f32(bf.b[i])
-                                               : (h == 0 ? fmaf(128.0f, sc, bf16_to_f32(bf.b[i])) : 0.0f);
+                    // the bias term once per block (8-bit: on its first half)
+                    const float bi = (Bits == 4 || h == 0) ? bf16_to_f32(bf.b[i]) : 0.0f;
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
                         int idot;
                         if constexpr (Bits == 4) idot = dot_u4_i8(bf.c[i], xp[b]);
-                        else idot = dot_u8_i8(bf.c[i], xp[b][0]);
+                        else idot = dot_u8_i8(bf.c[i], xp[b][0]) + qsum[b];
                         const float t_ = dv[b] * float(idot);
                         acc[i][b] = fmaf(bi, sv[b], fmaf(sc, t_, acc[i][b]));
                     }
@@ -396,8 +410,7 @@ qg_status launch_q8(const qg::Params &p, const qg::Q8Args &a, int blocks, int wa
         });
         if (err != hipSuccess) return QG_ERR_LAUNCH;
     }
-    hipLaunchKernelGGL(kern, dim3(blocks), dim3(waves * qg::kWave), size_t(lds), stream, p, a);
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    return qgl::launch_kernel(kern, dim3(blocks), dim3(waves * qg::kWave), size_t(lds), stream, p, a);
 }
 
 // The instance for a code width, batch size, tile shape and activation side
@@ -491,9 +504,8 @@ qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *
     if (!aligned_to(x, 16) || !aligned_to(xq, 16) || !aligned_to(ds, 4)) return QG_ERR_MISALIGNED;
     const int64_t units = int64_t(batch) * k / 8;
     const int64_t grid = (units + 255) / 256;
-    hipLaunchKernelGGL(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq,
-                       reinterpret_cast<uint32_t *>(ds));
-    return hipGetLastError() == hipSuccess ? QG_OK : QG_ERR_LAUNCH;
+    return qgl::launch_kernel(qg::qg_quantize_q8_kernel, dim3(unsigned(grid)), dim3(256), 0, stream, x, units, xq,
+                              reinterpret_cast<uint32_t *>(ds));
 }
 
 qg_status qgemv_affine_u4_q8(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases,

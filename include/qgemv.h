@@ -20,8 +20,11 @@
  *    frees or synchronizes; work is enqueued on `stream` and runs
  *    asynchronously.  `stream` may be 0 (the null stream).
  *  - Arguments are validated completely before any HIP call.  On an error
- *    nothing is launched and y is not touched.  Launch failures reported by
- *    hipGetLastError map to QG_ERR_LAUNCH.  No C++ exception crosses the ABI.
+ *    nothing is launched and y is not touched.  A launch that fails
+ *    (hipLaunchKernel's own status) maps to QG_ERR_LAUNCH; the thread's
+ *    last-error state is neither read nor cleared, so an error left by an
+ *    earlier, unrelated HIP call is never reported as this call's.  No C++
+ *    exception crosses the ABI.
  *  - Preconditions (else the listed error):
  *      n >= 1, k >= 1                                  QG_ERR_BAD_SHAPE
  *      k % group_size == 0, group_size in {32,64,128}  QG_ERR_BAD_GROUP_SIZE
@@ -31,9 +34,11 @@
  *        row_scale 4-byte; y 4-byte (f32) or 2-byte (bf16) QG_ERR_MISALIGNED
  *      1 <= batch <= 4                                 QG_ERR_BAD_BATCH
  *      out_dtype is QG_OUT_F32 or QG_OUT_BF16          QG_ERR_BAD_DTYPE
- *      the activation block (k * batch values, staged in LDS) fits the
- *        staging limit qg_max_k(format, batch)         QG_ERR_TOO_LARGE
+ *      n <= 2^31, k <= 2^30                            QG_ERR_BAD_SHAPE
  *      non-null pointers                               QG_ERR_NULL_POINTER
+ *    There is no limit on k * batch beyond that: activations that do not fit
+ *    the kernels' LDS staging are read from memory (through the caches) by
+ *    the steps that use them.
  *  - Results: fp32 accumulation.  Within 1e-3 relative error of the exact
  *    product per element (elements whose exact value nearly cancels are judged
  *    against 2^-12 * sum|w x|).  Run-to-run deterministic (no atomics), and a
@@ -65,7 +70,8 @@ typedef enum qg_status {
     QG_ERR_BAD_BITS = 7,
     QG_ERR_BAD_VALUE = 8,     /* a quantizer was given a non-finite weight,
                                  or a fused norm a negative / non-finite eps */
-    QG_ERR_TOO_LARGE = 9,     /* k * batch beyond the activation staging limit */
+    QG_ERR_TOO_LARGE = 9,     /* beyond an LDS staging limit: the int8 route's
+                                 activation blocks, the standalone norm's k */
     QG_ERR_DEVICE = 10,       /* no usable HIP device / attribute query failed */
     QG_ERR_LAUNCH = 11        /* the kernel launch itself failed              */
 } qg_status;
@@ -86,7 +92,8 @@ typedef enum qg_format {
 
 /*
  * FP4-E2M1 weights with one bf16 scale per group of `group_size` columns.
- * Part 2 post, "The assumption that failed the profiler": E2M1 codes (sign in
+ * "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus (Part 2)",
+ * section "The assumption that failed the profiler": E2M1 codes (sign in
  * code bit 3, every magnitude exact in BF16), a per-group scale folded out of
  * the per-weight math as one multiply-add per group.
  *
@@ -119,7 +126,9 @@ qg_status qgemv_affine_u4(const uint32_t *codes, const uint16_t *scales,
                           qg_out_dtype out_dtype, hipStream_t stream);
 
 /*
- * Min-max affine 8-bit codes (same source and bias fold as qgemv_affine_u4).
+ * Min-max affine 8-bit codes (mlxcel issue #683, "Step 2 result" and "Why
+ * gemma-4-12b is slow": the 8-bit group-64 MLP matrices that dominate the
+ * decode bytes; same layout rules and bias fold as qgemv_affine_u4).
  *   codes   DEVICE uint32 [n, k/4]: code j of a word in bits [8j, 8j+8).
  */
 qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales,
@@ -129,7 +138,8 @@ qg_status qgemv_affine_u8(const uint32_t *codes, const uint16_t *scales,
 
 /*
  * FP8-E4M3 (OCP "FN": max 448, S.1111.111 = NaN) weights with one fp32 scale
- * per row.  Part 2 post, "The assumption that failed the profiler": the FP8
+ * per row.  "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus
+ * (Part 2)", section "The assumption that failed the profiler": the FP8
  * lm_head matvec does one multiply-add per weight byte with no separate
  * dequantization pass; the row scale is applied once to the row's sum.
  *
@@ -216,13 +226,16 @@ const char *qg_status_string(qg_status status);
  *                                                  QG_ERR_MISALIGNED
  *   eps    >= 0 and finite                        else QG_ERR_BAD_VALUE
  *   plan   as in the *_plan variants (NULL: the default launch)
- *   x and gamma are held in LDS together: (batch + 1) * k * 2 bytes must fit
- *   the same 128 KiB as the staging limit, else QG_ERR_TOO_LARGE
  *
  * Everything else (arguments, layouts, errors, accuracy, determinism, batch
  * consistency) is as in the plain calls.  r[b] is summed in an order fixed by
  * k, so the result is also bitwise the same for every plan and batch size.
- * x itself is not modified.
+ * x itself is not modified.  One exception to "exactly what the plain entry
+ * point returns": where x and gamma do not fit in 128 KiB of LDS together
+ * ((batch + 1) * k * 2 bytes, e.g. batch 4 at k = 15360), the call runs a
+ * kernel that stages x per step and adds the terms in another order; it
+ * meets the same accuracy bound but is not bitwise the plain call's, nor
+ * the fused call's at a batch size that fits.
  * ---------------------------------------------------------------------- */
 
 qg_status qgemv_fp4_e2m1_rmsnorm(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
@@ -242,7 +255,10 @@ qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, c
                                  int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
                                  hipStream_t stream);
 
-/* The fused variants' RMSNorm on its own: out[b, k] = x~[b, k] as defined
+/* The fused variants' RMSNorm on its own ("Hand-Writing Gemma 4
+ * Flash-Decoding + an FP4 Matvec Bonus (Part 2)", section "The starting
+ * point": RMSNorm as a decode-step bucket of its own; "Where it landed": its
+ * fusion as the next lever): out[b, k] = x~[b, k] as defined
  * above, with r[b] summed exactly as the fused matvec sums it, so the plain
  * entry point fed `out` returns bitwise what the fused variant returns.  For
  * consumers that need the normalized activations themselves.
@@ -340,9 +356,9 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   codes of qgemv_affine_u8 (codes uint32 [n, k/4], code j of a word in
  *   bits [8j, 8j+8)).  One block is two 16-byte chunks of codes; a code c
  *   enters the 4-wide dot as the signed byte c - 128 (its top bit flipped)
- *   and the block adds 128 * scale * s back with the bias, so that
- *   y[b, r] = sum over blocks of scale*d*sum(c*q) + bias*s as for u4 (up to
- *   the fp32 rounding of 128 * scale + bias).
+ *   and 128 times the chunk's activation-code sum is added back to the
+ *   integer dot, so that y[b, r] = sum over blocks of scale*d*sum(c*q) +
+ *   bias*s exactly as for u4.
  * None of these calls allocates device memory; all are asynchronous on
  * `stream`. */
 qg_status qg_quantize_q8_1(const uint16_t *x, int64_t k, int32_t batch, int8_t *xq, uint16_t *ds,
@@ -363,10 +379,6 @@ qg_status qgemv_affine_u8_q8_fused(const uint32_t *codes, const uint16_t *scales
 /* QG_ABI_VERSION of the loaded library. */
 int qg_abi_version(void);
 
-/* Largest k a device entry point accepts for this format and batch (the
- * activation block is staged in LDS once per workgroup); 0 for a bad format
- * or batch. */
-int64_t qg_max_k(qg_format format, int32_t batch);
 
 /* ------------------------------------------------------------------------
  * Measurement
@@ -377,8 +389,9 @@ int64_t qg_max_k(qg_format format, int32_t batch);
  * lane (`unroll` in {1,2,4,8,16} loads in flight per lane) and writes one xor
  * of what each thread read to out[blocks * threads_per_block] (DEVICE).  It is
  * the reference for the achievable HBM read bandwidth that the matvec is
- * compared with: the Part 2 post ("What we'd tell the next person") proves a
- * streaming kernel's ceiling with a same-run reference kernel.
+ * compared with: "Hand-Writing Gemma 4 Flash-Decoding + an FP4 Matvec Bonus
+ * (Part 2)", section "What we'd tell the next person", proves a streaming
+ * kernel's ceiling with a same-run reference kernel.
  *   pattern 0: grid-stride rounds; 1: each wavefront streams its own
  *   contiguous range; 2: as 1 with each lane reading two adjacent 16-byte
  *   units (unroll >= 2); 3, 4, 5: patterns 0, 1, 2 with non-temporal loads.
@@ -399,7 +412,10 @@ qg_status qg_stream_probe(const void *buf, int64_t bytes, int32_t pattern, int32
  * ---------------------------------------------------------------------- */
 
 /*
- * FP4-E2M1 group-absmax quantizer.  Per group: s = bf16_rne(absmax / 6);
+ * FP4-E2M1 group-absmax quantizer ("Hand-Writing Gemma 4 Flash-Decoding + an
+ * FP4 Matvec Bonus (Part 2)", section "The assumption that failed the
+ * profiler": E2M1 codes with the sign in bit 3 and per-group scales; section
+ * "Where it landed": per-group scaling).  Per group: s = bf16_rne(absmax / 6);
  * code = nearest E2M1 value to w / s, ties to the even mantissa bit,
  * saturating at 6; sign bit set iff w < 0; s == 0 gives code 0.
  *   w       HOST float [n, k] (finite)
@@ -410,8 +426,8 @@ qg_status qg_quantize_fp4_e2m1(const float *w, int64_t n, int64_t k, int32_t gro
                                uint8_t *codes, uint16_t *scales);
 
 /*
- * Min-max affine quantizer (#683 "Step 2 result": scale and bias rounded to
- * bf16 before q is computed).  Per group: s = bf16_rne((max - min) / (2^bits-1)),
+ * Min-max affine quantizer (mlxcel issue #683, "Step 2 result": scale and
+ * bias rounded to bf16 before q is computed, self-consistent triples).  Per group: s = bf16_rne((max - min) / (2^bits-1)),
  * b = bf16_rne(min), q = clamp(rint((w - b) / s), 0, 2^bits - 1) with rint
  * rounding half to even; s == 0 gives q = 0.
  *   codes   HOST uint32 [n, k*bits/32], u32 low-first
@@ -422,7 +438,10 @@ qg_status qg_quantize_affine(const float *w, int64_t n, int64_t k, int32_t bits,
                              uint16_t *biases);
 
 /*
- * FP8-E4M3 row-absmax quantizer.  s_n = absmax_n / 448 (one binary32
+ * FP8-E4M3 row-absmax quantizer ("Hand-Writing Gemma 4 Flash-Decoding + an
+ * FP4 Matvec Bonus (Part 2)", section "The starting point": the FP8 lm_head
+ * matvec, one multiply-add per weight byte, its scale applied once per row).
+ * s_n = absmax_n / 448 (one binary32
  * division); code = nearest finite E4M3 to w / s_n (float64 quotient), ties to
  * even, saturating at 448; sign bit set iff w < 0; s_n == 0 gives code 0.
  *   codes      HOST uint8 [n, k];  row_scale  HOST float [n]
@@ -430,21 +449,25 @@ qg_status qg_quantize_affine(const float *w, int64_t n, int64_t k, int32_t bits,
 qg_status qg_quantize_fp8_e4m3_rowwise(const float *w, int64_t n, int64_t k,
                                        uint8_t *codes, float *row_scale);
 
-/* One code per byte (values < 16) <-> two per byte, even index in the low nibble.
- * count must be even. */
+/* One code per byte (values < 16) <-> two per byte, even index in the low nibble
+ * (the low-first order the mlxcel issue #683, "Step 2 result", states for
+ * u32 words, applied to the two codes of a byte).  count must be even. */
 qg_status qg_pack_nibbles(const uint8_t *one_code_per_byte, int64_t count, uint8_t *packed);
 qg_status qg_unpack_nibbles(const uint8_t *packed, int64_t count, uint8_t *one_code_per_byte);
 
-/* One code per byte (values < 2^bits) <-> u32 low-first words; bits 4 or 8;
- * count a multiple of 32/bits. */
+/* One code per byte (values < 2^bits) <-> u32 low-first words (mlxcel issue
+ * #683, "Step 2 result": affine codes packed into u32 words low-first); bits 4
+ * or 8; count a multiple of 32/bits. */
 qg_status qg_pack_u32(const uint8_t *one_code_per_byte, int64_t count, int32_t bits,
                       uint32_t *packed);
 qg_status qg_unpack_u32(const uint32_t *packed, int64_t count, int32_t bits,
                         uint8_t *one_code_per_byte);
 
 /* Bytes of one packed weight matrix (codes + scales [+ biases]), or -1 for
- * invalid arguments.  These are also the weight part of the algorithmic bytes
- * a matvec must move. */
+ * invalid arguments (mlxcel issue #683, "Step 2 result" and "Why gemma-4-12b
+ * is slow": checkpoint bytes at 8.5 and 4.5 bits per weight, which these
+ * reproduce for the 144 MLP matrices).  These are also the weight part of the
+ * algorithmic bytes a matvec must move. */
 int64_t qg_bytes_fp4(int64_t n, int64_t k, int32_t group_size);
 int64_t qg_bytes_affine(int64_t n, int64_t k, int32_t bits, int32_t group_size);
 int64_t qg_bytes_fp8(int64_t n, int64_t k);

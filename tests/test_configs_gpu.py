@@ -3,9 +3,12 @@ times (the plain entry points).
 
 For each matrix the library quantizes the seeded fp32 weights and the GPU
 computes every output.  The oracle independently re-quantizes a seeded sample
-of rows from the same seeded weights (checking the codes bit for bit) and
-computes those outputs in float64; they must meet the parity criterion.  All
-outputs must be finite and a second launch must reproduce them bitwise.
+of rows from the same seeded weights (checking the library's codes bit for
+bit), then computes every output in float64 from the packed arrays (row
+blocks of 4096 over a thread pool): every element of every config must meet
+the parity criterion, and the report (maximum error, unguarded maximum,
+elements that used the cancellation floor) is logged per config.  A second
+launch must reproduce the outputs bitwise.
 
 Workloads (weights ~ N(0, 0.02), x ~ N(0, 1) in bf16, batch 1 unless noted):
   FP4-E2M1 g32: Gemma-4-12B gate_up 30720x3840, qkv 8192x3840,
@@ -14,9 +17,13 @@ Workloads (weights ~ N(0, 0.02), x ~ N(0, 1) in bf16, batch 1 unless noted):
   FP8-E4M3 row scale: lm_head 262144x3840, batch 1 and 4
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
+from threadpoolctl import threadpool_limits
 
 import block_quantized_weight_qgemv_amd as q
 import synth
@@ -44,6 +51,29 @@ def _launch(fmt, dargs, xd, y, gs):
         q.qgemv_affine_u8(dargs[0], dargs[1], dargs[2], xd, y, gs)
     else:
         q.qgemv_fp8_e4m3(dargs[0], dargs[1], xd, y)
+
+
+def _oracle(fmt, arrays, x, gs):
+    if fmt == "fp4":
+        return G.gemv_fp4_e2m1(arrays[0], arrays[1], x, gs)
+    if fmt in ("u4", "u8"):
+        return G.gemv_affine(arrays[0], arrays[1], arrays[2], x, 4 if fmt == "u4" else 8, gs)
+    return G.gemv_fp8_e4m3(arrays[0], arrays[1], x)
+
+
+def _oracle_all_rows(fmt, arrays, x, gs, block=4096):
+    """The float64 oracle on every row of the packed arrays, 4096-row blocks
+    spread over the host cores (one BLAS thread per worker)."""
+    n = arrays[0].shape[0]
+    bounds = [(r, min(n, r + block)) for r in range(0, n, block)]
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+
+    def one(b):
+        return _oracle(fmt, [a[b[0]:b[1]] for a in arrays], x, gs)
+
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(one, bounds))
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
 
 
 def _full_size(fmt, name, batch=1, gs=None):
@@ -87,8 +117,12 @@ def _full_size(fmt, name, batch=1, gs=None):
         y_ref, a_ref = G.gemv_fp8_e4m3(ora[0], ora[1], x)
     for a_lib, a_ora in zip(arrays, ora):
         assert np.array_equal(a_lib[rows], a_ora), "library and oracle codes differ"
-    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "%s %s" % (fmt, name))
-    log("full-size %s %s: %r" % (fmt, name, r))
+    parity.assert_parity(y1[:, rows], y_ref, a_ref, "%s %s sampled" % (fmt, name))
+    # every output element against the oracle on the library's packed arrays
+    log("full-size %s %s: oracle on all %d rows" % (fmt, name, n))
+    y_all, a_all = _oracle_all_rows(fmt, arrays, x, gs)
+    r = parity.assert_parity(y1, y_all, a_all, "%s %s all rows" % (fmt, name))
+    log("full-size %s %s batch=%d: %r" % (fmt, name, batch, r))
 
 
 @pytest.mark.parametrize("name", ["gate_up", "qkv", "o_proj", "fc_down"])
@@ -137,5 +171,8 @@ def test_fp4_gemm_gemma_shapes(name, m):
     ora = Q.quantize_fp4_e2m1(synth.weight_rows(sid, n, k, rows), gs)
     assert np.array_equal(codes[rows], ora[0]) and np.array_equal(scales[rows], ora[1])
     y_ref, a_ref = G.gemv_fp4_e2m1(ora[0], ora[1], x, gs)
-    r = parity.assert_parity(y1[:, rows], y_ref, a_ref, "GEMM %s m=%d" % (name, m))
+    parity.assert_parity(y1[:, rows], y_ref, a_ref, "GEMM %s m=%d sampled" % (name, m))
+    log("full-size GEMM fp4 %s m=%d: oracle on all %d rows" % (name, m, n))
+    y_all, a_all = _oracle_all_rows("fp4", [codes, scales], x, gs)
+    r = parity.assert_parity(y1, y_all, a_all, "GEMM %s m=%d all rows" % (name, m))
     log("full-size GEMM fp4 %s m=%d: %r" % (name, m, r))

@@ -150,7 +150,7 @@ def test_graph_replay_int8_route_matches_eager_bitwise():
         a2 = [dev(a) for a in q.qg_quantize_affine(w2, 4, 64)]
         x = dev(synth.activations(230 + ci, b, k))
         xq = torch.empty((b, k), dtype=torch.int8, device="cuda:0")
-        ds = torch.empty((b, k // 32, 2), dtype=torch.float32, device="cuda:0")
+        ds = torch.empty((b, k // 32, 2), dtype=torch.int16, device="cuda:0")
         ys = [torch.empty((b, n), dtype=torch.float32, device="cuda:0") for _ in range(3)]
         cases.append((a1, a2, x, xq, ds, ys))
 
