@@ -29,14 +29,20 @@ Modules
   norm      RMSNorm of the activations rounded to bf16, the input of the
             fused norm-then-matvec variants (Part 2 post, "Where it landed").
   q8        the int8 activation route for affine 4-bit weights: activation
-            blocks of 32 with a pair {d, s}, integer block dots and the bias
-            applied through the block's activation sum ("perf(cuda):
+            blocks of 32 with an fp16 pair {d, s}, integer block dots and the
+            bias applied through the block's activation sum ("perf(cuda):
             generalize Gemma 4 batched prefill ... dense Q4_K models",
             "Item C2").
+  superblock  the two-level 4-bit super-block format (256-weight
+            super-blocks with fp16 d and dmin, 32-weight sub-blocks with
+            six-bit scale and min factors): its storage records, quantizer,
+            exact dequantization, matvec and the pre-unpacked device
+            layout (same issue, "Work Item C (C1) done", "Item C2", "All
+            work items complete").
 
 Every function is pinned by a ``-m "not gpu"`` test in ``tests/test_oracle_*``
 against closed forms, library decoders, exact rational brute force or the
 pages' own byte accounting.  Functions with no such pin say "parity unpinned".
 """
 
-from . import formats, layout, quantize, gemv, norm, q8  # noqa: F401
+from . import formats, layout, quantize, gemv, norm, q8, superblock  # noqa: F401
