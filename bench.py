@@ -79,6 +79,8 @@ def algorithmic_bytes(fmt, n, k, batch, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         w = q.qg_bytes_fp4(n, k, gs)
+    elif fmt == "q4k":
+        w = q.qg_bytes_q4k(n, k)
     elif fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f", "u8q8", "u8q8f"):
         w = q.qg_bytes_affine(n, k, 8 if fmt.startswith("u8") else 4, gs)
     else:
@@ -90,6 +92,8 @@ def quantize(fmt, w, gs):
     import block_quantized_weight_qgemv_amd as q
     if fmt == "fp4":
         return q.qg_quantize_fp4_e2m1(w, gs)
+    if fmt == "q4k":
+        return q.qg_repack_q4k(q.qg_quantize_q4k(w))
     if fmt in ("u4", "u8", "u4q8", "u4q8mv", "u4q8f", "u8q8", "u8q8f"):
         return q.qg_quantize_affine(w, 8 if fmt.startswith("u8") else 4, gs)
     return q.qg_quantize_fp8_e4m3_rowwise(w)
@@ -141,6 +145,8 @@ class Workload:
             q.qgemv_fp4_e2m1(d[0], d[1], self.x, self.y, self.gs, plan=self.plan)
         elif self.fmt == "u4":
             q.qgemv_affine_u4(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
+        elif self.fmt == "q4k":
+            q.qgemv_q4k(d[0], d[1], d[2], self.x, self.y, plan=self.plan)
         elif self.fmt == "u8":
             q.qgemv_affine_u8(d[0], d[1], d[2], self.x, self.y, self.gs, plan=self.plan)
         elif self.fmt == "u4q8f":
@@ -295,6 +301,9 @@ def run_default(args):
 SWEEP = [
     ("fp4", "gate_up", 1, 32), ("fp4", "qkv", 1, 32), ("fp4", "o_proj", 1, 32), ("fp4", "fc_down", 1, 32),
     ("u4", "mlp_up", 1, 64), ("u4", "mlp_down", 1, 64), ("u4", "llama_up", 1, 64), ("u4", "llama_down", 1, 64),
+    # the two-level super-block 4-bit format beside affine u4 g64 (pre-unpacked device layout)
+    ("q4k", "mlp_up", 1, None), ("q4k", "mlp_down", 1, None), ("q4k", "llama_up", 1, None),
+    ("q4k", "llama_down", 1, None), ("q4k", "mlp_up", 4, None),
     ("u8", "mlp_up", 1, 64), ("u8", "mlp_down", 1, 64), ("u8", "llama_up", 1, 64), ("u8", "llama_down", 1, 64),
     ("fp8", "lm_head", 1, None), ("fp8", "lm_head", 4, None), ("fp4", "tiny", 1, 32),
     # the int8 activation route for u4 (quantize + matvec, and the matvec

@@ -22,6 +22,7 @@ QG_FMT_FP4_E2M1 = _b.QG_FMT_FP4_E2M1
 QG_FMT_AFFINE_U4 = _b.QG_FMT_AFFINE_U4
 QG_FMT_AFFINE_U8 = _b.QG_FMT_AFFINE_U8
 QG_FMT_FP8_E4M3 = _b.QG_FMT_FP8_E4M3
+QG_FMT_Q4K = _b.QG_FMT_Q4K
 qg_plan = _b.qg_plan
 
 __all__ = [
@@ -32,6 +33,7 @@ __all__ = [
     "qg_quantize_fp4_e2m1", "qg_quantize_affine", "qg_quantize_fp8_e4m3_rowwise",
     "qg_pack_nibbles", "qg_unpack_nibbles", "qg_pack_u32", "qg_unpack_u32",
     "qg_bytes_fp4", "qg_bytes_affine", "qg_bytes_fp8", "lib",
+    "qgemv_q4k", "qg_quantize_q4k", "qg_repack_q4k", "qg_bytes_q4k", "qg_bytes_q4k_records", "QG_FMT_Q4K",
 ]
 
 
@@ -210,6 +212,35 @@ def _affine(name, bits, codes, scales, biases, x, y, group_size, plan, stream, g
         st = fn(cp, sp, bp, xp, gp, float(eps), yp, n, k, int(group_size), batch, out, _plan_ptr(plan),
                 _stream(stream, y.device))
         _check(st, name + "_rmsnorm")
+    return y
+
+
+def qgemv_q4k(codes, sub, sup, x, y, plan=None, stream=None, gamma=None, eps=0.0):
+    """Two-level super-block 4-bit weights in the device layout of qg_repack_q4k:
+    y[b, n] = sum_k (d*sc*q - dmin*m)[n, k] * x[b, k].
+
+    codes uint32 [n, k/8], sub uint16 [n, k/32] (sc | m << 8), sup uint32
+    [n, k/256] (fp16 d | dmin << 16), x bf16 [batch, k], y float32 or bf16.
+    With gamma (bf16 [k]) the call is the fused-RMSNorm variant.
+    """
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
+    bp = _dev_ptr(sub, "sub", (torch.int16, torch.uint16), (2,))
+    sp = _dev_ptr(sup, "sup", (torch.int32, torch.uint32), (2,))
+    n = codes.shape[0]
+    xp, yp, batch, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 8 != k or tuple(sub.shape) != (n, k // 32) or tuple(sup.shape) != (n, k // 256):
+        raise ValueError("shapes: codes %s, sub %s, sup %s, k=%d"
+                         % (tuple(codes.shape), tuple(sub.shape), tuple(sup.shape), k))
+    _same_device(codes, sub, sup, x, y)
+    if gamma is None:
+        st = _lib.qgemv_q4k_plan(cp, bp, sp, xp, yp, n, k, batch, out, _plan_ptr(plan), _stream(stream, y.device))
+        _check(st, "qgemv_q4k")
+    else:
+        gp = _gamma(gamma, k, x)
+        st = _lib.qgemv_q4k_rmsnorm(cp, bp, sp, xp, gp, float(eps), yp, n, k, batch, out, _plan_ptr(plan),
+                                    _stream(stream, y.device))
+        _check(st, "qgemv_q4k_rmsnorm")
     return y
 
 
@@ -424,6 +455,28 @@ def qg_quantize_affine(w, bits, group_size=64):
     return codes, scales, biases
 
 
+def qg_quantize_q4k(w):
+    """float32 [n, k] -> storage records uint8 [n, k/256, 144] of the two-level format."""
+    w = _host_in(w, np.float32, "w")
+    n, k = w.shape
+    rec = np.empty((n, max(k // 256, 1), 144), np.uint8)
+    _check(_lib.qg_quantize_q4k(_ptr(w), n, k, _ptr(rec)), "qg_quantize_q4k")
+    return rec
+
+
+def qg_repack_q4k(records):
+    """Storage records [n, k/256, 144] -> the device layout (codes uint32
+    [n, k/8], sub uint16 [n, k/32], sup uint32 [n, k/256])."""
+    rec = _host_in(records, np.uint8, "records")
+    n, nsb = rec.shape[0], rec.shape[1]
+    k = nsb * 256
+    codes = np.empty((n, k // 8), np.uint32)
+    sub = np.empty((n, k // 32), np.uint16)
+    sup = np.empty((n, nsb), np.uint32)
+    _check(_lib.qg_repack_q4k(_ptr(rec), n, k, _ptr(codes), _ptr(sub), _ptr(sup)), "qg_repack_q4k")
+    return codes, sub, sup
+
+
 def qg_quantize_fp8_e4m3_rowwise(w):
     """float32 [n, k] -> (codes uint8 [n, k], row_scale float32 [n])."""
     w = _host_in(w, np.float32, "w")
@@ -477,3 +530,13 @@ def qg_bytes_affine(n, k, bits, group_size=64):
 
 def qg_bytes_fp8(n, k):
     return int(_lib.qg_bytes_fp8(int(n), int(k)))
+
+
+def qg_bytes_q4k(n, k):
+    """Bytes of the super-block format's device layout (what qgemv_q4k reads)."""
+    return int(_lib.qg_bytes_q4k(int(n), int(k)))
+
+
+def qg_bytes_q4k_records(n, k):
+    """Bytes of the super-block format's storage records."""
+    return int(_lib.qg_bytes_q4k_records(int(n), int(k)))

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 # QG_ABI_VERSION of include/qgemv.h that these declarations follow; a
 # library that reports another version is refused at load.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 QG_OK = 0
 QG_OUT_F32 = 0
@@ -20,6 +20,7 @@ QG_FMT_FP4_E2M1 = 0
 QG_FMT_AFFINE_U4 = 1
 QG_FMT_AFFINE_U8 = 2
 QG_FMT_FP8_E4M3 = 3
+QG_FMT_Q4K = 4
 
 STATUS_NAMES = {
     0: "QG_OK", 1: "QG_ERR_NULL_POINTER", 2: "QG_ERR_BAD_SHAPE", 3: "QG_ERR_BAD_GROUP_SIZE",
@@ -55,6 +56,13 @@ SIGNATURES = {
     "qgemv_affine_u8_rmsnorm": (_st, [_p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _i32,
                                       _p, _p]),
     "qgemv_fp8_e4m3_rmsnorm": (_st, [_p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "qgemv_q4k": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _p]),
+    "qgemv_q4k_plan": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "qgemv_q4k_rmsnorm": (_st, [_p, _p, _p, _p, _p, ctypes.c_float, _p, _i64, _i64, _i32, _i32, _p, _p]),
+    "qg_quantize_q4k": (_st, [_p, _i64, _i64, _p]),
+    "qg_repack_q4k": (_st, [_p, _i64, _i64, _p, _p, _p]),
+    "qg_bytes_q4k_records": (_i64, [_i64, _i64]),
+    "qg_bytes_q4k": (_i64, [_i64, _i64]),
     "qg_rmsnorm_bf16": (_st, [_p, _p, ctypes.c_float, _p, _i64, _i32, _p]),
     "qgemm_fp4_e2m1": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qg_quantize_q8_1": (_st, [_p, _i64, _i32, _p, _p, _p]),

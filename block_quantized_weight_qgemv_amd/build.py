@@ -42,7 +42,7 @@ def _run(cmd):
 
 
 HIP_SOURCES = ["qgemv_api.hip", "qgemv_fp4.hip", "qgemv_affine_u4.hip", "qgemv_affine_u8.hip", "qgemv_fp8.hip",
-               "qgemm.hip", "qgemv_q8.hip"]
+               "qgemv_q4k.hip", "qgemm.hip", "qgemv_q8.hip"]
 
 
 def build(verbose=False):

@@ -8,6 +8,10 @@
 //  - min-max affine 4/8-bit, group 64, u32 low-first, with scale and bias
 //    rounded to bf16 before q is computed (mlxcel issue #683, "Step 2 result").
 //  - FP8-E4M3 with one fp32 scale per row (Part 2 post, the FP8 lm_head).
+//  - the two-level super-block 4-bit format, its storage records and the
+//    pre-unpacked device layout ("perf(cuda): generalize Gemma 4 batched
+//    prefill + flash attn + decode graphs to dense Q4_K models", sections
+//    "Work Item C (C1) done", "Item C2" and "All work items complete").
 //
 // All arithmetic is IEEE double (or the single binary32 division of the FP8
 // row scale) with one rounding per operation; this file must be built without
@@ -58,6 +62,35 @@ uint16_t bf16_rne(double v) {
     const int64_t exp_bf = static_cast<int64_t>(r >> 7) - 1023 + 127;
     if (exp_bf >= 255) return sign | 0x7F80;
     return sign | static_cast<uint16_t>((exp_bf << 7) | (r & 0x7F));
+}
+
+// Round a double to the nearest fp16, ties to even: normal results keep the
+// top 10 fraction bits of the binary64 pattern (42 bits dropped, rounded on
+// the combined exponent|fraction field); results below 2^-14 are multiples of
+// the fp16 subnormal step 2^-24; 65520 and above overflow to infinity.
+uint16_t f16_rne(double v) {
+    const uint64_t bits = f64_bits(v);
+    const uint16_t sign = static_cast<uint16_t>((bits >> 48) & 0x8000u);
+    const uint64_t mag = bits & 0x7FFFFFFFFFFFFFFFull;
+    if (mag > 0x7FF0000000000000ull) return 0x7E00;               // NaN
+    const double a = std::fabs(v);
+    if (a < 0x1p-14) {
+        const double q = std::nearbyint(a * 0x1p24);              // exact scaling
+        return sign | static_cast<uint16_t>(q);                   // 1024 -> min normal
+    }
+    const uint64_t r = (mag + ((1ull << 41) - 1) + ((mag >> 42) & 1)) >> 42;
+    const int64_t exp16 = static_cast<int64_t>(r >> 10) - 1023 + 15;
+    if (exp16 >= 31) return sign | 0x7C00;
+    return sign | static_cast<uint16_t>((exp16 << 10) | (r & 0x3FF));
+}
+
+double f16_to_double(uint16_t h) {
+    const int e = (h >> 10) & 0x1F, f = h & 0x3FF;
+    double m;
+    if (e == 0) m = std::ldexp(static_cast<double>(f), -24);
+    else if (e == 31) m = f ? NAN : INFINITY;
+    else m = std::ldexp(static_cast<double>(1024 + f), e - 25);
+    return (h & 0x8000) ? -m : m;
 }
 
 // Nearest E2M1 magnitude index (0..7) of a >= 0, ties to even mantissa bit.
@@ -265,6 +298,110 @@ qg_status qg_unpack_u32(const uint32_t *packed, int64_t count, int32_t bits, uin
     for (int64_t i = 0; i < count; ++i)
         out[i] = static_cast<uint8_t>((packed[i / per] >> (bits * (i % per))) & mask);
     return QG_OK;
+}
+
+// Two-level super-block 4-bit format: see include/qgemv.h for the record
+// layout and the rule; one super-block (256 weights, 8 sub-blocks) at a time.
+qg_status qg_quantize_q4k(const float *w, int64_t n, int64_t k, uint8_t *records) {
+    if (!w || !records) return QG_ERR_NULL_POINTER;
+    if (n < 1 || k < 256 || k % 256) return QG_ERR_BAD_SHAPE;
+    if (!all_finite(w, n * k)) return QG_ERR_BAD_VALUE;
+    const int64_t nsb = k / 256;
+    parallel_rows(n, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t b = 0; b < nsb; ++b) {
+                const float *blk = w + r * k + b * 256;
+                uint8_t *rec = records + (r * nsb + b) * 144;
+                double s[8], off[8], smax = 0.0, omax = 0.0;
+                for (int j = 0; j < 8; ++j) {
+                    float mn = blk[32 * j], mx = blk[32 * j];
+                    for (int i = 1; i < 32; ++i) {
+                        mn = std::min(mn, blk[32 * j + i]);
+                        mx = std::max(mx, blk[32 * j + i]);
+                    }
+                    const double lo = std::min(static_cast<double>(mn), 0.0);
+                    s[j] = (static_cast<double>(mx) - lo) / 15.0 + 0.0;
+                    off[j] = 0.0 - lo;
+                    smax = std::max(smax, s[j]);
+                    omax = std::max(omax, off[j]);
+                }
+                const uint16_t db = f16_rne(smax / 63.0), mb = f16_rne(omax / 63.0);
+                const double d = f16_to_double(db), dmin = f16_to_double(mb);
+                uint64_t fsc = 0, fm = 0;
+                int sc[8], m[8];
+                for (int j = 0; j < 8; ++j) {
+                    sc[j] = d > 0.0 ? static_cast<int>(std::min(std::max(std::nearbyint(s[j] / d), 0.0), 63.0)) : 0;
+                    m[j] = dmin > 0.0 ? static_cast<int>(std::min(std::max(std::nearbyint(off[j] / dmin), 0.0), 63.0))
+                                      : 0;
+                    fsc |= static_cast<uint64_t>(sc[j]) << (6 * j);
+                    fm |= static_cast<uint64_t>(m[j]) << (6 * j);
+                }
+                rec[0] = static_cast<uint8_t>(db & 0xFF);
+                rec[1] = static_cast<uint8_t>(db >> 8);
+                rec[2] = static_cast<uint8_t>(mb & 0xFF);
+                rec[3] = static_cast<uint8_t>(mb >> 8);
+                for (int i = 0; i < 6; ++i) {
+                    rec[4 + i] = static_cast<uint8_t>((fsc >> (8 * i)) & 0xFF);
+                    rec[10 + i] = static_cast<uint8_t>((fm >> (8 * i)) & 0xFF);
+                }
+                for (int j = 0; j < 8; ++j) {
+                    const double S = d * sc[j], M = dmin * m[j];            // exact
+                    for (int i = 0; i < 32; ++i) {
+                        uint8_t q = 0;
+                        if (S > 0.0) {
+                            const double t = std::nearbyint((static_cast<double>(blk[32 * j + i]) + M) / S);
+                            q = static_cast<uint8_t>(std::min(std::max(t, 0.0), 15.0));
+                        }
+                        const int col = 32 * j + i;
+                        uint8_t &byte = rec[16 + col / 2];
+                        if (col % 2 == 0) byte = q;
+                        else byte = static_cast<uint8_t>(byte | (q << 4));
+                    }
+                }
+            }
+        }
+    });
+    return QG_OK;
+}
+
+qg_status qg_repack_q4k(const uint8_t *records, int64_t n, int64_t k, uint32_t *codes, uint16_t *sub,
+                        uint32_t *super) {
+    if (!records || !codes || !sub || !super) return QG_ERR_NULL_POINTER;
+    if (n < 1 || k < 256 || k % 256) return QG_ERR_BAD_SHAPE;
+    const int64_t nsb = k / 256;
+    parallel_rows(n, [&](int64_t r0, int64_t r1) {
+        for (int64_t r = r0; r < r1; ++r) {
+            for (int64_t b = 0; b < nsb; ++b) {
+                const uint8_t *rec = records + (r * nsb + b) * 144;
+                super[r * nsb + b] = static_cast<uint32_t>(rec[0]) | (static_cast<uint32_t>(rec[1]) << 8) |
+                                     (static_cast<uint32_t>(rec[2]) << 16) | (static_cast<uint32_t>(rec[3]) << 24);
+                uint64_t fsc = 0, fm = 0;
+                for (int i = 0; i < 6; ++i) {
+                    fsc |= static_cast<uint64_t>(rec[4 + i]) << (8 * i);
+                    fm |= static_cast<uint64_t>(rec[10 + i]) << (8 * i);
+                }
+                for (int j = 0; j < 8; ++j)
+                    sub[r * (k / 32) + b * 8 + j] = static_cast<uint16_t>(((fsc >> (6 * j)) & 63) |
+                                                                          (((fm >> (6 * j)) & 63) << 8));
+                // the 128 code bytes are the 32 words of the super-block, low byte first
+                for (int wd = 0; wd < 32; ++wd)
+                    codes[r * (k / 8) + b * 32 + wd] =
+                        static_cast<uint32_t>(rec[16 + 4 * wd]) | (static_cast<uint32_t>(rec[17 + 4 * wd]) << 8) |
+                        (static_cast<uint32_t>(rec[18 + 4 * wd]) << 16) | (static_cast<uint32_t>(rec[19 + 4 * wd]) << 24);
+            }
+        }
+    });
+    return QG_OK;
+}
+
+int64_t qg_bytes_q4k_records(int64_t n, int64_t k) {
+    if (n < 1 || k < 256 || k % 256) return -1;
+    return n * (k / 256) * 144;
+}
+
+int64_t qg_bytes_q4k(int64_t n, int64_t k) {
+    if (n < 1 || k < 256 || k % 256) return -1;
+    return n * (k / 2) + n * (k / 32) * 2 + n * (k / 256) * 4;
 }
 
 int64_t qg_bytes_fp4(int64_t n, int64_t k, int32_t group_size) {

@@ -37,6 +37,7 @@ FmtInfo fmt_info(qg_format f) {
         case QG_FMT_FP4_E2M1: return {qg::FmtFP4::kWpc, qg::FmtFP4::kPieces, qg::FmtFP4::kSums};
         case QG_FMT_AFFINE_U4: return {qg::FmtAffineU4::kWpc, qg::FmtAffineU4::kPieces, qg::FmtAffineU4::kSums};
         case QG_FMT_AFFINE_U8: return {qg::FmtAffineU8::kWpc, qg::FmtAffineU8::kPieces, qg::FmtAffineU8::kSums};
+        case QG_FMT_Q4K: return {qg::FmtQ4K::kWpc, qg::FmtQ4K::kPieces, qg::FmtQ4K::kSums};
         default: return {qg::FmtFP8::kWpc, qg::FmtFP8::kPieces, qg::FmtFP8::kSums};
     }
 }
@@ -121,6 +122,8 @@ Split split_of(qg_format f, const Params &p) {
         sp.seg_groups = p.groups / segs;
         if ((int64_t(sp.seg_chunks) << 0) % (int64_t(1) << p.group_shift)) return sp;
         if (sp.seg_groups < 2 || sp.seg_groups % 2 || sp.seg_groups > 128) return sp;
+        // the two-level format: whole super-blocks of 8 groups per segment
+        if (f == QG_FMT_Q4K && sp.seg_groups % 8) return sp;
     } else {
         sp.seg_groups = 0;
     }
@@ -190,6 +193,7 @@ bool row_instance_for(qg_format f, int r, int b, int j) {
         case QG_FMT_FP4_E2M1: return row_instance_exists<qg::FmtFP4>(r, b, j);
         case QG_FMT_AFFINE_U4: return row_instance_exists<qg::FmtAffineU4>(r, b, j);
         case QG_FMT_AFFINE_U8: return row_instance_exists<qg::FmtAffineU8>(r, b, j);
+        case QG_FMT_Q4K: return row_instance_exists<qg::FmtQ4K>(r, b, j);
         default: return row_instance_exists<qg::FmtFP8>(r, b, j);
     }
 }
@@ -355,6 +359,7 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         case QG_FMT_FP4_E2M1: return qgl::launch_fp4(p, pl, batch, lds, stream);
         case QG_FMT_AFFINE_U4: return qgl::launch_affine_u4(p, pl, batch, lds, stream);
         case QG_FMT_AFFINE_U8: return qgl::launch_affine_u8(p, pl, batch, lds, stream);
+        case QG_FMT_Q4K: return qgl::launch_q4k(p, pl, batch, lds, stream);
         default: return qgl::launch_fp8(p, pl, batch, lds, stream);
     }
 }
@@ -438,6 +443,24 @@ qg_status fp8_entry(const uint8_t *codes, const float *row_scale, const uint16_t
     if ((st = set_norm(p, nm)) != QG_OK) return st;
     p.row_scale = row_scale;
     return run(QG_FMT_FP8_E4M3, p, batch, plan, stream);
+}
+
+qg_status q4k_entry(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                    void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out, const qg_plan *plan,
+                    const Norm *nm, hipStream_t stream) {
+    qg_status st = check_common(QG_FMT_Q4K, codes, x, y, n, k, batch, out);
+    if (st != QG_OK) return st;
+    if (!sub || !super) return QG_ERR_NULL_POINTER;
+    if (k % 256) return QG_ERR_BAD_SHAPE;
+    if (!aligned(sub, 2) || !aligned(super, 4)) return QG_ERR_MISALIGNED;
+    if ((st = check_plan(plan)) != QG_OK) return st;
+    Params p = base_params(QG_FMT_Q4K, codes, x, y, n, k, out);
+    if ((st = set_norm(p, nm)) != QG_OK) return st;
+    p.scales = sub;
+    p.biases = reinterpret_cast<const uint16_t *>(super);
+    p.groups = int32_t(k / 32);                 // sub-blocks: one 16-byte chunk each
+    p.group_shift = 0;
+    return run(QG_FMT_Q4K, p, batch, plan, stream);
 }
 
 }  // namespace
@@ -552,6 +575,24 @@ qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, c
     return fp8_entry(codes, row_scale, x, y, n, k, batch, out_dtype, plan, &nm, stream);
 }
 
+qg_status qgemv_q4k(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                    void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream) {
+    return q4k_entry(codes, sub, super, x, y, n, k, batch, out_dtype, nullptr, nullptr, stream);
+}
+
+qg_status qgemv_q4k_plan(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                         void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
+                         const qg_plan *plan, hipStream_t stream) {
+    return q4k_entry(codes, sub, super, x, y, n, k, batch, out_dtype, plan, nullptr, stream);
+}
+
+qg_status qgemv_q4k_rmsnorm(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                            const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k, int32_t batch,
+                            qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream) {
+    const Norm nm{gamma, eps};
+    return q4k_entry(codes, sub, super, x, y, n, k, batch, out_dtype, plan, &nm, stream);
+}
+
 qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, uint16_t *out, int64_t k,
                           int32_t batch, hipStream_t stream) {
     if (!x || !gamma || !out) return QG_ERR_NULL_POINTER;
@@ -576,7 +617,7 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
 
 qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out) {
     if (!out) return QG_ERR_NULL_POINTER;
-    if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_FP8_E4M3) return QG_ERR_BAD_DTYPE;
+    if (format < QG_FMT_FP4_E2M1 || format > QG_FMT_Q4K) return QG_ERR_BAD_DTYPE;
     if (n < 1 || k < 1 || k % fmt_info(format).wpc) return QG_ERR_BAD_SHAPE;
     if (batch < 1 || batch > 4) return QG_ERR_BAD_BATCH;
     int cus = 0;
@@ -584,7 +625,7 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     if (st != QG_OK) return st;
     // the format's usual group size, aligned parameter arrays
     Params p = base_params(format, nullptr, nullptr, nullptr, n, k, QG_OUT_F32);
-    const int gs = format == QG_FMT_FP4_E2M1 ? 32 : (format == QG_FMT_FP8_E4M3 ? 0 : 64);
+    const int gs = format == QG_FMT_FP4_E2M1 || format == QG_FMT_Q4K ? 32 : (format == QG_FMT_FP8_E4M3 ? 0 : 64);
     p.groups = gs ? int32_t(k / gs) : 0;
     p.group_shift = gs ? log2i(gs / fmt_info(format).wpc) : 0;
     p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));

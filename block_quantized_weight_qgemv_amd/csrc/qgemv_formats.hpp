@@ -9,6 +9,9 @@
 //   kSums       whether the fold needs the chunk's activation sum (affine)
 //   kAuxArrays  per-group parameter arrays (0 FP8, 1 FP4, 2 affine)
 //   kRowScale   whether rows carry one fp32 scale (FP8)
+//   kSuper      whether the second parameter array holds one 32-bit word per
+//               super-block of 8 chunks (the two-level format) instead of a
+//               16-bit value per group
 //   unit_pieces turns one raw unit of x into its kPpu pieces (reorders or
 //               widens the activations to match the decode's output order)
 //   dot         raw dot of one code chunk with the chunk's pieces
@@ -35,6 +38,7 @@ struct FmtFP4 {
     static constexpr bool kSums = false;
     static constexpr int kAuxArrays = 1;
     static constexpr bool kRowScale = false;
+    static constexpr bool kSuper = false;
 
     // piece q holds columns 8q .. 8q+7 in natural order
     __device__ static __forceinline__ void unit_pieces(uint4 v, uint4 (&out)[kPpu]) { out[0] = v; }
@@ -71,6 +75,7 @@ struct FmtAffineU4 {
     static constexpr bool kSums = true;
     static constexpr int kAuxArrays = 2;
     static constexpr bool kRowScale = false;
+    static constexpr bool kSuper = false;
 
     // piece q holds columns 8q..8q+7 reordered as (0,2),(4,6),(1,3),(5,7)
     __device__ static __forceinline__ void unit_pieces(uint4 v, uint4 (&out)[kPpu]) {
@@ -102,6 +107,31 @@ struct FmtAffineU4 {
     }
 };
 
+// Two-level super-block 4-bit codes: the codes and their decode are those of
+// the affine 4-bit format (u32 low-first nibbles); a 32-weight sub-block is
+// one 16-byte chunk, with six-bit factors sc and m (one 16-bit word,
+// sc | m << 8), and every 8 sub-blocks share a 32-bit word of fp16 d and
+// dmin (d | dmin << 16).  The sub-block's weights are d*sc*q - dmin*m, so
+// its scale is d*sc (exact in fp32: 11 x 6 bits) and its bias -dmin*m, folded
+// as the affine bias through the chunk's activation sum.
+//
+// "perf(cuda): generalize Gemma 4 batched prefill + flash attn + decode
+// graphs to dense Q4_K models", sections "Work Item C (C1) done" (the
+// d*sc*nibble - dmin*mn decode) and "All work items complete" (the
+// pre-unpacked scale layout of the decode matvec).
+struct FmtQ4K : FmtAffineU4 {
+    static constexpr bool kSuper = true;
+
+    __device__ static __forceinline__ float f16_lo(uint32_t w) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xFFFFu)));
+    }
+    // scale and bias of a sub-block from its factors and its super-block word
+    __device__ static __forceinline__ void params(uint32_t sub16, uint32_t sup, float &s, float &b) {
+        s = f16_lo(sup) * static_cast<float>(sub16 & 0xFFu);
+        b = -(f16_lo(sup >> 16) * static_cast<float>((sub16 >> 8) & 0xFFu));
+    }
+};
+
 // Min-max affine 8-bit codes, u32 low-first: bytes become f32 with the byte
 // converters and meet f32 activations.
 struct FmtAffineU8 {
@@ -112,6 +142,7 @@ struct FmtAffineU8 {
     static constexpr bool kSums = true;
     static constexpr int kAuxArrays = 2;
     static constexpr bool kRowScale = false;
+    static constexpr bool kSuper = false;
 
     // 8 bf16 (columns 8u..8u+7 of the chunk) become two f32 pieces
     __device__ static __forceinline__ void unit_pieces(uint4 v, uint4 (&out)[kPpu]) {
@@ -147,6 +178,7 @@ struct FmtFP8 {
     static constexpr bool kSums = false;
     static constexpr int kAuxArrays = 0;
     static constexpr bool kRowScale = true;
+    static constexpr bool kSuper = false;
 
     __device__ static __forceinline__ void unit_pieces(uint4 v, uint4 (&out)[kPpu]) { out[0] = v; }
 

@@ -172,6 +172,10 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // groups per segment, at most 128, starting on 4-byte boundaries).
     const int g_lo = seg * p.seg_groups;
     const int aux_off = g_lo + 2 * min(lane, p.seg_groups / 2 - 1);
+    // two-level format: the segment's super-block words, one per lane (the
+    // host guarantees whole super-blocks of 8 groups per segment)
+    const int sgroups = p.groups >> 3;                    // super-blocks per row
+    const int sup_off = (g_lo >> 3) + min(lane, (p.seg_groups >> 3) - 1);
     // (lanes past the segment's last chunk read past the resource: no access)
     auto code_off = [&](int j) {
         const int c = c_lo + kWave * j + lane;
@@ -196,10 +200,15 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
             for (int i = 0; i < R; ++i) bf.a[i][0] = buffer_param_pair(rs, uint32_t(i * p.groups + aux_off) * 2);
         }
-        if constexpr (Fmt::kAuxArrays >= 2) {
+        if constexpr (Fmt::kAuxArrays >= 2 && !Fmt::kSuper) {
             const rsrc_t rbias = make_rsrc(p.biases + rb * p.groups, pbytes);
 #pragma unroll
             for (int i = 0; i < R; ++i) bf.a[i][1] = buffer_param_pair(rbias, uint32_t(i * p.groups + aux_off) * 2);
+        }
+        if constexpr (Fmt::kSuper) {
+            const rsrc_t rsup = make_rsrc(p.biases + rb * sgroups * 2, uint32_t(valid * sgroups * 4));
+#pragma unroll
+            for (int i = 0; i < R; ++i) bf.a[i][1] = buffer_param_pair(rsup, uint32_t(i * sgroups + sup_off) * 4);
         }
         if constexpr (Fmt::kRowScale) {
 #pragma unroll
@@ -344,13 +353,19 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
                 const int src = (e >> 1) & (kWave - 1);
                 const bool hi = e & 1;
                 sv[j] = bv[j] = 0.0f;
-                if constexpr (Fmt::kAuxArrays >= 1) {
+                if constexpr (Fmt::kSuper) {
                     const uint32_t v = lane_read(bf.a[i][0], src);
-                    sv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
-                }
-                if constexpr (Fmt::kAuxArrays >= 2) {
-                    const uint32_t v = lane_read(bf.a[i][1], src);
-                    bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                    const uint32_t w = lane_read(bf.a[i][1], (e >> 3) & (kWave - 1));
+                    Fmt::params(hi ? (v >> 16) : (v & 0xFFFFu), w, sv[j], bv[j]);
+                } else {
+                    if constexpr (Fmt::kAuxArrays >= 1) {
+                        const uint32_t v = lane_read(bf.a[i][0], src);
+                        sv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                    }
+                    if constexpr (Fmt::kAuxArrays >= 2) {
+                        const uint32_t v = lane_read(bf.a[i][1], src);
+                        bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                    }
                 }
             }
             if (row0 + i < b_end) {
@@ -474,7 +489,10 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
             const int64_t row = min(row0 + i, row_hi);
             b.c[i] = load_code_chunk(p.codes + row * p.row_bytes + lane_off);
             if constexpr (Fmt::kAuxArrays >= 1) b.a[i][0] = load_param(p.scales + row * p.groups + g);
-            if constexpr (Fmt::kAuxArrays >= 2) b.a[i][1] = load_param(p.biases + row * p.groups + g);
+            if constexpr (Fmt::kSuper)
+                b.a[i][1] = load_param_pair(p.biases + (row * (p.groups >> 3) + (g >> 3)) * 2);
+            else if constexpr (Fmt::kAuxArrays >= 2)
+                b.a[i][1] = load_param(p.biases + row * p.groups + g);
             if constexpr (Fmt::kRowScale) b.rs[i] = p.row_scale[row];
         }
         if constexpr (kXGlobal) {
@@ -588,8 +606,12 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
             float s_[R], b_[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) {
-                s_[i] = Fmt::kAuxArrays >= 1 ? bf16_to_f32(bf.a[i][0]) : 0.0f;
-                b_[i] = Fmt::kAuxArrays >= 2 ? bf16_to_f32(bf.a[i][LK::NA - 1]) : 0.0f;
+                if constexpr (Fmt::kSuper) {
+                    Fmt::params(bf.a[i][0], bf.a[i][1], s_[i], b_[i]);
+                } else {
+                    s_[i] = Fmt::kAuxArrays >= 1 ? bf16_to_f32(bf.a[i][0]) : 0.0f;
+                    b_[i] = Fmt::kAuxArrays >= 2 ? bf16_to_f32(bf.a[i][LK::NA - 1]) : 0.0f;
+                }
             }
             // one batch row at a time: its pieces are live only for its own
             // dots (each accumulator's order of additions is unchanged)

@@ -122,5 +122,6 @@ qg_status launch_fp4(const Params &p, const Plan &pl, int32_t batch, int64_t lds
 qg_status launch_affine_u4(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s);
 qg_status launch_affine_u8(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s);
 qg_status launch_fp8(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s);
+qg_status launch_q4k(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s);
 
 }  // namespace qgl

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 4
+#define QG_ABI_VERSION 5
 
 typedef enum qg_status {
     QG_OK = 0,
@@ -83,7 +83,8 @@ typedef enum qg_format {
     QG_FMT_FP4_E2M1 = 0,
     QG_FMT_AFFINE_U4 = 1,
     QG_FMT_AFFINE_U8 = 2,
-    QG_FMT_FP8_E4M3 = 3
+    QG_FMT_FP8_E4M3 = 3,
+    QG_FMT_Q4K = 4
 } qg_format;
 
 /* ------------------------------------------------------------------------
@@ -161,6 +162,34 @@ qg_status qgemv_fp8_e4m3(const uint8_t *codes, const float *row_scale,
                          int64_t n, int64_t k, int32_t batch,
                          qg_out_dtype out_dtype, hipStream_t stream);
 
+/*
+ * Two-level super-block 4-bit weights ("Q4_K-style"), in the pre-unpacked
+ * device layout that qg_repack_q4k writes.  The SharpInference issue
+ * "perf(cuda): generalize Gemma 4 batched prefill + flash attn + decode
+ * graphs to dense Q4_K models", section "Work Item C (C1) done": a
+ * super-block of 256 weights decodes as d * sc * nibble - dmin * m with
+ * per-32-weight factors sc and m; section "All work items complete": a
+ * decode repack that pre-unpacks the scales lifted the matvec from 74% to
+ * 89% of HBM bandwidth.  The pages print no bit layout; the one defined here
+ * is described at qg_quantize_q4k.
+ *
+ *   codes  DEVICE uint32 [n, k/8]: code j of a word in bits [4j, 4j+4)
+ *          (as qgemv_affine_u4), 16-byte aligned
+ *   sub    DEVICE uint16 [n, k/32]: sc | m << 8 of each 32-weight sub-block
+ *          (six-bit factors, one byte each), 2-byte aligned
+ *   super  DEVICE uint32 [n, k/256]: fp16 d | fp16 dmin << 16 of each
+ *          256-weight super-block, 4-byte aligned
+ *   x, y   as for qgemv_fp4_e2m1
+ *   W^[n,k] = d * sc[j] * q[n,k] - dmin * m[j],  j = k/32 (exact in fp32:
+ *   d * sc has at most 17 significant bits), folded per sub-block as
+ *   (d*sc) * sum(q*x) - (dmin*m) * sum(x).
+ *   k % 256 == 0                                  else QG_ERR_BAD_SHAPE
+ * Everything else (batch, output, errors, accuracy, determinism, plans) as
+ * for qgemv_affine_u4.
+ */
+qg_status qgemv_q4k(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                    void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Explicit launch shape.  The plain entry points pick a launch shape from the
  * matrix shape and the device's compute-unit count.  The *_plan variants take
@@ -195,6 +224,9 @@ qg_status qgemv_fp8_e4m3_plan(const uint8_t *codes, const float *row_scale,
                               const uint16_t *x, void *y,
                               int64_t n, int64_t k, int32_t batch,
                               qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
+qg_status qgemv_q4k_plan(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                         void *y, int64_t n, int64_t k, int32_t batch, qg_out_dtype out_dtype,
+                         const qg_plan *plan, hipStream_t stream);
 
 /* The launch shape the plain entry point would use on the current device
  * (needs a HIP device for its compute-unit count, else QG_ERR_DEVICE). */
@@ -254,6 +286,9 @@ qg_status qgemv_fp8_e4m3_rmsnorm(const uint8_t *codes, const float *row_scale, c
                                  const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k,
                                  int32_t batch, qg_out_dtype out_dtype, const qg_plan *plan,
                                  hipStream_t stream);
+qg_status qgemv_q4k_rmsnorm(const uint32_t *codes, const uint16_t *sub, const uint32_t *super, const uint16_t *x,
+                            const uint16_t *gamma, float eps, void *y, int64_t n, int64_t k, int32_t batch,
+                            qg_out_dtype out_dtype, const qg_plan *plan, hipStream_t stream);
 
 /* The fused variants' RMSNorm on its own ("Hand-Writing Gemma 4
  * Flash-Decoding + an FP4 Matvec Bonus (Part 2)", section "The starting
@@ -471,6 +506,47 @@ qg_status qg_unpack_u32(const uint32_t *packed, int64_t count, int32_t bits,
 int64_t qg_bytes_fp4(int64_t n, int64_t k, int32_t group_size);
 int64_t qg_bytes_affine(int64_t n, int64_t k, int32_t bits, int32_t group_size);
 int64_t qg_bytes_fp8(int64_t n, int64_t k);
+
+/*
+ * Two-level super-block 4-bit quantizer ("perf(cuda): generalize Gemma 4
+ * batched prefill + flash attn + decode graphs to dense Q4_K models",
+ * sections "Work Item C (C1) done": the d*sc*nibble - dmin*mn decode of a
+ * 256-element super-block; "Item C2": 32-element sub-blocks with their own
+ * scale and min).  The pages print neither the packed layout nor the
+ * quantizer; this library defines them.  Storage record, 144 bytes per
+ * super-block of 256 consecutive weights of a row:
+ *   bytes 0-1 d, 2-3 dmin (fp16, little-endian); bytes 4-9 the eight six-bit
+ *   sub-block scale factors sc[0..7], sc[j] in bits 6j..6j+5 of the 48-bit
+ *   little-endian field; bytes 10-15 the eight min factors m[j], the same
+ *   way; bytes 16-143 the 256 codes, two per byte, the even weight in the
+ *   low nibble.  W^ = d*sc[j]*q - dmin*m[j].
+ * Quantization (IEEE double, one rounding per operation): per sub-block
+ * lo = min(min w, 0), s = (max w - lo)/15 + 0, off = 0 - lo; d =
+ * fp16_rne(max s / 63), dmin = fp16_rne(max off / 63); sc = clamp(rne(s/d),
+ * 0, 63), m = clamp(rne(off/dmin), 0, 63) (0 when the fp16 value is 0); q =
+ * clamp(rne((w + dmin*m)/(d*sc)), 0, 15) (0 when d*sc is 0).
+ *   w        HOST float [n, k] (finite), k % 256 == 0
+ *   records  HOST uint8 [n, k/256, 144]
+ */
+qg_status qg_quantize_q4k(const float *w, int64_t n, int64_t k, uint8_t *records);
+
+/*
+ * The decode repack of the SharpInference issue "perf(cuda): generalize
+ * Gemma 4 batched prefill + flash attn + decode graphs to dense Q4_K
+ * models" ("All work items complete": scales pre-unpacked into their own
+ * array): storage records -> the device layout
+ * of qgemv_q4k (codes uint32 [n, k/8], sub uint16 [n, k/32] = sc | m << 8,
+ * super uint32 [n, k/256] = d | dmin << 16).  All HOST pointers.
+ */
+qg_status qg_repack_q4k(const uint8_t *records, int64_t n, int64_t k, uint32_t *codes, uint16_t *sub,
+                        uint32_t *super);
+
+/* Bytes of the super-block format ("generalize Gemma 4 batched prefill ...
+ * dense Q4_K models", "All work items complete"):
+ * the storage records (4.5 bits per weight) and the device layout the matvec
+ * reads (4.625 bits per weight); -1 for invalid arguments. */
+int64_t qg_bytes_q4k_records(int64_t n, int64_t k);
+int64_t qg_bytes_q4k(int64_t n, int64_t k);
 
 #ifdef __cplusplus
 }

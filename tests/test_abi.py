@@ -220,7 +220,7 @@ def test_int8_route_u8_validation(name):
 # The *_plan variants compute what their plain call computes (cited there);
 # only the launch shape differs.
 UNCITED_PLUMBING = {"qg_status_string", "qg_abi_version", "qg_plan_query", "qgemv_fp4_e2m1_plan",
-                    "qgemv_affine_u4_plan", "qgemv_affine_u8_plan", "qgemv_fp8_e4m3_plan"}
+                    "qgemv_affine_u4_plan", "qgemv_affine_u8_plan", "qgemv_fp8_e4m3_plan", "qgemv_q4k_plan"}
 PAGE_TITLES = re.compile(r"Hand-Writing Gemma 4 Flash-Decoding \+ an FP4 Matvec Bonus \(Part 2\)|"
                          r"mlxcel issue #683|generalize Gemma 4 batched prefill")
 
@@ -241,3 +241,18 @@ def test_every_declaration_cites_its_passage():
         assert PAGE_TITLES.search(comment), "%s: no page cited" % name
         assert re.search(r'"[^"]+"', comment), "%s: no section named" % name
     assert UNCITED_PLUMBING <= set(names)
+
+
+def _q4k(codes=A, sub=A2, sup=A2, x=A3, y=A4, n=8, k=512, b=1, out=0):
+    return LIB.qgemv_q4k(codes, sub, sup, x, y, n, k, b, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"codes": None}, NULL), ({"sub": None}, NULL), ({"sup": None}, NULL), ({"x": None}, NULL),
+    ({"k": 384}, SHAPE), ({"k": 0}, SHAPE), ({"n": 0}, SHAPE), ({"codes": ODD}, MIS),
+    ({"sup": ctypes.c_void_p(0x200002)}, MIS), ({"sub": ctypes.c_void_p(0x200001)}, MIS),
+    ({"b": 0}, BATCH), ({"b": 5}, BATCH), ({"out": 2}, DTYPE),
+])
+def test_q4k_validation(kw, status):
+    # every argument error is returned before any device call
+    assert _q4k(**kw) == status

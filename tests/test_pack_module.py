@@ -109,3 +109,23 @@ def test_pack_module_errors():
     with pytest.raises(q.QgError) as e:
         q.qg_pack_nibbles(np.array([1, 16], np.uint8))
     assert e.value.name == "QG_ERR_BAD_VALUE"
+
+
+def test_q4k_quantizer_and_repack_match_oracle():
+    """The library's two-level quantizer writes the oracle's storage records
+    bit for bit, and its repack the oracle's device layout."""
+    from oracle import superblock as SB
+    golden = np.zeros((1, 256), np.float32)
+    golden[0, :32] = np.arange(32) % 16 / 4.0
+    for w in (synth.weights(11, 300, 768), _edge_weights(8, 512, 7), golden,
+              (synth.weights(12, 64, 256) * np.float32(1e-3))):   # fp16-subnormal d
+        rec = q.qg_quantize_q4k(w)
+        ref = SB.quantize_q4k(w)
+        assert np.array_equal(rec, ref)
+        for u, v in zip(q.qg_repack_q4k(rec), SB.repack_q4k(ref)):
+            assert u.dtype == v.dtype and np.array_equal(u, v)
+    assert q.qg_bytes_q4k(15360, 3840) == SB.bytes_device(15360, 3840)
+    assert q.qg_bytes_q4k_records(15360, 3840) == SB.bytes_storage(15360, 3840)
+    assert q.qg_bytes_q4k(8, 100) == -1 and q.qg_bytes_q4k_records(8, 100) == -1
+    with pytest.raises(q.QgError):
+        q.qg_quantize_q4k(np.zeros((2, 128), np.float32))          # k not a multiple of 256
