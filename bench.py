@@ -306,6 +306,9 @@ SWEEP = [
     ("q4k", "llama_down", 1, None), ("q4k", "mlp_up", 4, None),
     ("u8", "mlp_up", 1, 64), ("u8", "mlp_down", 1, 64), ("u8", "llama_up", 1, 64), ("u8", "llama_down", 1, 64),
     ("fp8", "lm_head", 1, None), ("fp8", "lm_head", 4, None), ("fp4", "tiny", 1, 32),
+    # batch 2-4 (batch 3-4 of the 4-bit formats on the matrix blocks)
+    ("fp4", "gate_up", 2, 32), ("fp4", "gate_up", 3, 32), ("fp4", "gate_up", 4, 32), ("fp4", "qkv", 4, 32),
+    ("fp4", "o_proj", 4, 32), ("fp4", "fc_down", 4, 32), ("u4", "mlp_up", 3, 64),
     # the int8 activation route for u4 (quantize + matvec, and the matvec
     # alone) beside the bf16 route, at batch 1 and 4
     ("u4q8", "mlp_up", 1, 64), ("u4q8mv", "mlp_up", 1, 64), ("u4q8", "mlp_down", 1, 64),

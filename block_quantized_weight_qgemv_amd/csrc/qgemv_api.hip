@@ -202,18 +202,21 @@ bool row_instance_for(qg_format f, int r, int b, int j) {
 // (qgemv_fp8_mfma.hpp): 4-row tiles, x in LDS.  Its default launch is one
 // workgroup of 8 waves per CU (fewer workgroups when tiles are few);
 // rows_per_tile is fixed.  It takes every k whose batch-4 activations fit its
-// LDS (k <= 16368), at batch 3 as at batch 4, so that both batch sizes of
-// the group add a row's terms in the same order; longer rows take the vector
-// kernels, as batch 1 and 2 do.
+// LDS beside the fused norm's sums (k <= 16304), at batch 3 as at batch 4 and
+// with or without the norm, so that every call of the group adds a row's
+// terms in the same order; longer rows take the vector kernels, as batch 1
+// and 2 do.
 bool fp8_mfma_takes(const Params &p) {
-    const int64_t norm_bytes = p.norm ? int64_t(4) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
+    // the fused norm's sums counted for the plain call too: both calls of a
+    // k take the same kernel, so the fused one stays bitwise the plain one's
+    const int64_t norm_bytes = int64_t(4) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4;
     return int64_t(4) * p.k * 2 + qg::kLdsSink + norm_bytes <= kMaxLds;
 }
 
 Plan fp8_default_plan(const Params &p, int cus) {
     Plan pl;
     pl.row_kernel = false;
-    pl.fp8_mfma = true;
+    pl.mfma = true;
     pl.passes = p.passes;
     pl.rows_per_tile = qg::kFp8TileRows;
     pl.waves_per_block = 8;
@@ -263,6 +266,77 @@ bool norm_row_fits(const Params &p, int32_t batch) {
     return (b + 1) * p.k * 2 + kCounterBytes + int64_t(p.segs) * b * 4 + norm_bytes <= kMaxLds;
 }
 
+// The 4-bit formats (FP4, affine u4, the two-level format) at three or four
+// activation rows run on the matrix blocks (qgemv_mfma4.hpp) where x at batch
+// 4 fits its LDS (decided by k and the norm alone, so batch 3 and 4 add a
+// row's terms in one order): 4-row tiles, one workgroup of 8 waves per CU
+// (fewer when there are fewer tiles than CUs); rows_per_tile of a plan is
+// ignored.
+bool mfma4_format(qg_format f) { return f == QG_FMT_FP4_E2M1 || f == QG_FMT_AFFINE_U4 || f == QG_FMT_Q4K; }
+
+int64_t mfma4_lds(qg_format f, const Params &p, int32_t batch) {
+    const int64_t norm_bytes = p.norm ? int64_t(batch) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4 : 0;
+    return qg::mfma4_lds_bytes(p.chunks, batch, fmt_info(f).sums) + norm_bytes;
+}
+
+// (the fused norm's sums are counted for the plain call too, as for FP8, and
+// 1 KiB is kept for the split-K partials of at least one tile).  This kernel
+// runs one workgroup per CU, so it may take all of gfx950's 160 KiB of LDS.
+constexpr int64_t kM4PartReserve = 1024;
+constexpr int64_t kM4MaxLds = 160 * 1024;
+
+bool mfma4_takes(qg_format f, const Params &p) {
+    const int64_t norm_bytes = int64_t(4) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4;
+    return mfma4_format(f) &&
+           qg::mfma4_lds_bytes(p.chunks, 4, fmt_info(f).sums) + norm_bytes + kM4PartReserve <= kM4MaxLds;
+}
+
+Plan mfma4_plan(const Params &p, int cus, const qg_plan *override_plan) {
+    Plan pl;
+    pl.row_kernel = false;
+    pl.mfma = true;
+    pl.passes = p.passes;
+    pl.rows_per_tile = qg::kM4Rows;
+    pl.waves_per_block = 8;
+    if (override_plan && override_plan->waves_per_block) pl.waves_per_block = override_plan->waves_per_block;
+    // at least one tile per workgroup (the waves split a workgroup's steps)
+    const int64_t max_blocks = (p.n + qg::kM4Rows - 1) / qg::kM4Rows;
+    int64_t blocks = int64_t(cus) * 8 / pl.waves_per_block;
+    if (override_plan && override_plan->blocks) blocks = override_plan->blocks;
+    else if (blocks > max_blocks) blocks = max_blocks;
+    pl.blocks = int(blocks < 1 ? 1 : blocks);
+    return pl;
+}
+
+qg_status run_mfma4(qg_format f, Params p, int32_t batch, const qg_plan *override_plan, hipStream_t stream, int cus) {
+    p.passes = (p.chunks + qg::kM4Slots - 1) / qg::kM4Slots;
+    Plan pl = mfma4_plan(p, cus, override_plan);
+    const int64_t base = qg::mfma4_lds_bytes(p.chunks, batch, fmt_info(f).sums);
+    const int64_t norm_bytes = mfma4_lds(f, p, batch) - base;
+    // split-K partials: [tile row][step][batch row] floats for the
+    // workgroup's tiles, when a tile has several steps; more, smaller
+    // workgroups where they would not fit
+    const int ps = qg::kM4StepPasses;
+    const int64_t steps = (p.passes + ps - 1) / ps;
+    const int64_t tiles = (p.n + qg::kM4Rows - 1) / qg::kM4Rows;
+    int64_t part_bytes = 0;
+    if (steps > 1) {
+        const int64_t per_tile = int64_t(qg::kM4Rows) * steps * batch * 4;
+        const int64_t max_tiles = (kM4MaxLds - base - norm_bytes) / per_tile;     // >= 1 (kM4PartReserve)
+        if ((tiles + pl.blocks - 1) / pl.blocks > max_tiles) pl.blocks = int((tiles + max_tiles - 1) / max_tiles);
+        part_bytes = (tiles + pl.blocks - 1) / pl.blocks * per_tile;
+    }
+    p.part_offset = int32_t(base);
+    p.norm_offset = int32_t(base + part_bytes);
+    const int64_t lds = base + part_bytes + norm_bytes;
+    p.total_waves = pl.blocks * pl.waves_per_block;
+    switch (f) {
+        case QG_FMT_FP4_E2M1: return qgl::launch_fp4(p, pl, batch, lds, stream);
+        case QG_FMT_AFFINE_U4: return qgl::launch_affine_u4(p, pl, batch, lds, stream);
+        default: return qgl::launch_q4k(p, pl, batch, lds, stream);
+    }
+}
+
 // Launch plan for the LDS kernel: the plan's rows per tile and waves, x
 // staged in LDS when it fits beside the norm's sums, read from memory with
 // the weights (one-row tiles) otherwise.
@@ -285,6 +359,7 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
     if (st != QG_OK) return st;
     if (f == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch && fp8_mfma_takes(p))
         return run_fp8(p, batch, override_plan, stream, cus);
+    if (batch >= qg::kM4MinBatch && mfma4_takes(f, p)) return run_mfma4(f, p, batch, override_plan, stream, cus);
     const Split sp = split_of(f, p);
     if (sp.ok) {
         p.segs = sp.segs;
@@ -629,6 +704,14 @@ qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, q
     p.groups = gs ? int32_t(k / gs) : 0;
     p.group_shift = gs ? log2i(gs / fmt_info(format).wpc) : 0;
     p.scales = p.biases = reinterpret_cast<const uint16_t *>(uintptr_t(256));
+    if (batch >= qg::kM4MinBatch && mfma4_takes(format, p)) {
+        p.passes = (p.chunks + qg::kM4Slots - 1) / qg::kM4Slots;
+        const Plan pl = mfma4_plan(p, cus, nullptr);
+        out->rows_per_tile = pl.rows_per_tile;
+        out->waves_per_block = pl.waves_per_block;
+        out->blocks = pl.blocks;
+        return QG_OK;
+    }
     if (format == QG_FMT_FP8_E4M3 && batch >= qg::kFp8MfmaMinBatch && fp8_mfma_takes(p)) {
         p.passes = (p.chunks + qg::kFp8Slots - 1) / qg::kFp8Slots;
         const Plan pl = fp8_default_plan(p, cus);

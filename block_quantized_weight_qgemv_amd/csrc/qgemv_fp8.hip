@@ -34,7 +34,7 @@ qg_status launch_fp8_n(const Params &p, const Plan &pl, int32_t batch, int64_t l
 }  // namespace
 
 qg_status launch_fp8(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
-    if (!pl.fp8_mfma || batch < qg::kFp8MfmaMinBatch) return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, s);
+    if (!pl.mfma || batch < qg::kFp8MfmaMinBatch) return launch_fmt<qg::FmtFP8>(p, pl, batch, lds, s);
     return p.norm ? launch_fp8_n<true>(p, pl, batch, lds, s) : launch_fp8_n<false>(p, pl, batch, lds, s);
 }
 

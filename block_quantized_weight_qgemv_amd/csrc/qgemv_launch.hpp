@@ -7,6 +7,7 @@
 #include "qgemv.h"
 #include "qgemv_device.hpp"
 #include "qgemv_kernels.hpp"
+#include "qgemv_mfma4.hpp"
 
 #include <mutex>
 
@@ -25,7 +26,7 @@ struct Plan {
     int blocks;
     bool row_kernel;       // x in registers (row kernel) or staged in LDS
     int passes;            // row kernel: passes per K segment (1, 2 or 4)
-    bool fp8_mfma = false; // FP8 at batch 3-4 on the matrix-core kernel
+    bool mfma = false;     // batch 3-4 on a matrix-core kernel (FP8, or the 4-bit formats)
 };
 
 
@@ -108,8 +109,20 @@ qg_status launch_r(const Params &p, const Plan &pl, int32_t batch, int64_t lds, 
     }
 }
 
+// The 4-bit formats at batch 3-4 on the matrix blocks (qgemv_mfma4.hpp):
+// steps of kM4StepPasses passes, kM4Depth of them in flight per wave.
+template <class Fmt, bool kNorm>
+qg_status launch_mfma4_n(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
+    if (batch == 3) return launch<qg::qgemv_mfma4_kernel<Fmt, 3, kNorm>>(p, pl, lds, s);
+    return launch<qg::qgemv_mfma4_kernel<Fmt, 4, kNorm>>(p, pl, lds, s);
+}
+
 template <class Fmt>
 qg_status launch_fmt(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
+    if constexpr (Fmt::kWpc == 32) {
+        if (pl.mfma && batch >= qg::kM4MinBatch)
+            return p.norm ? launch_mfma4_n<Fmt, true>(p, pl, batch, lds, s) : launch_mfma4_n<Fmt, false>(p, pl, batch, lds, s);
+    }
     switch (pl.rows_per_tile) {
         case 1: return launch_r<Fmt, 1>(p, pl, batch, lds, s);
         case 2: return launch_r<Fmt, 2>(p, pl, batch, lds, s);

@@ -206,13 +206,13 @@ def test_fused_norm_bitwise_across_plans_and_batch(fmt, k, gs):
         ys.append(run_norm(fmt, arrays, x, gamma, 1e-5, n, gs, plan=plan))
     for plan, y in zip(PLANS[1:], ys[1:]):
         assert np.array_equal(y, ys[0]), plan
-    if fmt != "fp8":
+    if fmt not in ("fp8", "fp4"):
         for b in range(4):
             y1 = run_norm(fmt, arrays, x[b:b + 1], gamma, 1e-5, n, gs)
             assert np.array_equal(y1[0], ys[0][b]), b
     else:
-        # FP8 sums on the vector unit below 3 activation rows and on the
-        # matrix cores from 3 on: bitwise inside each group of batch sizes
+        # FP8 and FP4 sum on the vector unit below 3 activation rows and on
+        # the matrix cores from 3 on: bitwise inside each group of batch sizes
         y2 = run_norm(fmt, arrays, x[:2], gamma, 1e-5, n, gs)
         for b in range(2):
             y1 = run_norm(fmt, arrays, x[b:b + 1], gamma, 1e-5, n, gs)
@@ -242,27 +242,28 @@ def test_fused_norm_does_not_touch_x_and_handles_a_zero_row():
 
 
 def test_fused_norm_beyond_lds():
-    """Batch 4 at k = 15360: x and gamma ((4 + 1) * k * 2 bytes) exceed 128 KiB
-    of LDS, so the LDS kernel takes the call (another order of additions):
-    it meets the widened parity bar; batch 3 still fits and stays bitwise
-    the plain call on the separately normalized x."""
-    n, k, gs = 64, 15360, 32
-    arrays = _quantize("fp4", synth.weights(35, n, k), gs)
+    """u8 at batch 4 and k = 15360: x and gamma ((4 + 1) * k * 2 bytes) exceed
+    128 KiB of LDS, so the LDS kernel takes the call (another order of
+    additions): it meets the widened parity bar; batch 3 still fits and stays
+    bitwise the plain call on the separately normalized x."""
+    n, k, gs = 64, 15360, 64
+    fmt = "u8"
+    arrays = _quantize(fmt, synth.weights(35, n, k), gs)
     x = synth.activations(35, 4, k)
     gamma = _gamma(k, 8)
     eps = 1e-5
-    log("norm beyond LDS fp4 n=%d k=%d batch=4" % (n, k))
-    y4 = run_norm("fp4", arrays, x, gamma, eps, n, gs)
+    log("norm beyond LDS u8 n=%d k=%d batch=4" % (n, k))
+    y4 = run_norm(fmt, arrays, x, gamma, eps, n, gs)
     xn = N.rmsnorm_bf16(x, gamma, eps)
     amb, other = _ambiguous(x, gamma, eps)
-    y_ref, a_ref = _oracle("fp4", arrays, xn, gs)
+    y_ref, a_ref = _oracle(fmt, arrays, xn, gs)
     dx = np.where(amb, np.abs(F.bf16_bits_to_f64(other) - F.bf16_bits_to_f64(xn)), 0.0)
-    extra = dx @ np.abs(_dequant("fp4", arrays, k, gs)).T
+    extra = dx @ np.abs(_dequant(fmt, arrays, k, gs)).T
     bar = 1e-3 * np.maximum(np.abs(y_ref), 2.0 ** -12 * a_ref) + extra
     assert np.all(np.abs(y4.astype(np.float64) - y_ref) <= bar)
-    y3 = run_norm("fp4", arrays, x[:3], gamma, eps, n, gs)
+    y3 = run_norm(fmt, arrays, x[:3], gamma, eps, n, gs)
     xg = host_bits(q.qg_rmsnorm_bf16(dev(x[:3]), dev(gamma), eps))
-    assert np.array_equal(y3, run("fp4", arrays, xg, n, gs=gs))
+    assert np.array_equal(y3, run(fmt, arrays, xg, n, gs=gs))
 
 
 def test_fused_norm_argument_errors():

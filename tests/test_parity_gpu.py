@@ -271,26 +271,32 @@ def test_zero_scale_rows_give_zero():
 
 # ---------------------------------------------------------------- bitwise consistency
 
-@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 3840), ("u4", 64, 4096), ("u8", 64, 3840), ("fp8", None, 3840)])
+# formats whose batch 3-4 runs on the matrix blocks (for rows whose x fits
+# their LDS): another order of additions than batch 1-2
+MATRIX_FROM_3 = {"fp4", "u4", "fp8"}
+
+
+@pytest.mark.parametrize("fmt,gs,k", [("fp4", 32, 3840), ("u4", 64, 4096), ("u8", 64, 3840), ("fp8", None, 3840),
+                                      ("fp4", 64, 15360), ("u4", 128, 14336)])
 def test_batch_rows_match_single_calls_bitwise(fmt, gs, k):
     n = 515
     w = synth.weights(9, n, k)
     arrays = _quantize(fmt, w, gs)
     x4 = synth.activations(9, 4, k)
-    log("batch consistency %s" % fmt)
+    log("batch consistency %s k=%d" % (fmt, k))
     y4 = run(fmt, arrays, x4, n, gs=gs)
     ys = {bsz: run(fmt, arrays, x4[:bsz], n, gs=gs) for bsz in (1, 2, 3)}
     ys[4] = y4
     singles = [run(fmt, arrays, x4[b:b + 1], n, gs=gs)[0] for b in range(4)]
-    if fmt != "fp8":
+    if fmt not in MATRIX_FROM_3:
         for b in range(4):
             assert np.array_equal(singles[b], y4[b]), (fmt, b)
         for bsz in (2, 3):
             assert np.array_equal(ys[bsz], y4[:bsz])
     else:
-        # FP8 sums on the vector unit below 3 activation rows and on the
-        # matrix cores from 3 on: bitwise inside each group, and both groups
-        # within the parity bound of the exact result
+        # the vector unit below 3 activation rows, the matrix cores from 3
+        # on: bitwise inside each group, and both groups within the parity
+        # bound of the exact result
         for b in range(2):
             assert np.array_equal(singles[b], ys[2][b]), b
         assert np.array_equal(ys[3], y4[:3])
@@ -307,7 +313,8 @@ PLANS = [None, {"rows_per_tile": 1}, {"rows_per_tile": 2}, {"rows_per_tile": 4},
 
 
 @pytest.mark.parametrize("fmt,gs,k,batch", [("fp4", 32, 3840, 2), ("u4", 64, 15360, 2), ("u8", 128, 1024, 2),
-                                            ("fp8", None, 2048, 2), ("fp8", None, 3840, 4), ("fp8", None, 5120, 3)])
+                                            ("fp8", None, 2048, 2), ("fp8", None, 3840, 4), ("fp8", None, 5120, 3),
+                                            ("fp4", 32, 3840, 4), ("u4", 64, 4096, 3), ("fp4", 128, 15360, 3)])
 def test_launch_shapes_bitwise_identical(fmt, gs, k, batch):
     n = 1001
     w = synth.weights(10, n, k)
@@ -456,8 +463,15 @@ def test_split_k_batch_and_bf16(fmt, gs, k):
     bmax = 4
     log("split-K batch/bf16 %s k=%d batch<=%d" % (fmt, k, bmax))
     yb = run(fmt, arrays, x4[:bmax], n, gs=gs)
-    for b in range(bmax):
-        assert np.array_equal(run(fmt, arrays, x4[b:b + 1], n, gs=gs)[0], yb[b])
+    # batch rows alone give their bits inside the vector group (1-2) and,
+    # for the formats that take the matrix blocks from 3 on, inside 3-4
+    y2 = run(fmt, arrays, x4[:2], n, gs=gs)
+    for b in range(2):
+        assert np.array_equal(run(fmt, arrays, x4[b:b + 1], n, gs=gs)[0], y2[b])
+    if fmt in MATRIX_FROM_3:
+        assert np.array_equal(run(fmt, arrays, x4[:3], n, gs=gs), yb[:3])
+    else:
+        assert np.array_equal(y2, yb[:2])
     y16 = run(fmt, arrays, x4[:bmax], n, gs=gs, bf16=True)
     assert np.array_equal(y16, F.f64_to_bf16_bits(yb.astype(np.float64)))
     y_ref, a_ref = _oracle(fmt, arrays, x4[:bmax], gs)
