@@ -199,15 +199,22 @@ def time_steps(launch, steps, warmup, mode="graph"):
 def cpu_baseline(wl, target_s=12.0):
     """The float64 oracle on the host cores over the same packed matrix.
 
-    Row blocks of 2048 rows are spread over one worker thread per usable core
-    (BLAS pinned to one thread per worker); whole matvecs are repeated until
-    about `target_s` seconds have passed.
+    Row blocks of 2048 rows are spread over one worker thread per core of
+    the process's CPU share (the cores it may run on, at most 16: the host
+    share of one GPU on a shared node; BLAS pinned to one thread per worker);
+    whole matvecs are repeated until about `target_s` seconds have passed.
+    The host's core counts and the numpy/BLAS builds are recorded with the
+    figure.
     """
     from concurrent.futures import ThreadPoolExecutor
-    from threadpoolctl import threadpool_limits
+    import numpy
+    from threadpoolctl import threadpool_info, threadpool_limits
     from oracle import gemv as G
 
-    cores = min(16, len(os.sched_getaffinity(0)))
+    usable = len(os.sched_getaffinity(0))
+    cores = min(16, usable)
+    blas = [{k: d.get(k) for k in ("internal_api", "version", "threading_layer", "num_threads")}
+            for d in threadpool_info() if d.get("user_api") == "blas"]
     arrays, x, n, gs = wl.host, wl.x_host, wl.n, wl.gs
     blocks = [(r, min(n, r + 2048)) for r in range(0, n, 2048)]
 
@@ -236,6 +243,8 @@ def cpu_baseline(wl, target_s=12.0):
         "kind": "oracle",
         "sample": "%d full %dx%d matvecs (same packed weights and x), float64 oracle, "
                   "%d threads over 2048-row blocks, %.1f s" % (passes, wl.n, wl.k, cores, dt),
+        "host": {"os_cpu_count": os.cpu_count(), "usable_cpus": usable, "threads": cores,
+                 "numpy": numpy.__version__, "blas": blas},
     }
 
 
@@ -318,9 +327,10 @@ SWEEP = [
     ("u4q8f", "mlp_up", 1, 64), ("u4q8f", "mlp_down", 1, 64), ("u4q8f", "llama_up", 1, 64),
     ("u4q8f", "llama_down", 1, 64), ("u4q8f", "mlp_up", 4, 64), ("u4q8f", "mlp_down", 4, 64),
     ("u4", "mlp_up", 2, 64), ("u4q8f", "mlp_up", 2, 64),
-    # the int8 route for 8-bit codes beside the bf16 route (which cannot
-    # stage 3840x15360's x at batch 4: fp32 activations exceed its LDS limit)
-    ("u8", "mlp_up", 4, 64),
+    # the int8 route for 8-bit codes beside the bf16 route (whose fp32
+    # activations at 3840x15360, batch 4, are read from memory with the
+    # weights instead of staged in LDS)
+    ("u8", "mlp_up", 4, 64), ("u8", "mlp_down", 4, 64), ("q4k", "mlp_down", 4, None),
     ("u8q8", "mlp_up", 1, 64), ("u8q8", "mlp_down", 1, 64), ("u8q8", "mlp_up", 4, 64), ("u8q8", "mlp_down", 4, 64),
     ("u8q8f", "mlp_up", 1, 64), ("u8q8f", "mlp_down", 1, 64), ("u8q8f", "mlp_up", 4, 64),
     ("u8q8f", "mlp_down", 4, 64),
@@ -340,7 +350,8 @@ def run_sweep(args):
     rows = []
     only = set(args.only.split(",")) if args.only else None
     for fmt, name, batch, gs in SWEEP:
-        if only and name not in only and "%s:%s" % (fmt, name) not in only:
+        if only and name not in only and "%s:%s" % (fmt, name) not in only \
+                and "%s:%s:%d" % (fmt, name, batch) not in only:
             continue
         wl = Workload(fmt, name, batch=batch, gs=gs, plan=parse_plan(args.plan))
         steps = args.sweep_steps or timed_steps(wl.launch, args.mode)
@@ -706,7 +717,7 @@ def main(argv=None):
     ap.add_argument("--plan", default="", help="rows_per_tile,waves_per_block,blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--only", default="", help="with --sweep: comma list of shape names or fmt:shape")
+    ap.add_argument("--only", default="", help="with --sweep: comma list of shape names, fmt:shape or fmt:shape:batch")
     ap.add_argument("--sweep-steps", type=int, default=0,
                     help="with --sweep: this many timed steps per workload (default: about 25 ms of them)")
     ap.add_argument("--out", default="")
