@@ -102,6 +102,12 @@ __device__ __forceinline__ uint32_t buffer_param_pair(rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, kCacheNonTemporal);
 }
 
+// Keeps the loads issued before it above it.  The compiler may otherwise
+// sink a prefetch's loads to their first use, past the steps consumed
+// before it, so that a wave starts with one step in flight instead of D.
+// Emits no instruction.
+__device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
 // Activations are shared by every wave: ordinary cached loads.
 __device__ __forceinline__ uint4 load_x_unit(const uint16_t *p) { return *reinterpret_cast<const uint4 *>(p); }
 

@@ -259,6 +259,7 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
         sl[d] = kH == 2 ? sl[0] : (shared ? next_tile() : d);
         issue(buf[d], sl[d], half_of(d));
     }
+    issue_fence();
     // the lane's slice of x for every pass of a tile (kH > 0)
     constexpr int kXr = kXReg ? kH * PS : 1;
     uint4 xreg[kXr][2];

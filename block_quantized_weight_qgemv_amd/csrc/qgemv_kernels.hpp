@@ -306,30 +306,32 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
                 }
         }
     }
+    // The rest of the prefetch: the tiles of buffers 1..D-1 (issued below,
+    // on the path that runs the main loop, or only the real ones when the
+    // wave has fewer tiles than buffers).
     if constexpr (!norm) {
 #pragma unroll
-        for (int d = 1; d < D; ++d) {
-            tl[d] = next_issue();
-            issue(buf[d], tl[d]);
-        }
+        for (int d = 1; d < D; ++d) tl[d] = next_issue();
     }
 
     // activation pieces (and chunk sums) in registers
     uint4 xp[B][J][Fmt::kPieces];
     float xs[B][J];
+    auto make_pieces = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < B; ++b)
+        for (int b = 0; b < B; ++b)
 #pragma unroll
-        for (int j = 0; j < J; ++j) {
+            for (int j = 0; j < J; ++j) {
 #pragma unroll
-            for (int u = 0; u < Fmt::kRawUnits; ++u) {
-                uint4 pc[Fmt::kPpu];
-                Fmt::unit_pieces(xraw[b][j][u], pc);
+                for (int u = 0; u < Fmt::kRawUnits; ++u) {
+                    uint4 pc[Fmt::kPpu];
+                    Fmt::unit_pieces(xraw[b][j][u], pc);
 #pragma unroll
-                for (int m = 0; m < Fmt::kPpu; ++m) xp[b][j][u * Fmt::kPpu + m] = pc[m];
+                    for (int m = 0; m < Fmt::kPpu; ++m) xp[b][j][u * Fmt::kPpu + m] = pc[m];
+                }
+                xs[b][j] = Fmt::kSums ? chunk_sum(xraw[b][j]) : 0.0f;
             }
-            xs[b][j] = Fmt::kSums ? chunk_sum(xraw[b][j]) : 0.0f;
-        }
+    };
 
     float acc[R][B];
 #pragma unroll
@@ -405,18 +407,45 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // edge from a middle step to the head and waited for the whole prefetch
     // at every first step).  What the last refills brought is consumed after
     // the loop, in order.
-    while (tl[D - 1] < T) {
+    //
+    // Workgroups with at least 3 tiles per wave run the D-deep pipeline from
+    // the first step: the prefetch goes out before the first tile is
+    // consumed (a fence keeps it there), which shortens the ramp (15360 x
+    // 3840 u4: 9.25 -> 8.9 us).  Left to itself the compiler sinks those
+    // loads to their first use, which measured faster with fewer tiles per
+    // wave (8192 x 3840 FP4, 2 per wave: 5.68 against 5.85 us with the
+    // fence, 6.07 one tile at a time), so the other workgroups keep that
+    // form.  Each path has its own copy of the main loop, so the compiler's
+    // waits in each count all D buffers.
+    auto run_tiles = [&]() __attribute__((always_inline)) {
+        make_pieces();
+        while (tl[D - 1] < T) {
 #pragma unroll
-        for (int d = 0; d < D; ++d) {
-            const int nt = next_issue();
-            consume(buf[d], tl[d]);
-            tl[d] = nt;
-            issue(buf[d], nt);
+            for (int d = 0; d < D; ++d) {
+                const int nt = next_issue();
+                consume(buf[d], tl[d]);
+                tl[d] = nt;
+                issue(buf[d], nt);
+            }
         }
-    }
 #pragma unroll
-    for (int d = 0; d < D - 1; ++d)
-        if (tl[d] < T) consume(buf[d], tl[d]);
+        for (int d = 0; d < D - 1; ++d)
+            if (tl[d] < T) consume(buf[d], tl[d]);
+    };
+    if (T >= 3 * G) {
+        if constexpr (!norm) {
+#pragma unroll
+            for (int d = 1; d < D; ++d) issue(buf[d], tl[d]);
+        }
+        issue_fence();
+        run_tiles();
+    } else {
+        if constexpr (!norm) {
+#pragma unroll
+            for (int d = 1; d < D; ++d) issue(buf[d], tl[d]);
+        }
+        run_tiles();
+    }
     wait_vm_loads<0>();
 
     if (S > 1) {
@@ -560,6 +589,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         // nothing to stage: the steps carry their activations
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        issue_fence();
     } else {
         constexpr int kXU = 8;
         uint4 xr[kXU], gr[kXU];
@@ -579,6 +609,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
         wait_vm_loads<R + R * Fmt::kAuxArrays + (Fmt::kRowScale ? R : 0)>();
 #pragma unroll
         for (int d = 1; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        issue_fence();
 
 #pragma unroll
         for (int i = 0; i < kXU; ++i) stage_unit(int(threadIdx.x) + i * int(blockDim.x), xr[i], gr[i]);

@@ -225,6 +225,13 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
             put_unit(base + int(threadIdx.x), v);
         }
     } else {
+        // The first step's loads go out right behind the activations', and
+        // the wave waits for the activations alone; the rest of the prefetch
+        // follows the barrier.  (Activations loaded first and waited for
+        // before any weight load, or the whole prefetch issued before the
+        // wait, both measured slower: a cold x takes 1 to 3 us to arrive
+        // either way, and the stream needs one step per wave in flight
+        // meanwhile, not more.)
         constexpr int kXu = 8;
         const int round = kXu * int(blockDim.x);
         uint4 xr[kXu];
@@ -260,6 +267,7 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
     __syncthreads();
 #pragma unroll
     for (int d = 1; d < D; ++d) issue(buf[d], i_begin + d);
+    issue_fence();
 
     // the lane's first LDS unit of a pass, less the pass's offset; a step's
     // passes past the tile's passes read the zero pass

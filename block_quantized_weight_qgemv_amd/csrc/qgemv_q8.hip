@@ -238,6 +238,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        issue_fence();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < kSX; ++i) quant_store(i * nt + tid, xv[i]);
@@ -289,6 +290,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
 
     #pragma unroll
         for (int d = 0; d < D; ++d) issue(buf[d], max(0, min(d, steps - 1)));
+        issue_fence();
         __builtin_amdgcn_sched_barrier(0);
 
     #pragma unroll
