@@ -15,6 +15,7 @@ Workloads (weights ~ N(0, 0.02), x ~ N(0, 1) in bf16, batch 1 unless noted):
                 o_proj 3840x4096, fc_down 3840x15360
   affine g64 4/8-bit: 15360x3840, 3840x15360, 14336x4096, 4096x14336
   FP8-E4M3 row scale: lm_head 262144x3840, batch 1 and 4
+  batch 4 of FP4 gate_up / fc_down and u4 15360x3840 / 3840x15360
 """
 
 import os
@@ -134,6 +135,14 @@ def test_fp4_gemma_shapes(name):
 @pytest.mark.parametrize("name", ["mlp_up", "mlp_down", "llama_up", "llama_down"])
 def test_affine_shapes(bits, name):
     _full_size("u4" if bits == 4 else "u8", name, gs=64)
+
+
+@pytest.mark.parametrize("fmt,name,gs", [("fp4", "gate_up", 32), ("fp4", "fc_down", 32),
+                                         ("u4", "mlp_up", 64), ("u4", "mlp_down", 64)])
+def test_batch4_matrix_blocks(fmt, name, gs):
+    """Batch 4 of the 4-bit formats (the 4x4x4 matrix-block kernel), every
+    row of the full-size matrix against the oracle."""
+    _full_size(fmt, name, batch=4, gs=gs)
 
 
 @pytest.mark.parametrize("batch", [1, 4])

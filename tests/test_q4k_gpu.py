@@ -133,8 +133,8 @@ def test_q4k_fused_norm_equals_plain_on_normalized_x():
     assert np.allclose(y, y_ref, rtol=1e-2, atol=1e-2 * np.max(np.abs(y_ref)))
 
 
-@pytest.mark.parametrize("name", ["mlp_up", "mlp_down"])
-def test_q4k_full_size_all_rows(name):
+@pytest.mark.parametrize("name,batch", [("mlp_up", 1), ("mlp_down", 1), ("mlp_up", 4)])
+def test_q4k_full_size_all_rows(name, batch):
     sid, n, k = synth.shape(name)
     log("q4k full-size %s [%d x %d]: generating" % (name, n, k))
     w = synth.weights(sid, n, k)
@@ -143,13 +143,13 @@ def test_q4k_full_size_all_rows(name):
     assert np.array_equal(rec[rows], SB.quantize_q4k(synth.weight_rows(sid, n, k, rows)))
     del w
     dargs = [dev(a) for a in q.qg_repack_q4k(rec)]
-    x = synth.activations(sid, 1, k)
-    log("q4k full-size %s: launching" % name)
+    x = synth.activations(sid, batch, k)
+    log("q4k full-size %s batch %d: launching" % (name, batch))
     y1 = _run(dargs, x, n)
     assert np.array_equal(_run(dargs, x, n), y1), "second launch differs"
     del dargs
     torch.cuda.empty_cache()
     log("q4k full-size %s: oracle on all %d rows" % (name, n))
     y_ref, a_ref = SB.gemv_q4k(rec, x)
-    r = parity.assert_parity(y1, y_ref, a_ref, "q4k %s all rows" % name)
-    log("q4k full-size %s: %r" % (name, r))
+    r = parity.assert_parity(y1, y_ref, a_ref, "q4k %s batch %d all rows" % (name, batch))
+    log("q4k full-size %s batch %d: %r" % (name, batch, r))
