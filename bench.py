@@ -383,17 +383,19 @@ def run_sweep(args):
 
 
 def run_qgemm_sweep(args):
-    """The small-batch GEMM (qgemm_fp4_e2m1) on the Gemma-4-12B FP4 shapes at
-    m = 8 .. 128 activation rows: algorithmic bytes (weights + scales once,
-    x, y) per launch and MFMA rate, beside the same work done by ceil(m/4)
-    launches of the batch-4 matvec (which re-reads the weights each time)."""
+    """The small-batch GEMMs (qgemm_fp4_e2m1 on the Gemma-4-12B FP4 shapes,
+    qgemm_affine_u4 on 15360x3840 and 3840x15360 g64) at m = 8 .. 128
+    activation rows: algorithmic bytes (weights + parameters once, x, y) per
+    launch and MFMA rate, beside the same work done by ceil(m/4) launches of
+    the batch-4 matvec (which re-reads the weights each time)."""
     import torch
     import block_quantized_weight_qgemv_amd as q
     import synth
     rows = []
-    for name in ("gate_up", "qkv", "fc_down"):
-        wl = Workload("fp4", name, batch=4, gs=32)
-        wbytes = q.qg_bytes_fp4(wl.n, wl.k, 32)
+    for fmt, name in (("fp4", "gate_up"), ("fp4", "qkv"), ("fp4", "fc_down"), ("u4", "mlp_up"), ("u4", "mlp_down")):
+        gs = 32 if fmt == "fp4" else 64
+        wl = Workload(fmt, name, batch=4, gs=gs)
+        wbytes = q.qg_bytes_fp4(wl.n, wl.k, gs) if fmt == "fp4" else q.qg_bytes_affine(wl.n, wl.k, 4, gs)
         sid = synth.shape(name)[0]
         for m in (8, 16, 32, 64, 128):
             x = to_dev(synth.activations(sid, m, wl.k))
@@ -401,7 +403,10 @@ def run_qgemm_sweep(args):
 
             def gemm(i):
                 d = wl.dev[i % wl.copies]
-                q.qgemm_fp4_e2m1(d[0], d[1], x, y, 32)
+                if fmt == "fp4":
+                    q.qgemm_fp4_e2m1(d[0], d[1], x, y, gs)
+                else:
+                    q.qgemm_affine_u4(d[0], d[1], d[2], x, y, gs)
 
             steps = timed_steps(gemm, args.mode)
             us = time_steps(gemm, steps, max(1, steps // 10), args.mode) / steps * 1e3
@@ -416,12 +421,12 @@ def run_qgemm_sweep(args):
 
             msteps = max(10, timed_steps(matvecs, args.mode) // 2)
             us_mv = time_steps(matvecs, msteps, max(1, msteps // 10), args.mode) / msteps * 1e3
-            rows.append({"fmt": "fp4", "shape": name, "kernel": "qgemm", "n": wl.n, "k": wl.k, "m": m,
+            rows.append({"fmt": fmt, "shape": name, "kernel": "qgemm", "n": wl.n, "k": wl.k, "m": m,
                          "bytes": nbytes, "us": round(us, 3), "GBps": round(gbs, 1),
                          "frac_8TBps": round(gbs / HBM_PEAK_GBS, 4), "mfma_TFLOPs": round(tflops, 1),
                          "matvec_b4_x%d_us" % calls: round(us_mv, 3)})
             log("%-42s %9.2f us  %8.1f GB/s  %5.1f%%  %6.1f TFLOP/s  (%d batch-4 matvecs: %.2f us)"
-                % ("qgemm fp4 %s [%dx%d] m=%d" % (name, wl.n, wl.k, m), us, gbs, 100 * gbs / HBM_PEAK_GBS,
+                % ("qgemm %s %s [%dx%d] m=%d" % (fmt, name, wl.n, wl.k, m), us, gbs, 100 * gbs / HBM_PEAK_GBS,
                    tflops, calls, us_mv))
             del x, y
         del wl

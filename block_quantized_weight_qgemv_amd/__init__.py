@@ -27,6 +27,7 @@ qg_plan = _b.qg_plan
 
 __all__ = [
     "QgError", "qgemv_fp4_e2m1", "qgemv_affine_u4", "qgemv_affine_u8", "qgemv_fp8_e4m3", "qgemm_fp4_e2m1",
+    "qgemm_affine_u4",
     "qg_quantize_q8_1", "qgemv_affine_u4_q8", "qgemv_affine_u4_q8_fused", "qgemv_affine_u8_q8",
     "qgemv_affine_u8_q8_fused",
     "qg_plan", "qg_plan_query", "qg_stream_probe", "qg_status_string", "qg_abi_version",
@@ -166,6 +167,26 @@ def qgemm_fp4_e2m1(codes, scales, x, y, group_size, stream=None):
     _same_device(codes, scales, x, y)
     st = _lib.qgemm_fp4_e2m1(cp, sp, xp, yp, n, k, int(group_size), m, out, _stream(stream, y.device))
     _check(st, "qgemm_fp4_e2m1")
+    return y
+
+
+def qgemm_affine_u4(codes, scales, biases, x, y, group_size=64, stream=None):
+    """Y[m, n] = X[m, k] . W[n, k]^T for m activation rows, W affine 4-bit as
+    in qgemv_affine_u4 (codes int32/uint32 [n, k/8], scales and biases bf16
+    [n, k/gs]); x bf16 [m, k], y float32 or bf16 [m, n]."""
+    torch = _torch()
+    cp = _dev_ptr(codes, "codes", (torch.int32, torch.uint32), (2,))
+    sp = _dev_ptr(scales, "scales", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    bp = _dev_ptr(biases, "biases", (torch.bfloat16, torch.int16, torch.uint16), (2,))
+    n = codes.shape[0]
+    xp, yp, m, k, out = _x_y(x, y, n)
+    if codes.shape[1] * 8 != k or tuple(scales.shape) != (n, k // group_size) \
+            or tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("shapes: codes %s, scales %s, biases %s, k=%d, group_size=%d"
+                         % (tuple(codes.shape), tuple(scales.shape), tuple(biases.shape), k, group_size))
+    _same_device(codes, scales, biases, x, y)
+    st = _lib.qgemm_affine_u4(cp, sp, bp, xp, yp, n, k, int(group_size), m, out, _stream(stream, y.device))
+    _check(st, "qgemm_affine_u4")
     return y
 
 

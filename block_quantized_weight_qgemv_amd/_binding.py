@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 
 # QG_ABI_VERSION of include/qgemv.h that these declarations follow; a
 # library that reports another version is refused at load.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 QG_OK = 0
 QG_OUT_F32 = 0
@@ -65,6 +65,7 @@ SIGNATURES = {
     "qg_bytes_q4k": (_i64, [_i64, _i64]),
     "qg_rmsnorm_bf16": (_st, [_p, _p, ctypes.c_float, _p, _i64, _i32, _p]),
     "qgemm_fp4_e2m1": (_st, [_p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
+    "qgemm_affine_u4": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qg_quantize_q8_1": (_st, [_p, _i64, _i32, _p, _p, _p]),
     "qgemv_affine_u4_q8": (_st, [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),
     "qgemv_affine_u4_q8_fused": (_st, [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]),

@@ -25,6 +25,7 @@
 #pragma once
 
 #include "qgemv_common.hpp"
+#include "qgemv_formats.hpp"
 
 namespace qg {
 
@@ -34,6 +35,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 struct GemmParams {
     const unsigned char *codes;    // [n, k/2]: column 2j in the low nibble of byte j
     const uint16_t *scales;        // [n, k/gs] bf16
+    const uint16_t *biases;        // [n, k/gs] bf16 (affine 4-bit codes)
     const uint16_t *x;             // [m, k] bf16
     void *y;                       // [m, n] f32 or bf16
     int64_t n;
@@ -87,7 +89,15 @@ __host__ __device__ constexpr bool gemm_double_buffer(int tb) { return tb < 4; }
 // WPS = waves per slice (4, or 1 where few row tiles would leave compute
 // units idle; the order of additions is the same).  KS depends on n and k only, so a
 // row's bits do not depend on the other activation rows.
-template <int SPG, int TB, int KS, int WPS>
+//
+// kAffine: min-max affine 4-bit codes (u32 low-first, the same nibble order
+// as FP4) with a bf16 scale and bias per group.  The masked nibbles read as
+// E4M3 are exactly q * 2^-9 (as in the matvec), in the column order (0, 2,
+// 4, 6, 1, 3, 5, 7) of each 8, so x is staged in that order too; a group
+// folds as y += (512 s) * raw + b * X, X the group's activation sum, which
+// a second MFMA chain takes with A = 1 beside the weights' chain (exact
+// products, fp32 sums, no vector work in the staging).
+template <int SPG, int TB, int KS, int WPS, bool kAffine = false>
 __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmParams p) {
     static_assert(KS * TB <= 4, "LDS holds KS chunks of 16 TB activation rows");
     constexpr int kTokens = 16 * TB;
@@ -97,7 +107,10 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     constexpr int kXUnits = 512 * TB / ST;         // 16-byte activation units per thread per chunk
     constexpr int PD = gemm_depth(TB, KS);
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
-    constexpr int BS = 8 / TB > SPG ? 8 / TB : SPG;   // MFMA steps per batch of independent chains
+    // MFMA steps per batch of independent chains (affine, at 1024 threads:
+    // half as many, its sums' chains beside them fit the 128 registers)
+    constexpr int BS0 = kAffine && 64 * WPS * KS >= 1024 ? 4 / TB : 8 / TB;
+    constexpr int BS = BS0 > SPG ? BS0 : SPG;
     constexpr int GB = BS / SPG;                   // scale groups per batch
     // LDS (dynamic, gemm_general_lds bytes): per K slice, buffers of a
     // chunk's activations and scales.  With two (DB), chunk i + 1 is staged
@@ -108,9 +121,11 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     constexpr bool DB = gemm_double_buffer(TB);
     typedef uint16_t XBuf[kTokens][kGemmKC + kGemmXPad];
     typedef uint16_t SBuf[kGemmKC / 32][RW];
+    constexpr int NB = (DB ? 2 : 1) * KS;          // buffers of each kind
     extern __shared__ __attribute__((aligned(16))) unsigned char gsmem[];
     XBuf *xsa = reinterpret_cast<XBuf *>(gsmem);                      // [2][KS]
-    SBuf *ssa = reinterpret_cast<SBuf *>(gsmem + (DB ? 2 : 1) * KS * sizeof(XBuf));   // [DB ? 2 : 1][KS]
+    SBuf *ssa = reinterpret_cast<SBuf *>(gsmem + NB * sizeof(XBuf));   // [DB ? 2 : 1][KS]
+    SBuf *bsa = ssa + NB;                                              // affine: biases, as the scales
 
     const int ks = threadIdx.x / ST;               // K slice
     const int tid = threadIdx.x % ST;              // thread in the slice
@@ -137,6 +152,7 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     uint4 wn[PD][2];                               // 16-byte pieces 4j + g of the chunk row
     uint4 xr[PD][kXUnits];
     uint16_t sr[PD][2];
+    uint16_t br[PD][kAffine ? 2 : 1];
     auto load_chunk = [&](int d, int c_in) __attribute__((always_inline)) {
         const int c = min(c_in, nch - 1);
         const int64_t kb = int64_t(c) * (kGemmKC / 2);        // byte offset of the chunk in a row
@@ -162,6 +178,7 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
             const int gg = min(c * gpc + min(grp, gpc - 1), p.groups - 1);
             const int64_t row = min(rbase + r, p.n - 1);
             sr[d][j] = p.scales[row * p.groups + gg];
+            if constexpr (kAffine) br[d][j] = p.biases[row * p.groups + gg];
         }
     };
 
@@ -190,12 +207,19 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
             const int kk = c * kGemmKC + (u & 31) * 8;
             // units past k are stored as zeros (the MFMA of a partial last
             // chunk stops at a whole group, but LDS stays defined)
-            *reinterpret_cast<uint4 *>(&xw[u >> 5][(u & 31) * 8]) = kk < p.k ? xr[d][j] : make_uint4(0, 0, 0, 0);
+            uint4 v = kk < p.k ? xr[d][j] : make_uint4(0, 0, 0, 0);
+            if constexpr (kAffine) {
+                uint4 pc[1];
+                FmtAffineU4::unit_pieces(v, pc);
+                v = pc[0];
+            }
+            *reinterpret_cast<uint4 *>(&xw[u >> 5][(u & 31) * 8]) = v;
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int e = tid + ST * j;
             sw[e / RW][e % RW] = sr[d][j];
+            if constexpr (kAffine) bsa[par * KS + ks][e / RW][e % RW] = br[d][j];
         }
     };
     if constexpr (DB) {
@@ -236,6 +260,7 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
 #pragma unroll
                 for (int s0 = 0; s0 < 8; s0 += BS) {
                     f32x4_t dd[GB][TB];
+                    f32x4_t xg[kAffine ? GB : 1][kAffine ? TB : 1];   // affine: the group's activation sums
 #pragma unroll
                     for (int gb = 0; gb < GB; ++gb) {
                         // 8 weights of row li per step, k = 32s + 8g + i: one dword, four pair conversions
@@ -243,10 +268,19 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
 #pragma unroll
                         for (int j = 0; j < SPG; ++j) {
                             const uint32_t q = wc[s0 + gb * SPG + j];
-                            const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
-                            const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
-                            const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
-                            const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                            bf16x2_t p0, p1, p2, p3;
+                            if constexpr (kAffine) {
+                                const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+                                p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+                                p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+                                p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+                                p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+                            } else {
+                                p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
+                                p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
+                                p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
+                                p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                            }
                             a[j] = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                                            __builtin_shufflevector(p2, p3, 0, 1, 2, 3),
                                                            0, 1, 2, 3, 4, 5, 6, 7);
@@ -254,14 +288,21 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
 #pragma unroll
                         for (int b = 0; b < TB; ++b) {
                             f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
+                            f32x4_t o0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                             for (int j = 0; j < SPG; ++j) {
                                 const int s = s0 + gb * SPG + j;
                                 const bf16x8_t xv =
                                     *reinterpret_cast<const bf16x8_t *>(&xs[16 * b + li][32 * s + 8 * g]);
                                 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], xv, d0, 0, 0, 0);
+                                if constexpr (kAffine) {
+                                    const bf16x8_t ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
+                                                           __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+                                    o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, xv, o0, 0, 0, 0);
+                                }
                             }
                             dd[gb][b] = d0;
+                            if constexpr (kAffine) xg[gb][b] = o0;
                         }
                     }
 #pragma unroll
@@ -270,10 +311,27 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
                         const uint2 sp = *reinterpret_cast<const uint2 *>(&ss[gi][16 * w + 4 * g]);
                         const float sc[4] = {bf16_to_f32(sp.x & 0xFFFFu), bf16_to_f32(sp.x >> 16),
                                              bf16_to_f32(sp.y & 0xFFFFu), bf16_to_f32(sp.y >> 16)};
+                        if constexpr (kAffine) {
+                            const uint2 bp =
+                                *reinterpret_cast<const uint2 *>(&bsa[par * KS + ks][gi][16 * w + 4 * g]);
+                            const float bi[4] = {bf16_to_f32(bp.x & 0xFFFFu), bf16_to_f32(bp.x >> 16),
+                                                 bf16_to_f32(bp.y & 0xFFFFu), bf16_to_f32(bp.y >> 16)};
 #pragma unroll
-                        for (int b = 0; b < TB; ++b)
+                            for (int b = 0; b < TB; ++b) {
+                                // (every element of the sums' D is activation row 16b + li's sum)
+                                const float xsg = xg[gb][b][0];
 #pragma unroll
-                            for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[v], dd[gb][b][v], acc[b][v]);
+                                for (int v = 0; v < 4; ++v) {
+                                    acc[b][v] = fmaf(sc[v] * 512.0f, dd[gb][b][v], acc[b][v]);
+                                    acc[b][v] = fmaf(bi[v], xsg, acc[b][v]);
+                                }
+                            }
+                        } else {
+#pragma unroll
+                            for (int b = 0; b < TB; ++b)
+#pragma unroll
+                                for (int v = 0; v < 4; ++v) acc[b][v] = fmaf(sc[v], dd[gb][b][v], acc[b][v]);
+                        }
                     }
                 }
             }
@@ -320,11 +378,12 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     }
 }
 
-// LDS bytes of qgemm_fp4_kernel<SPG, TB, KS, WPS>: one or two buffers per K
-// slice of a chunk's activations and scales
-__host__ __device__ constexpr int64_t gemm_general_lds(int tb, int ks, int wps) {
+// LDS bytes of qgemm_fp4_kernel<SPG, TB, KS, WPS, kAffine>: one or two
+// buffers per K slice of a chunk's activations and scales (and, affine, its
+// biases)
+__host__ __device__ constexpr int64_t gemm_general_lds(int tb, int ks, int wps, bool affine = false) {
     return (gemm_double_buffer(tb) ? 2 : 1) * int64_t(ks) *
-           (16 * tb * (kGemmKC + kGemmXPad) * 2 + (kGemmKC / 32) * 16 * wps * 2);
+           (16 * tb * (kGemmKC + kGemmXPad) * 2 + (affine ? 2 : 1) * (kGemmKC / 32) * 16 * wps * 2);
 }
 
 // ------------------------------------------------------------------ m <= 16

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define QG_ABI_VERSION 5
+#define QG_ABI_VERSION 6
 
 typedef enum qg_status {
     QG_OK = 0,
@@ -337,6 +337,27 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
 #define QG_GEMM_MAX_M 65536
 qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, void *y, int64_t n,
                          int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype, hipStream_t stream);
+
+/* The same GEMM for min-max affine 4-bit weights in the layout of
+ * qgemv_affine_u4 (codes uint32 [n, k/8] low-first, bf16 scales and biases
+ * [n, k/group_size]).  The SharpInference issue ("generalize Gemma 4 batched
+ * prefill ..."), "Item C2", runs its short-prompt GEMM on a 4-bit format with
+ * a per-sub-block minimum, folded through the activations' sums; here the
+ * codes meet bf16 activations in bf16 MFMA and each group folds as
+ * y += s * sum_{k in group} q * x + b * sum_{k in group} x, in fp32 (the
+ * decode and the activation-sum fold of the affine matvec).  The summation
+ * order depends on k and the group size only: bitwise the same for every m
+ * (row i of Y does not depend on the other rows of X), not bitwise the
+ * matvec's, and within the same 1e-3 bar against the exact sum.
+ *   codes     uint32 [n, k/8] (DEVICE), 16-byte aligned
+ *   scales, biases  bf16 [n, k/group_size] (DEVICE), 2-byte aligned
+ *   x, y, n, k, group_size, m: as for qgemm_fp4_e2m1, with the same errors
+ *   (a null biases pointer: QG_ERR_NULL_POINTER)
+ * Every m takes the kernel that stages x chunk by chunk.  No device memory
+ * is allocated; asynchronous on `stream`. */
+qg_status qgemm_affine_u4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
+                          void *y, int64_t n, int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype,
+                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Int8 activation route for affine 4-bit and 8-bit weights.

@@ -162,6 +162,21 @@ def test_qgemm_argument_errors():
     assert fn(A, A2, A3, ctypes.c_void_p(0x400002), 64, 256, 32, 8, 0, None) == MIS   # f32 y 2-byte aligned
 
 
+def test_qgemm_affine_argument_errors():
+    fn = LIB.qgemm_affine_u4
+    assert fn(None, A2, A2, A3, A4, 64, 256, 64, 8, 0, None) == NULL
+    assert fn(A, A2, None, A3, A4, 64, 256, 64, 8, 0, None) == NULL          # biases
+    assert fn(A, A2, A2, A3, A4, 0, 256, 64, 8, 0, None) == SHAPE
+    assert fn(A, A2, A2, A3, A4, 64, 272, 64, 8, 0, None) == SHAPE            # k % 32
+    assert fn(A, A2, A2, A3, A4, 64, 256, 16, 8, 0, None) == GROUP
+    assert fn(A, A2, A2, A3, A4, 64, 320, 128, 8, 0, None) == GROUP           # k % group_size
+    assert fn(A, A2, A2, A3, A4, 64, 256, 64, 0, 0, None) == BATCH
+    assert fn(A, A2, A2, A3, A4, 64, 256, 64, 65537, 0, None) == BATCH
+    assert fn(A, A2, A2, A3, A4, 64, 256, 64, 8, 2, None) == DTYPE
+    assert fn(ODD, A2, A2, A3, A4, 64, 256, 64, 8, 0, None) == MIS
+    assert fn(A, A2, ctypes.c_void_p(0x400001), A3, A4, 64, 256, 64, 8, 0, None) == MIS   # biases odd
+
+
 def _q8(codes=A, scales=A2, biases=A2, xq=A3, ds=A4, y=A4, n=8, k=128, gs=64, b=1, out=0):
     return LIB.qgemv_affine_u4_q8(codes, scales, biases, xq, ds, y, n, k, gs, b, out, None)
 
