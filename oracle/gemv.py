@@ -16,8 +16,10 @@ where x^ is the bf16 activation read exactly and W^ is the dequantized weight:
   FP8-E4M3   W^[n,k] = row_scale[n] * E4M3(code[n,k])
              (Part 2 post: the FP8 lm_head matvec applies a row scale once)
 
-This is the "FP64 host reference over the same bf16-rounded inputs" of the
-Part 2 post ("The test that catches what parity misses").  Each function also
+It is the double-precision, host-side check that the Part 2 post's section
+"The test that catches what parity misses" calls for: the GPU's inputs, as
+stored (bf16 activations, packed weights), summed without rounding error
+worth the name.  Each function also
 returns the conditioning mass A[b, n] = sum_k |W^[n,k] x^[b,k]|, which bounds
 the rounding error of any summation order and is used by the parity criterion.
 
