@@ -197,3 +197,65 @@ def test_graph_replay_int8_route_matches_eager_bitwise():
         for ci, (got, want) in enumerate(zip(outputs(), eager)):
             for j, (a, b) in enumerate(zip(got, want)):
                 assert np.array_equal(a, b), (rep, ci, j)
+
+
+def test_graph_replay_matrix_blocks_q4k_and_gemm_match_eager_bitwise():
+    """The other kernels in one captured step: FP4 and u4 at batch 3 and 4
+    (the 4x4x4 matrix-block kernel, split-K partials in LDS), the two-level
+    format at batch 1 and 4, and the affine GEMM at 24 rows.  Three replays,
+    each after the outputs were cleared outside the graph, equal the eager
+    step bitwise."""
+    calls = []
+    for bi, batch in enumerate((3, 4)):
+        w = synth.weights(230 + bi, 512, 3840)
+        codes, scales = q.qg_quantize_fp4_e2m1(w, 32)
+        x = dev(synth.activations(230 + bi, batch, 3840))
+        y = torch.empty((batch, 512), dtype=torch.float32, device="cuda:0")
+        c, s = dev(codes), dev(scales)
+        calls.append((lambda c=c, s=s, x=x, y=y: q.qgemv_fp4_e2m1(c, s, x, y, 32), y))
+        wa = synth.weights(240 + bi, 300, 15360)
+        a = [dev(t) for t in q.qg_quantize_affine(wa, 4, 64)]
+        xa = dev(synth.activations(240 + bi, batch, 15360))
+        ya = torch.empty((batch, 300), dtype=torch.float32, device="cuda:0")
+        calls.append((lambda a=a, x=xa, y=ya: q.qgemv_affine_u4(a[0], a[1], a[2], x, y, 64), ya))
+    for batch in (1, 4):
+        wq = synth.weights(250 + batch, 700, 3840)
+        dq = [dev(t) for t in q.qg_repack_q4k(q.qg_quantize_q4k(wq))]
+        xq = dev(synth.activations(250 + batch, batch, 3840))
+        yq = torch.empty((batch, 700), dtype=torch.float32, device="cuda:0")
+        calls.append((lambda d=dq, x=xq, y=yq: q.qgemv_q4k(d[0], d[1], d[2], x, y), yq))
+    wg = synth.weights(260, 1000, 4096)
+    ag = [dev(t) for t in q.qg_quantize_affine(wg, 4, 64)]
+    xg = dev(synth.activations(260, 24, 4096))
+    yg = torch.empty((24, 1000), dtype=torch.float32, device="cuda:0")
+    calls.append((lambda a=ag, x=xg, y=yg: q.qgemm_affine_u4(a[0], a[1], a[2], x, y, 64), yg))
+
+    def step():
+        for fn, _ in calls:
+            fn()
+
+    log("graph (matrix blocks, two-level, GEMM): eager step")
+    step()
+    torch.cuda.synchronize()
+    eager = [y.cpu().numpy().copy() for _, y in calls]
+    assert all(np.isfinite(e).all() for e in eager)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    scratch = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(3):
+        for _, y in calls:
+            y.zero_()
+        scratch.mul_(1.0001).add_(0.5)
+        torch.cuda.synchronize()
+        log("graph (matrix blocks, two-level, GEMM): replay %d" % rep)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, ((_, y), e) in enumerate(zip(calls, eager)):
+            assert np.array_equal(y.cpu().numpy(), e), (rep, i)
