@@ -47,12 +47,28 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // wave calls this together).  amax is a max over the four lanes; the block
 // stores d = fp16_rne(amax / 127), its codes are rne(x / d) with that stored
 // d, clamped to +-127 (0 when d is 0), and s = fp16_rne(d * sum(q)) (an
-// integer sum over the four lanes; d * sum is exact in fp32).  The quotients
-// are correctly rounded fp32 divisions: a quotient of a bf16 by 127 or by an
-// fp16 value is never within fp32 rounding of an fp16 or integer midpoint
-// unless it lies on it, so these are the exact-arithmetic decisions, and the
-// result does not depend on how the block is split.  packed holds the lane's
-// eight codes in column order; ds is the block's {d, s} word.
+// integer sum over the four lanes; d * sum is exact in fp32).  amax / 127 is
+// a correctly rounded fp32 division: a quotient of a bf16 by 127 is never
+// within fp32 rounding of an fp16 midpoint unless it lies on it.  The codes
+// come from rne_quotient below.  Every decision is the exact-arithmetic one,
+// and the result does not depend on how the block is split.  packed holds the
+// lane's eight codes in column order; ds is the block's {d, s} word.
+//
+// rne_quotient: rne(v / d) for a bf16 v and an fp16-valued d > 0 with
+// |v / d| <= 128, given r4096 = 4096 * rcp(d), rcp within an ulp of 1 / d.
+// v * r4096 is 4096 * v / d to within 2^-4.4, so its rint t is the integer
+// nearest 4096 * v / d whenever that value is not within 0.05 of a
+// half-integer, and t / 4096 is exact.  A quotient of a bf16 by an fp16 value
+// is either a half-integer or more than 2^-12 from every half-integer (write
+// both over the coarser of their last-bit units), so t / 4096 equals v / d
+// when v / d is a half-integer and lies on the same side of every
+// half-integer as v / d otherwise: its rint (ties to even) is rne(v / d).
+// (Checked exhaustively on the CPU over every fp16 d and every bf16 v in
+// range, with rcp rounded to nearest and one ulp either way.)
+__device__ __forceinline__ float rne_quotient(float v, float r4096) {
+    return __builtin_rintf(__builtin_rintf(v * r4096) * 0x1p-12f);
+}
+
 __device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[2], uint32_t &ds) {
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     float v[8];
@@ -70,13 +86,14 @@ __device__ __forceinline__ void quantize_unit(const uint4 w, uint32_t (&packed)[
     const uint32_t dh = f32_to_f16_bits(__fdiv_rn(amax, 127.0f));
     const float d = f16_bits_to_f32(dh);
     const bool live = d > 0.0f;
+    const float r4096 = __builtin_amdgcn_rcpf(live ? d : 1.0f) * 4096.0f;
     int sum = 0;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         uint32_t word = 0;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float r = live ? fminf(fmaxf(__builtin_rintf(__fdiv_rn(v[4 * h + j], d)), -127.0f), 127.0f) : 0.0f;
+            const float r = live ? fminf(fmaxf(rne_quotient(v[4 * h + j], r4096), -127.0f), 127.0f) : 0.0f;
             const int qi = int(r);
             sum += qi;
             word |= (uint32_t(qi) & 0xFFu) << (8 * j);
