@@ -402,16 +402,24 @@ __device__ __forceinline__ void store_y(const Params &p, int b, int64_t row, flo
         reinterpret_cast<float *>(p.y)[int64_t(b) * p.n + row] = out;
 }
 
-// Reduce a tile's R x B accumulators over the wave and write the R rows of y
-// (rows at or past row_end are skipped).  rs(i) is the scale applied to row i
-// (1 unless the format has per-row scales).  Zeroes acc.
+// Reduce a tile's R x B accumulators over the wave and write the first
+// `rows` rows of the tile (rows <= R, the same in every lane) to y from row0
+// on.  rs(i) is the scale applied to row i (1 unless the format has per-row
+// scales).  Zeroes acc.
 template <int R, int B, class RowScale>
-__device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B], int64_t row0, int64_t row_end,
-                                             int lane, RowScale rs) {
+__device__ __forceinline__ void reduce_store(const Params &p, float (&acc)[R][B], int64_t row0, int rows, int lane,
+                                             RowScale rs) {
     reduce_tile<R, B>(acc, lane, [&](int i, int b, float total) {
-        const int64_t row = row0 + i;
-        if (row < row_end) store_y(p, b, row, total * rs(i));
+        if (i < rows) store_y(p, b, row0 + i, total * rs(i));
     });
+}
+
+// rows of a tile of R rows starting at row0 that lie before row_end (0..R);
+// row0 and row_end are uniform
+template <int R>
+__device__ __forceinline__ int tile_rows(int64_t row0, int64_t row_end) {
+    const int64_t d = row_end - row0;
+    return d < R ? (d > 0 ? int(d) : 0) : R;
 }
 
 }  // namespace qg

@@ -102,7 +102,8 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     const int G = (blockDim.x >> 6) / S;
     const int gw = w / S, seg = w - gw * S;     // wave gw of segment seg
     const int64_t b_rows = b_end - b_begin;
-    const int T = int((b_rows + R - 1) / R);
+    const int brows = int(b_rows);                        // rows of the workgroup (< 2^31)
+    const int T = (brows + R - 1) / R;
     const int c_lo = seg * p.seg_chunks;
     const int c_hi = min(p.chunks, c_lo + p.seg_chunks);
 
@@ -187,7 +188,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         // through a loop over its distinct values)
         const int t = __builtin_amdgcn_readfirstlane(t_in);
         const int64_t row0 = b_begin + int64_t(t) * R;
-        const int64_t valid = t < T ? min(int64_t(R), b_end - row0) : 0;
+        const int valid = t < T ? min(R, brows - t * R) : 0;
         const int64_t rb = valid ? row0 : 0;
         const rsrc_t rc = make_rsrc(p.codes + rb * p.row_bytes, uint32_t(valid * p.row_bytes));
 #pragma unroll
@@ -343,34 +344,77 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
     // behind the staged activations
     float *part = reinterpret_cast<float *>(smem + p.part_offset);
 
+    // Where the group parameters of this lane's chunk in each pass sit: the
+    // lane whose dword holds them, and a byte selector that moves the right
+    // 16-bit half of that dword to the top of a word (a bf16 parameter as
+    // fp32) or, for the two-level format's factors, to the bottom: one v_perm
+    // per parameter in place of a shift, a mask and a select.  The selectors
+    // take a register per pass; instances whose activations already fill the
+    // register file (more than one batch row with chunk sums) select in the
+    // loop instead.
+    constexpr bool kSelPerm = B == 1 || !Fmt::kSums;
+    constexpr int JS = kSelPerm ? J : 1;
+    int psrc[JS], psup[JS];
+    uint32_t psel[JS];
+    if constexpr (kSelPerm) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int e = ((c_lo + kWave * j + lane) >> p.group_shift) - g_lo;   // group in the segment
+            psrc[j] = (e >> 1) & (kWave - 1);
+            psup[j] = (e >> 3) & (kWave - 1);
+            if constexpr (Fmt::kSuper)
+                psel[j] = (e & 1) ? 0x0c0c0302u : 0x0c0c0100u;
+            else
+                psel[j] = (e & 1) ? 0x03020c0cu : 0x01000c0cu;
+        }
+    }
+
     auto consume = [&](const Buf &bf, int t) __attribute__((always_inline)) {
         const int64_t row0 = b_begin + int64_t(t) * R;
+        const int rows = min(R, brows - t * R);            // rows of the tile in the workgroup's range
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             // group parameters of this lane's chunk in every pass
             float sv[J], bv[J];
 #pragma unroll
             for (int j = 0; j < J; ++j) {
-                const int e = ((c_lo + kWave * j + lane) >> p.group_shift) - g_lo;   // group in the segment
-                const int src = (e >> 1) & (kWave - 1);
-                const bool hi = e & 1;
                 sv[j] = bv[j] = 0.0f;
-                if constexpr (Fmt::kSuper) {
-                    const uint32_t v = lane_read(bf.a[i][0], src);
-                    const uint32_t w = lane_read(bf.a[i][1], (e >> 3) & (kWave - 1));
-                    Fmt::params(hi ? (v >> 16) : (v & 0xFFFFu), w, sv[j], bv[j]);
-                } else {
-                    if constexpr (Fmt::kAuxArrays >= 1) {
-                        const uint32_t v = lane_read(bf.a[i][0], src);
-                        sv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                if constexpr (kSelPerm) {
+                    if constexpr (Fmt::kSuper) {
+                        const uint32_t v = lane_read(bf.a[i][0], psrc[j]);
+                        const uint32_t w = lane_read(bf.a[i][1], psup[j]);
+                        Fmt::params(__builtin_amdgcn_perm(v, v, psel[j]), w, sv[j], bv[j]);
+                    } else {
+                        if constexpr (Fmt::kAuxArrays >= 1) {
+                            const uint32_t v = lane_read(bf.a[i][0], psrc[j]);
+                            sv[j] = __uint_as_float(__builtin_amdgcn_perm(v, v, psel[j]));
+                        }
+                        if constexpr (Fmt::kAuxArrays >= 2) {
+                            const uint32_t v = lane_read(bf.a[i][1], psrc[j]);
+                            bv[j] = __uint_as_float(__builtin_amdgcn_perm(v, v, psel[j]));
+                        }
                     }
-                    if constexpr (Fmt::kAuxArrays >= 2) {
-                        const uint32_t v = lane_read(bf.a[i][1], src);
-                        bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                } else {
+                    const int e = ((c_lo + kWave * j + lane) >> p.group_shift) - g_lo;   // group in the segment
+                    const int src = (e >> 1) & (kWave - 1);
+                    const bool hi = e & 1;
+                    if constexpr (Fmt::kSuper) {
+                        const uint32_t v = lane_read(bf.a[i][0], src);
+                        const uint32_t w = lane_read(bf.a[i][1], (e >> 3) & (kWave - 1));
+                        Fmt::params(hi ? (v >> 16) : (v & 0xFFFFu), w, sv[j], bv[j]);
+                    } else {
+                        if constexpr (Fmt::kAuxArrays >= 1) {
+                            const uint32_t v = lane_read(bf.a[i][0], src);
+                            sv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                        }
+                        if constexpr (Fmt::kAuxArrays >= 2) {
+                            const uint32_t v = lane_read(bf.a[i][1], src);
+                            bv[j] = __uint_as_float(hi ? (v & 0xFFFF0000u) : (v << 16));
+                        }
                     }
                 }
             }
-            if (row0 + i < b_end) {
+            if (i < rows) {
 #pragma unroll
                 for (int j = 0; j < J; ++j) {
                     if (c_lo + kWave * j + lane < c_hi) {
@@ -384,14 +428,13 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             }
         }
         if (S == 1) {
-            reduce_store<R, B>(p, acc, row0, b_end, lane, [&](int i) {
+            reduce_store<R, B>(p, acc, row0, rows, lane, [&](int i) {
                 if constexpr (Fmt::kRowScale) return pick_uniform(bf.rs, i);
                 return 1.0f;
             });
         } else {
             reduce_tile<R, B>(acc, lane, [&](int i, int b, float total) {
-                const int64_t row = row0 + i;
-                if (row < b_end) part[((row - b_begin) * S + seg) * B + b] = total;
+                if (i < rows) part[((t * R + i) * S + seg) * B + b] = total;
             });
         }
     };
@@ -679,7 +722,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
             }
         }
         if (j == passes - 1) {
-            reduce_store<R, B>(p, acc, row0, r_end, lane, [&](int i) {
+            reduce_store<R, B>(p, acc, row0, tile_rows<R>(row0, r_end), lane, [&](int i) {
                 if constexpr (Fmt::kRowScale) return pick_uniform(bf.rs, i);
                 return 1.0f;
             });

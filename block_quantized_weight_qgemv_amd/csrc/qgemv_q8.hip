@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(512) qgemv_affine_q8_kernel(const Params p, co
                 }
             }
         }
-        if (j == passes - 1) reduce_store<R, B>(p, acc, row0, r_end, lane, [](int) { return 1.0f; });
+        if (j == passes - 1) reduce_store<R, B>(p, acc, row0, tile_rows<R>(row0, r_end), lane, [](int) { return 1.0f; });
     };
 
     run_pipeline<D>(buf, steps, issue, consume);
