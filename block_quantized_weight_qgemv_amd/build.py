@@ -26,6 +26,10 @@ HIP_FLAGS = [
     "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
     # no packed fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary vector registers: left to itself the compiler
+    # put the GEMM's in accumulation registers and read every result back
+    # with one v_accvgpr_read per element (a quarter of the GEMM's VALU work)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",

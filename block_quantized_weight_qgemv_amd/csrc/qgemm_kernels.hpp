@@ -50,8 +50,12 @@ constexpr int kGemmXPad = 8;       // LDS row padding (bf16) against bank confli
 
 // chunks in flight per lane: the register ring holds PD chunks' loads (two
 // with four K slices: 16 waves per workgroup hide the latency, and a deeper
-// ring would not fit the 128 registers a 1024-thread workgroup leaves)
-constexpr int gemm_depth(int tb, int ks) { return ks == 4 ? 2 : (tb == 1 ? 4 : (tb == 2 ? 3 : 2)); }
+// ring would not fit the 128 registers a 1024-thread workgroup leaves; one
+// for the affine codes with 64 activation rows, whose second ring set, the
+// sums' chains and the MFMA results would not fit 256 vector registers)
+constexpr int gemm_depth(int tb, int ks, bool affine = false) {
+    return ks == 4 ? 2 : (tb == 1 ? 4 : (tb == 2 ? 3 : (affine ? 1 : 2)));
+}
 
 // Exchange of a 4 x 4 block of dwords among lanes l, l + 16, l + 32, l + 48
 // (index g = l >> 4): lane g's d[r] becomes lane r's d[g] before.  Two
@@ -105,7 +109,7 @@ __global__ void __launch_bounds__(64 * WPS * KS) qgemm_fp4_kernel(const GemmPara
     constexpr int RW = 16 * WPS;                   // weight rows per workgroup
     static_assert((512 * TB) % ST == 0, "whole activation units per thread");
     constexpr int kXUnits = 512 * TB / ST;         // 16-byte activation units per thread per chunk
-    constexpr int PD = gemm_depth(TB, KS);
+    constexpr int PD = gemm_depth(TB, KS, kAffine);
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
     // MFMA steps per batch of independent chains (affine, at 1024 threads:
     // half as many, its sums' chains beside them fit the 128 registers)
