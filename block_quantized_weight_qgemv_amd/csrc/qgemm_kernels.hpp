@@ -407,7 +407,7 @@ __host__ __device__ constexpr int64_t gemm_general_lds(int tb, int ks, int wps, 
 // operands of a group are the same values in both kernels.  So a row's bits
 // are the same whichever kernel, m or launch computes it.
 constexpr int kGemmSmallWaves = 8;                 // most waves per workgroup
-constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane
+constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane (8 measured slower)
 
 // VS: a chunk's gpc group scales of a row are read as one vector (they are
 // aligned to 2 * gpc bytes when the groups per row are a multiple of gpc).
@@ -423,31 +423,6 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
     const int nch = (p.k + kGemmKC - 1) / kGemmKC;
     const int xstride = nch * kGemmKC + kGemmXPad; // bf16 per staged activation row
     const int64_t row_bytes = p.k / 2;
-
-    // x -> LDS once: m rows, zeros from k to the end of the last chunk;
-    // kStage loads in flight per thread (one at a time, every thread would
-    // wait out the load latency once per unit)
-    constexpr int kStage = 16;
-    const int upr = xstride / 8;                   // 16-byte units per staged row
-    const int units = p.m * upr;
-    for (int u0 = threadIdx.x; u0 < units; u0 += kStage * int(blockDim.x)) {
-        uint4 v[kStage];
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int u = min(u0 + i * int(blockDim.x), units - 1);
-            const int t = u / upr, ku = (u - t * upr) * 8;
-            v[i] = load_x_unit(p.x + int64_t(t) * p.k + min(ku, p.k - 8));
-        }
-#pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const int u = u0 + i * int(blockDim.x);
-            if (u < units) {
-                const int t = u / upr, ku = (u - t * upr) * 8;
-                *reinterpret_cast<uint4 *>(xs + t * xstride + ku) = ku < p.k ? v[i] : make_uint4(0u, 0u, 0u, 0u);
-            }
-        }
-    }
-    __syncthreads();
 
     // 16-row tiles split evenly over the grid's waves (contiguous ranges);
     // a wave's items are its tiles' chunks in order
@@ -595,6 +570,35 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
         sl[d] = d;
         issue(buf[d], d);
     }
+    // (the ring's weight loads go out first: they do not depend on x, and
+    // arrive while x is staged; the fence keeps the compiler from sinking
+    // them to their first use)
+    issue_fence();
+    // x -> LDS once: m rows, zeros from k to the end of the last chunk;
+    // kStage loads in flight per thread (one at a time, every thread would
+    // wait out the load latency once per unit)
+    constexpr int kStage = 16;
+    const int upr = xstride / 8;                   // 16-byte units per staged row
+    const int units = p.m * upr;
+    for (int u0 = threadIdx.x; u0 < units; u0 += kStage * int(blockDim.x)) {
+        uint4 v[kStage];
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int u = min(u0 + i * int(blockDim.x), units - 1);
+            const int t = u / upr, ku = (u - t * upr) * 8;
+            v[i] = load_x_unit(p.x + int64_t(t) * p.k + min(ku, p.k - 8));
+        }
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int u = u0 + i * int(blockDim.x);
+            if (u < units) {
+                const int t = u / upr, ku = (u - t * upr) * 8;
+                *reinterpret_cast<uint4 *>(xs + t * xstride + ku) = ku < p.k ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+    }
+    __syncthreads();
+
     while (sl[PD - 1] < items) {
 #pragma unroll
         for (int d = 0; d < PD; ++d) {
