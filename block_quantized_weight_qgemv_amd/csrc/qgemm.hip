@@ -75,6 +75,49 @@ qg_status gemm_general(const qg::GemmParams &p, int spg, int ks, hipStream_t str
     return QG_ERR_LAUNCH;     // not reached: every (group size, tb, ks, wps) above has an instance
 }
 
+// Up to 16 activation rows whose x fits in LDS: x staged once per
+// workgroup, weight tiles streamed without barriers (the same bits as the
+// general kernel)
+bool gemm_small_fits(int64_t k, int32_t m) { return m <= 16 && qg::gemm_small_lds(k, m) <= 128 * 1024; }
+
+template <bool kAffine>
+qg_status gemm_small(const qg::GemmParams &p, int spg, int ks, hipStream_t stream) {
+    const int cus = device_cus();
+    if (cus < 1) return QG_ERR_DEVICE;
+    const int64_t small_lds = qg::gemm_small_lds(p.k, p.m);
+    // one workgroup per CU (x fills most of its LDS), with as many waves as
+    // the 16-row tiles need to cover the chip, 1..8
+    const int64_t rtiles = (p.n + 15) / 16;
+    int64_t wpb = (rtiles + cus - 1) / cus;
+    wpb = wpb < 1 ? 1 : (wpb > qg::kGemmSmallWaves ? qg::kGemmSmallWaves : wpb);
+    int64_t blocks = (rtiles + wpb - 1) / wpb;
+    if (blocks > cus) blocks = cus;
+    const dim3 sgrid{unsigned(blocks)}, sblock{unsigned(64 * wpb)};
+    // a chunk's group parameters as one vector load when they are aligned
+    const int gpc = 8 / spg;
+    const uintptr_t va = uintptr_t(2 * gpc);
+    const bool vs = p.groups % gpc == 0 && aligned_to(p.scales, va) && (!kAffine || aligned_to(p.biases, va));
+#define QG_GEMM_SMALL(S, K, V)                                                                          \
+    if (spg == S && ks == K && vs == V) {                                                               \
+        auto kern = qg::qgemm_fp4_small_kernel<S, K, V, kAffine>;                                       \
+        static std::once_flag once;                                                                     \
+        static hipError_t attr = hipSuccess;                                                            \
+        std::call_once(once, [kern] {                                                                   \
+            attr = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                            \
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);         \
+        });                                                                                             \
+        if (attr != hipSuccess) return QG_ERR_LAUNCH;                                                   \
+        return qgl::launch_kernel(kern, sgrid, sblock, size_t(small_lds), stream, p);                   \
+    }
+#define QG_GEMM_SMALL_V(S, K) QG_GEMM_SMALL(S, K, true) QG_GEMM_SMALL(S, K, false)
+    QG_GEMM_SMALL_V(1, 1) QG_GEMM_SMALL_V(1, 2) QG_GEMM_SMALL_V(1, 4)
+    QG_GEMM_SMALL_V(2, 1) QG_GEMM_SMALL_V(2, 2) QG_GEMM_SMALL_V(2, 4)
+    QG_GEMM_SMALL_V(4, 1) QG_GEMM_SMALL_V(4, 2) QG_GEMM_SMALL_V(4, 4)
+#undef QG_GEMM_SMALL_V
+#undef QG_GEMM_SMALL
+    return QG_ERR_LAUNCH;     // not reached: every (group size, ks, vector load) above has an instance
+}
+
 // the arguments both GEMMs share, checked before any HIP call
 qg_status gemm_check(const void *codes, const uint16_t *scales, const uint16_t *x, void *y, int64_t n, int64_t k,
                      int32_t group_size, int32_t m, qg_out_dtype out_dtype) {
@@ -117,43 +160,7 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
     const qg::GemmParams p = gemm_params(codes, scales, x, y, n, k, group_size, m, out_dtype);
     const int ks = gemm_k_slices(n, k);
     const int spg = group_size / 32;
-    // up to 16 activation rows whose x fits in LDS: x staged once per
-    // workgroup, weight tiles streamed without barriers (the same bits)
-    const int64_t small_lds = qg::gemm_small_lds(k, m);
-    if (m <= 16 && small_lds <= 128 * 1024) {
-        const int cus = device_cus();
-        if (cus < 1) return QG_ERR_DEVICE;
-        // one workgroup per CU (x fills most of its LDS), with as many waves
-        // as the 16-row tiles need to cover the chip, 1..8
-        const int64_t rtiles = (n + 15) / 16;
-        int64_t wpb = (rtiles + cus - 1) / cus;
-        wpb = wpb < 1 ? 1 : (wpb > qg::kGemmSmallWaves ? qg::kGemmSmallWaves : wpb);
-        int64_t blocks = (rtiles + wpb - 1) / wpb;
-        if (blocks > cus) blocks = cus;
-        const dim3 sgrid{unsigned(blocks)}, sblock{unsigned(64 * wpb)};
-        // a chunk's group scales as one vector load when they are aligned
-        const int gpc = 8 / spg;
-        const bool vs = p.groups % gpc == 0 && aligned_to(scales, uintptr_t(2 * gpc));
-#define QG_GEMM_SMALL(S, K, V)                                                                          \
-        if (spg == S && ks == K && vs == V) {                                                           \
-            static std::once_flag once;                                                                 \
-            static hipError_t attr = hipSuccess;                                                        \
-            std::call_once(once, [] {                                                                   \
-                attr = hipFuncSetAttribute(reinterpret_cast<const void *>(qg::qgemm_fp4_small_kernel<S, K, V>), \
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);      \
-            });                                                                                         \
-            if (attr != hipSuccess) return QG_ERR_LAUNCH;                                               \
-            return qgl::launch_kernel(qg::qgemm_fp4_small_kernel<S, K, V>, sgrid, sblock, size_t(small_lds), \
-                                      stream, p);                                                       \
-        }
-#define QG_GEMM_SMALL_V(S, K) QG_GEMM_SMALL(S, K, true) QG_GEMM_SMALL(S, K, false)
-        QG_GEMM_SMALL_V(1, 1) QG_GEMM_SMALL_V(1, 2) QG_GEMM_SMALL_V(1, 4)
-        QG_GEMM_SMALL_V(2, 1) QG_GEMM_SMALL_V(2, 2) QG_GEMM_SMALL_V(2, 4)
-        QG_GEMM_SMALL_V(4, 1) QG_GEMM_SMALL_V(4, 2) QG_GEMM_SMALL_V(4, 4)
-#undef QG_GEMM_SMALL_V
-#undef QG_GEMM_SMALL
-        return QG_ERR_LAUNCH;     // not reached
-    }
+    if (gemm_small_fits(k, m)) return gemm_small<false>(p, spg, ks, stream);
     return gemm_general<false>(p, spg, ks, stream);
 }
 
@@ -166,7 +173,10 @@ qg_status qgemm_affine_u4(const uint32_t *codes, const uint16_t *scales, const u
     if (!aligned_to(biases, 2)) return QG_ERR_MISALIGNED;
     qg::GemmParams p = gemm_params(codes, scales, x, y, n, k, group_size, m, out_dtype);
     p.biases = biases;
-    return gemm_general<true>(p, group_size / 32, gemm_k_slices(n, k), stream);
+    const int ks = gemm_k_slices(n, k);
+    const int spg = group_size / 32;
+    if (gemm_small_fits(k, m)) return gemm_small<true>(p, spg, ks, stream);
+    return gemm_general<true>(p, spg, ks, stream);
 }
 
 }  // extern "C"

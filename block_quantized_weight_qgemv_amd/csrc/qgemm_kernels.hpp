@@ -406,12 +406,19 @@ __host__ __device__ constexpr int64_t gemm_general_lds(int tb, int ks, int wps, 
 // order, and the slices are added in slice order at the end.  The MFMA
 // operands of a group are the same values in both kernels.  So a row's bits
 // are the same whichever kernel, m or launch computes it.
+//
+// kAffine: the affine 4-bit codes, as in qgemm_fp4_kernel: x staged in the
+// decode's column order, the codes decoded to q * 2^-9, a second MFMA chain
+// per group with B = 1 giving each activation row's group sum, and the fold
+// y += (512 s) * raw + b * X in group order.
 constexpr int kGemmSmallWaves = 8;                 // most waves per workgroup
-constexpr int kGemmSmallDepth = 4;                 // chunks in flight per lane (8 measured slower)
+// chunks in flight per lane (8 measured slower, with eight waves per CU and
+// with two or four)
+constexpr int kGemmSmallDepth = 4;
 
 // VS: a chunk's gpc group scales of a row are read as one vector (they are
 // aligned to 2 * gpc bytes when the groups per row are a multiple of gpc).
-template <int SPG, int KS, bool VS>
+template <int SPG, int KS, bool VS, bool kAffine = false>
 __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(const GemmParams p) {
     constexpr int gpc = kGemmKC / 32 / SPG;        // scale groups per chunk
     constexpr int PD = kGemmSmallDepth;
@@ -439,6 +446,7 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
     struct Buf {
         uint4 w[2];                                // 16-byte pieces 4j + g of the chunk row
         uint32_t sc[gpc];                          // the lane's row's group scales (bf16 bits)
+        uint32_t bi[kAffine ? gpc : 1];            // affine: its group biases (bf16 bits)
     };
     typedef unsigned short u16x8_t __attribute__((ext_vector_type(8)));
     typedef unsigned short u16x4_t __attribute__((ext_vector_type(4)));
@@ -458,27 +466,32 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             bf.w[j] = *reinterpret_cast<const uint4 *>(wrow + min(kb + 16 * (4 * j + g), row_bytes - 16));
-        const uint16_t *srow = p.scales + row * p.groups;
-        if constexpr (VS) {
-            // the chunk's groups, or the row's last gpc groups past the end
-            const int g0 = min(c * gpc, p.groups - gpc);
-            if constexpr (gpc == 8) {
-                const u16x8_t v = *reinterpret_cast<const u16x8_t *>(srow + g0);
+        // the chunk's group parameters of the row (as one vector with VS: the
+        // row's last gpc groups past the end)
+        auto params = [&](const uint16_t *arr, uint32_t (&out)[gpc]) __attribute__((always_inline)) {
+            const uint16_t *srow = arr + row * p.groups;
+            if constexpr (VS) {
+                const int g0 = min(c * gpc, p.groups - gpc);
+                if constexpr (gpc == 8) {
+                    const u16x8_t v = *reinterpret_cast<const u16x8_t *>(srow + g0);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) bf.sc[j] = v[j];
-            } else if constexpr (gpc == 4) {
-                const u16x4_t v = *reinterpret_cast<const u16x4_t *>(srow + g0);
+                    for (int j = 0; j < 8; ++j) out[j] = v[j];
+                } else if constexpr (gpc == 4) {
+                    const u16x4_t v = *reinterpret_cast<const u16x4_t *>(srow + g0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bf.sc[j] = v[j];
+                    for (int j = 0; j < 4; ++j) out[j] = v[j];
+                } else {
+                    const u16x2_t v = *reinterpret_cast<const u16x2_t *>(srow + g0);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) out[j] = v[j];
+                }
             } else {
-                const u16x2_t v = *reinterpret_cast<const u16x2_t *>(srow + g0);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) bf.sc[j] = v[j];
+                for (int j = 0; j < gpc; ++j) out[j] = srow[min(c * gpc + j, p.groups - 1)];
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < gpc; ++j) bf.sc[j] = srow[min(c * gpc + j, p.groups - 1)];
-        }
+        };
+        params(p.scales, bf.sc);
+        if constexpr (kAffine) params(p.biases, bf.bi);
     };
 
     f32x4_t acc[KS];
@@ -501,31 +514,57 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
         // kernel's (whose scale there is the last group's)
         // every group's chain first, then the folds in group order
         f32x4_t dd[gpc];
+        f32x4_t xg[kAffine ? gpc : 1];             // affine: each activation row's group sums
 #pragma unroll
         for (int j = 0; j < gpc; ++j) {
             f32x4_t d0 = {0.0f, 0.0f, 0.0f, 0.0f};
+            f32x4_t o0 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < SPG; ++t) {
                 const int s = j * SPG + t;
                 const bf16x8_t xa = *reinterpret_cast<const bf16x8_t *>(xrow + c * kGemmKC + 32 * s);
                 const uint32_t q = wst[s];
-                const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
-                const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
-                const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
-                const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                bf16x2_t p0, p1, p2, p3;
+                if constexpr (kAffine) {
+                    const uint32_t lo = q & 0x0F0F0F0Fu, hi = (q >> 4) & 0x0F0F0F0Fu;
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+                    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+                    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+                } else {
+                    p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 0);
+                    p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 1);
+                    p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 2);
+                    p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, 1.0f, 3);
+                }
                 const bf16x8_t wb = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
                                                             __builtin_shufflevector(p2, p3, 0, 1, 2, 3),
                                                             0, 1, 2, 3, 4, 5, 6, 7);
                 d0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, wb, d0, 0, 0, 0);
+                if constexpr (kAffine) {
+                    const bf16x8_t ones = {__bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f),
+                                           __bf16(1.0f), __bf16(1.0f), __bf16(1.0f), __bf16(1.0f)};
+                    o0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, ones, o0, 0, 0, 0);
+                }
             }
             dd[j] = d0;
+            if constexpr (kAffine) xg[j] = o0;
         }
         auto fold = [&](f32x4_t &a) __attribute__((always_inline)) {
 #pragma unroll
             for (int j = 0; j < gpc; ++j) {
                 const float sv = bf16_to_f32(bf.sc[j] & 0xFFFFu);
+                if constexpr (kAffine) {
+                    const float bv = bf16_to_f32(bf.bi[j] & 0xFFFFu);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) a[v] = fmaf(sv, dd[j][v], a[v]);
+                    for (int v = 0; v < 4; ++v) {
+                        a[v] = fmaf(sv * 512.0f, dd[j][v], a[v]);
+                        a[v] = fmaf(bv, xg[j][v], a[v]);
+                    }
+                } else {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) a[v] = fmaf(sv, dd[j][v], a[v]);
+                }
             }
         };
         if constexpr (KS == 1) {
@@ -593,7 +632,13 @@ __global__ void __launch_bounds__(64 * kGemmSmallWaves) qgemm_fp4_small_kernel(c
             const int u = u0 + i * int(blockDim.x);
             if (u < units) {
                 const int t = u / upr, ku = (u - t * upr) * 8;
-                *reinterpret_cast<uint4 *>(xs + t * xstride + ku) = ku < p.k ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+                uint4 vv = ku < p.k ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+                if constexpr (kAffine) {
+                    uint4 pc[1];
+                    FmtAffineU4::unit_pieces(vv, pc);
+                    vv = pc[0];
+                }
+                *reinterpret_cast<uint4 *>(xs + t * xstride + ku) = vv;
             }
         }
     }

@@ -6,8 +6,8 @@ matvec of every activation row (oracle.gemv.gemv_affine, bits = 4).
 Beyond parity (tests/parity.py's bar):
 * each activation row's output is bitwise what that row alone gives (m = 1)
   and what any other m gives, across the activation-row blocks of 16, 32 and
-  64 per workgroup and the one-wave K slices; repeated launches are bitwise
-  identical;
+  64 per workgroup, the one-wave K slices and the streaming kernel that takes
+  up to 16 rows with x in LDS; repeated launches are bitwise identical;
 * bf16 output is the RNE of the f32 output;
 * nothing outside y[m, n] is written;
 * the bias term alone (zero scales) and the scale term alone (zero biases)
@@ -53,6 +53,9 @@ CASES = [
     (1, 64, 64, 5), (64, 256, 32, 16), (100, 3840, 64, 16), (1000, 4224, 64, 17), (130, 128, 32, 33),
     (77, 15360, 128, 64), (200, 3840, 64, 65), (33, 512, 64, 100), (300, 4096, 128, 8), (64, 2048, 32, 130),
     (9000, 512, 64, 20), (9000, 768, 128, 40), (33000, 256, 64, 40), (33000, 512, 32, 70),
+    # up to 16 rows with x in LDS (the streaming kernel): group parameters
+    # loaded one by one (66 groups, not a multiple of 4), long rows
+    (1000, 4224, 64, 9), (50, 15360, 32, 6), (4100, 3840, 128, 16),
 ]
 
 
