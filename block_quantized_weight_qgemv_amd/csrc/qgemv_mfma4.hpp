@@ -138,6 +138,10 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
     };
     const uint32_t row_bytes = uint32_t(p.row_bytes);
     const int sgroups = p.groups >> 3;
+    // The group parameters are read with the default cache policy: a step's
+    // 2-byte loads of a row touch part of a 128-byte line whose rest the next
+    // step reads, and non-temporal loads let it be fetched again.
+    constexpr int kParamCache = 0;
     auto issue = [&](Buf &bf, int item_in) __attribute__((always_inline)) {
         const int item = __builtin_amdgcn_readfirstlane(item_in);
         int64_t row0;
@@ -156,13 +160,13 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
             bf.c[q] = buffer_code_chunk(rc, in ? uint32_t(ri) * row_bytes + uint32_t(c) * kChunkBytes : kOutOfRange);
             const int grp = c >> p.group_shift;
             bf.a0[q] = __builtin_amdgcn_raw_buffer_load_b16(
-                rs, int(in ? uint32_t(ri * p.groups + grp) * 2 : kOutOfRange), 0, kCacheNonTemporal);
+                rs, int(in ? uint32_t(ri * p.groups + grp) * 2 : kOutOfRange), 0, kParamCache);
             if constexpr (Fmt::kSuper)
                 bf.a1[q] = __builtin_amdgcn_raw_buffer_load_b32(
-                    rbias, int(in ? uint32_t(ri * sgroups + (grp >> 3)) * 4 : kOutOfRange), 0, kCacheNonTemporal);
+                    rbias, int(in ? uint32_t(ri * sgroups + (grp >> 3)) * 4 : kOutOfRange), 0, kParamCache);
             else if constexpr (Fmt::kAuxArrays >= 2)
                 bf.a1[q] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rbias, int(in ? uint32_t(ri * p.groups + grp) * 2 : kOutOfRange), 0, kCacheNonTemporal);
+                    rbias, int(in ? uint32_t(ri * p.groups + grp) * 2 : kOutOfRange), 0, kParamCache);
             else
                 bf.a1[q] = 0;
         }
