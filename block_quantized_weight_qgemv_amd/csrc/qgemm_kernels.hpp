@@ -1,6 +1,8 @@
 // Block-quantized weight GEMM for more than four activation rows (a short
 // prefill or a speculative-decoding batch): Y[m, n] = X[m, k] . W[n, k]^T with
-// W as FP4-E2M1 codes and bf16 group scales, the layout the matvec reads.
+// W as FP4-E2M1 codes and bf16 group scales, or as min-max affine 4-bit codes
+// with bf16 group scales and biases (kAffine), in the layouts the matvec
+// reads.
 //
 // The weights are decoded in registers and fed to bf16 MFMA; nothing is
 // written back to memory, so each weight byte is read from HBM once per 64

@@ -353,8 +353,10 @@ qg_status qgemm_fp4_e2m1(const uint8_t *codes, const uint16_t *scales, const uin
  *   scales, biases  bf16 [n, k/group_size] (DEVICE), 2-byte aligned
  *   x, y, n, k, group_size, m: as for qgemm_fp4_e2m1, with the same errors
  *   (a null biases pointer: QG_ERR_NULL_POINTER)
- * Every m takes the kernel that stages x chunk by chunk.  No device memory
- * is allocated; asynchronous on `stream`. */
+ * As for qgemm_fp4_e2m1, up to 16 rows whose x fits in LDS take the kernel
+ * that stages x once and streams the weight tiles, more rows the one that
+ * stages x chunk by chunk, with the same order of additions.  No device
+ * memory is allocated; asynchronous on `stream`. */
 qg_status qgemm_affine_u4(const uint32_t *codes, const uint16_t *scales, const uint16_t *biases, const uint16_t *x,
                           void *y, int64_t n, int64_t k, int32_t group_size, int32_t m, qg_out_dtype out_dtype,
                           hipStream_t stream);
