@@ -334,6 +334,11 @@ SWEEP = [
     ("u8q8", "mlp_up", 1, 64), ("u8q8", "mlp_down", 1, 64), ("u8q8", "mlp_up", 4, 64), ("u8q8", "mlp_down", 4, 64),
     ("u8q8f", "mlp_up", 1, 64), ("u8q8f", "mlp_down", 1, 64), ("u8q8f", "mlp_up", 4, 64),
     ("u8q8f", "mlp_down", 4, 64),
+    # one GPU's share of the Gemma shapes and the lm_head at tensor-parallel
+    # degree 8 (rows split for gate_up, qkv and the lm_head; K for o_proj and
+    # fc_down)
+    ("fp4", "gate_up_tp8", 1, 32), ("fp4", "qkv_tp8", 1, 32), ("fp4", "o_proj_tp8", 1, 32),
+    ("fp4", "fc_down_tp8", 1, 32), ("fp8", "lm_head_tp8", 1, None),
 ]
 
 

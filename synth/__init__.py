@@ -40,6 +40,13 @@ SHAPES = {
     "llama_up":      (7, 14336, 4096),     # Llama-3.1-8B gate/up
     "llama_down":    (8, 4096, 14336),
     "lm_head":       (9, 262144, 3840),    # 262K vocab x hidden 3840
+    # one GPU's share at tensor-parallel degree 8: column-parallel layers
+    # split their rows, row-parallel layers (o_proj, fc_down) their K
+    "gate_up_tp8":   (10, 3840, 3840),
+    "qkv_tp8":       (11, 1024, 3840),
+    "o_proj_tp8":    (12, 3840, 512),
+    "fc_down_tp8":   (13, 3840, 1920),
+    "lm_head_tp8":   (14, 32768, 3840),
 }
 
 

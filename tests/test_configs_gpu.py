@@ -16,6 +16,8 @@ Workloads (weights ~ N(0, 0.02), x ~ N(0, 1) in bf16, batch 1 unless noted):
   affine g64 4/8-bit: 15360x3840, 3840x15360, 14336x4096, 4096x14336
   FP8-E4M3 row scale: lm_head 262144x3840, batch 1 and 4
   batch 4 of FP4 gate_up / fc_down and u4 15360x3840 / 3840x15360
+  one GPU's share at tensor-parallel degree 8: FP4 3840x3840, 1024x3840,
+                3840x512, 3840x1920; FP8 32768x3840
 """
 
 import os
@@ -143,6 +145,16 @@ def test_batch4_matrix_blocks(fmt, name, gs):
     """Batch 4 of the 4-bit formats (the 4x4x4 matrix-block kernel), every
     row of the full-size matrix against the oracle."""
     _full_size(fmt, name, batch=4, gs=gs)
+
+
+@pytest.mark.parametrize("fmt,name,gs", [("fp4", "gate_up_tp8", 32), ("fp4", "qkv_tp8", 32),
+                                         ("fp4", "o_proj_tp8", 32), ("fp4", "fc_down_tp8", 32),
+                                         ("fp8", "lm_head_tp8", None)])
+def test_tensor_parallel_shards(fmt, name, gs):
+    """One GPU's share of the Gemma shapes and the lm_head at tensor-parallel
+    degree 8 (the shapes the sharded layers hand each GPU), every row against
+    the oracle."""
+    _full_size(fmt, name, gs=gs)
 
 
 @pytest.mark.parametrize("batch", [1, 4])
