@@ -30,6 +30,10 @@ HIP_FLAGS = [
     # put the GEMM's in accumulation registers and read every result back
     # with one v_accvgpr_read per element (a quarter of the GEMM's VALU work)
     "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the only atomics are one lane's LDS tile-counter increments: the
+    # compiler's wave-scan rewrite of them (exec popcounts and lane offsets)
+    # is work for nothing
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I" + INCLUDE, "-I" + CSRC,
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-ffp-contract=off",
