@@ -256,14 +256,12 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
             issue(buf[0], tl[0]);
             wait_vm_loads<kTileLoads>();
         });
-        // the rest of the prefetch goes out now (the barrier in block_rms has
-        // made the tile counters visible), so the weight stream runs while x
-        // is normalized in LDS in place, the work spread over the workgroup
-#pragma unroll
-        for (int d = 1; d < D; ++d) {
-            tl[d] = next_issue();
-            issue(buf[d], tl[d]);
-        }
+        // x is normalized in LDS in place, the work spread over the
+        // workgroup, and read into registers; the rest of the prefetch goes
+        // out behind that (the barrier in block_rms has made the tile
+        // counters visible).  Issued ahead of the normalization instead, the
+        // other waves' loads hold up the barrier below: about 0.4 us more per
+        // launch, measured.
         for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
             const int b = row_of<B>(u, upr);
             xlds[u] = norm_unit(xlds[u], glds[u - b * upr], pick_uniform(rn, b));
@@ -278,6 +276,11 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
 #pragma unroll
                 for (int u = 0; u < Fmt::kRawUnits; ++u) xraw[b][j][u] = xlds[u0 + u];
             }
+#pragma unroll
+        for (int d = 1; d < D; ++d) {
+            tl[d] = next_issue();
+            issue(buf[d], tl[d]);
+        }
     } else {
         // one issue ahead of both ways (a copy in each costs the plain
         // instances code and speed)
