@@ -301,9 +301,10 @@ int64_t mfma4_lds(qg_format f, const Params &p, int32_t batch) {
 
 // (the fused norm's sums are counted for the plain call too, as for FP8, and
 // 1 KiB is kept for the split-K partials of at least one tile).  This kernel
-// runs one workgroup per CU, so it may take all of gfx950's 160 KiB of LDS.
+// runs one workgroup per CU, so it may take all of gfx950's 160 KiB of LDS
+// (qgl::kM4MaxLds).
 constexpr int64_t kM4PartReserve = 1024;
-constexpr int64_t kM4MaxLds = 160 * 1024;
+using qgl::kM4MaxLds;
 
 bool mfma4_takes(qg_format f, const Params &p) {
     const int64_t norm_bytes = int64_t(4) * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4;
@@ -348,7 +349,17 @@ qg_status run_mfma4(qg_format f, Params p, int32_t batch, const qg_plan *overrid
     }
     p.part_offset = int32_t(base);
     p.norm_offset = int32_t(base + part_bytes);
-    const int64_t lds = base + part_bytes + norm_bytes;
+    int64_t lds = base + part_bytes + norm_bytes;
+    // fused norm: gamma in LDS too where it fits (bitwise the same as reading
+    // it from memory; only the norm's prologue gets shorter)
+    p.gamma_offset = 0;
+    if (p.norm) {
+        const int64_t g_off = (lds + 15) / 16 * 16;
+        if (g_off + int64_t(p.k) * 2 <= kM4MaxLds) {
+            p.gamma_offset = int32_t(g_off);
+            lds = g_off + int64_t(p.k) * 2;
+        }
+    }
     p.total_waves = pl.blocks * pl.waves_per_block;
     switch (f) {
         case QG_FMT_FP4_E2M1: return qgl::launch_fp4(p, pl, batch, lds, stream);

@@ -49,7 +49,7 @@ struct Params {
     float eps;                      // fused RMSNorm epsilon
     int32_t norm;                   // 1: x is RMS-normalized inside the kernel
     int32_t norm_offset;            // LDS byte offset of the norm's group sums
-    int32_t gamma_offset;           // row kernel: LDS byte offset of gamma (fused norm)
+    int32_t gamma_offset;           // LDS byte offset of gamma (fused norm; matrix blocks: 0 = not in LDS)
     int32_t x_global;               // LDS kernel: x too large for LDS, read from memory with the weights
 };
 
@@ -302,7 +302,10 @@ __device__ __forceinline__ int row_of(int i, int per) {
 // x[b] and k alone: not on the launch shape, the kernel or the batch size.
 // Only the workgroup's first four waves load (four groups per wave at a time):
 // the waves dispatched after them would find their loads queued behind the
-// weight stream of the whole chip.  `between` is called once by every wave,
+// weight stream of the whole chip.  Where four waves would need more than one
+// round of loads (more than 16 groups: k above 8192 at batch 1, batch 3-4 at
+// k = 3840), the first eight load, so that fewer rounds of memory latency
+// come before the first barrier.  `between` is called once by every wave,
 // by the loading waves right after their first loads are issued (the caller
 // can send its own loads behind them and wait for these alone).  With xdst
 // (and gdst) given, the raw units of x (and of gamma, [k/8]) are copied to LDS
@@ -316,12 +319,13 @@ __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&
                                           Between &&between, XIndex xidx = XIndex{}) {
     using Red = WaveSum<4>;
     const int lane = threadIdx.x & (kWave - 1);
-    const int W = min(int(blockDim.x >> 6), kStageThreads / kWave);    // loading waves
-    const int w = wave_in_block();
-    const bool loader = w < W;                     // uniform
     const int upr = p.k / 8;                       // 16-byte units per row
     const int gpr = (upr + kWave - 1) / kWave;     // groups per row
     const int ng = B * gpr;
+    constexpr int W4 = kStageThreads / kWave;
+    const int W = min(int(blockDim.x >> 6), ng > 4 * W4 ? 2 * W4 : W4);    // loading waves
+    const int w = wave_in_block();
+    const bool loader = w < W;                     // uniform
     uint4 v[4], gv[4];
     int uu[4], bb[4];
     auto load_round = [&](int g0) {

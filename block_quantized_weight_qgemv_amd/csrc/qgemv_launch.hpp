@@ -19,6 +19,9 @@ using qg::Params;
 // has 160 KiB of LDS per compute unit; 128 KiB leaves room for a second,
 // smaller workgroup.
 constexpr int64_t kMaxLds = 128 * 1024;
+// The matrix-block kernel runs one workgroup per compute unit and may take
+// all of it.
+constexpr int64_t kM4MaxLds = 160 * 1024;
 
 struct Plan {
     int rows_per_tile;
@@ -31,15 +34,15 @@ struct Plan {
 
 
 // One function per kernel instance, so that each instance raises its own
-// LDS limit once.
-template <auto Kern>
+// LDS limit (kLimit) once.
+template <auto Kern, int64_t kLimit = kMaxLds>
 inline qg_status launch(const Params &p, const Plan &pl, int64_t lds, hipStream_t stream) {
     if (lds > 64 * 1024) {
         static std::once_flag attr_once;
         static hipError_t attr_err = hipSuccess;
         std::call_once(attr_once, [&] {
             attr_err = hipFuncSetAttribute(reinterpret_cast<const void *>(Kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(kLimit));
         });
         if (attr_err != hipSuccess) return QG_ERR_LAUNCH;
     }
@@ -113,8 +116,8 @@ qg_status launch_r(const Params &p, const Plan &pl, int32_t batch, int64_t lds, 
 // steps of kM4StepPasses passes, kM4Depth of them in flight per wave.
 template <class Fmt, bool kNorm>
 qg_status launch_mfma4_n(const Params &p, const Plan &pl, int32_t batch, int64_t lds, hipStream_t s) {
-    if (batch == 3) return launch<qg::qgemv_mfma4_kernel<Fmt, 3, kNorm>>(p, pl, lds, s);
-    return launch<qg::qgemv_mfma4_kernel<Fmt, 4, kNorm>>(p, pl, lds, s);
+    if (batch == 3) return launch<qg::qgemv_mfma4_kernel<Fmt, 3, kNorm>, kM4MaxLds>(p, pl, lds, s);
+    return launch<qg::qgemv_mfma4_kernel<Fmt, 4, kNorm>, kM4MaxLds>(p, pl, lds, s);
 }
 
 template <class Fmt>

@@ -216,17 +216,27 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
     Buf buf[D];
     if constexpr (kNorm) {
         float rn[B];
-        block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, nullptr, [&] {
+        // gamma is copied to LDS with the norm's loads where the host found
+        // room for it beside x, the partials and the sums
+        uint4 *glds = p.gamma_offset ? reinterpret_cast<uint4 *>(smem + p.gamma_offset) : nullptr;
+        block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds, [&] {
             issue(buf[0], i_begin);
             wait_vm_loads<kStepLoads>();
         }, xl);
-        // (each thread rewrites only the unit it read)
-        for (int base = 0; base < x_units; base += blockDim.x) {
-            const int u = min(base + int(threadIdx.x), x_units - 1);
-            const int b = row_of<B>(u, upr);
-            const uint4 v = norm_unit(xlds[xpos(u)], load_x_unit(p.gamma + int64_t(u - b * upr) * 8),
-                                      pick_uniform(rn, b));
-            put_unit(base + int(threadIdx.x), v);
+        // One gamma unit per thread and pass, applied to that unit of every
+        // batch row (each thread rewrites only the units it read; lanes past
+        // the row's end compute on its last unit and store nothing).  Gamma
+        // read from memory here, one dependent load per unit of x, cost the
+        // batch-4 fused call ~2.5 us at k = 3840 and ~10 us at k = 15360.
+        for (int base = 0; base < upr; base += blockDim.x) {
+            const int gu_in = base + int(threadIdx.x);
+            const int gu = min(gu_in, upr - 1);
+            const uint4 gv = glds ? glds[gu] : load_x_unit(p.gamma + int64_t(gu) * 8);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const int u = b * upr + gu;
+                put_unit(gu_in < upr ? u : x_units, norm_unit(xlds[xpos(u)], gv, rn[b]));
+            }
         }
     } else {
         // The first step's loads go out right behind the activations', and

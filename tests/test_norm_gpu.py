@@ -116,6 +116,8 @@ CASES = [
     ("u8", 120, 14336, 64, 1), ("fp8", 1500, 3840, None, 1), ("fp8", 600, 3840, None, 4),
     ("fp4", 90, 3872, 32, 2),          # the LDS kernel
     ("fp8", 333, 5120, None, 3),       # the matrix-core kernel, rows of several steps
+    ("fp4", 200, 15360, 32, 4),        # matrix blocks, gamma in LDS beside 120 KiB of x
+    ("u4", 260, 15360, 64, 4),         # matrix blocks, gamma read from memory (no room in LDS)
 ]
 
 
