@@ -156,6 +156,51 @@ def test_fused_norm_parity(fmt, n, k, gs, batch):
         parity.assert_parity(y, y_ref, a_ref, "%s fused norm n=%d k=%d" % (fmt, n, k))
 
 
+def _exact_tie_inputs(k, seed):
+    """x, gamma, eps for which every fp32 step of the norm is exact: x has four
+    significant bits (its squares and their sums stay far inside fp32's 24),
+    eps tops the mean square up to exactly 4, so r = 1/2; gamma has seven
+    significant bits, so x * r * gamma is exact in fp32 and many values sit
+    exactly on a bf16 rounding midpoint."""
+    rng = np.random.default_rng(seed)
+    xv = rng.choice([-1.0, 1.0], k) * (8 + rng.integers(0, 8, k)) / 8.0 * 2.0 ** rng.integers(-1, 1, k)
+    gv = (64 + rng.integers(0, 64, k)) / 64.0 * 2.0 ** rng.integers(-1, 1, k)
+    x = F.f64_to_bf16_bits(xv)[None, :]
+    gamma = F.f64_to_bf16_bits(gv)
+    assert np.array_equal(F.bf16_bits_to_f64(x[0]), xv) and np.array_equal(F.bf16_bits_to_f64(gamma), gv)
+    mean_sq = float(np.sum(xv * xv)) / k
+    eps = 4.0 - mean_sq
+    assert eps >= 0.0 and np.float32(eps) == eps
+    return x, gamma, float(eps)
+
+
+@pytest.mark.parametrize("k", [3840, 15360])
+def test_norm_rounds_exact_midpoints_to_even(k):
+    """With every fp32 step exact (r = 1/2 exactly, exact products), the GPU's
+    rounding to bf16 is the only rounding: the standalone and the fused norm
+    must give the oracle's round-to-nearest-even bits everywhere, including
+    the values that sit exactly on a midpoint (rounded both up and down)."""
+    x, gamma, eps = _exact_tie_inputs(k, 11 + k)
+    log("norm exact midpoints k=%d" % k)
+    v = N.rmsnorm_f64(x, gamma, eps)
+    ref = N.rmsnorm_bf16(x, gamma, eps)
+    rv = F.bf16_bits_to_f64(ref)
+    # midpoints: the exact value is half way between its bf16 neighbours
+    up = (ref.astype(np.int32) + 1).astype(np.uint16)
+    dn = (ref.astype(np.int32) - 1).astype(np.uint16)
+    on_mid = (np.abs(v - (rv + F.bf16_bits_to_f64(up)) / 2) == 0) | (np.abs(v - (rv + F.bf16_bits_to_f64(dn)) / 2) == 0)
+    rounded_up = on_mid & (np.abs(rv) > np.abs(v))
+    rounded_dn = on_mid & (np.abs(rv) < np.abs(v))
+    assert rounded_up.sum() > 50 and rounded_dn.sum() > 50, (rounded_up.sum(), rounded_dn.sum())
+    got = host_bits(q.qg_rmsnorm_bf16(dev(x), dev(gamma), eps))
+    assert np.array_equal(got, ref), "%d of %d values differ" % (int(np.sum(got != ref)), k)
+    # the fused call on these inputs equals the plain call on them
+    n, gs = 96, 32
+    arrays = Q.quantize_fp4_e2m1(synth.weights(41, n, k), gs)
+    y = run_norm("fp4", arrays, x, gamma, eps, n, gs)
+    assert np.array_equal(y, run("fp4", arrays, got, n, gs=gs))
+
+
 @pytest.mark.parametrize("k", [8, 3840, 8200, 16384, 20480])
 def test_standalone_norm_kept_and_reread_rows(k):
     """Rows whose x and gamma fit in LDS beside the sums (k up to 16352) are
