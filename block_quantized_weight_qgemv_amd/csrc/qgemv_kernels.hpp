@@ -500,8 +500,7 @@ __global__ void __launch_bounds__(512) qgemv_row_kernel(const Params p) {
         for (int64_t idx = threadIdx.x; idx < b_rows * B; idx += blockDim.x) {
             const int64_t r = idx / B;
             const int b = int(idx - r * B);
-            float sum = part[(r * S) * B + b];
-            for (int sg = 1; sg < S; ++sg) sum += part[(r * S + sg) * B + b];
+            float sum = sum_in_order(part + (r * S) * B + b, S, B);
             const int64_t row = b_begin + r;
             if constexpr (Fmt::kRowScale) sum *= p.row_scale[row];
             store_y(p, b, row, sum);

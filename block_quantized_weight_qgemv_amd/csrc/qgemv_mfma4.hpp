@@ -427,8 +427,7 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
         const int rows = int(min(int64_t(T) * kM4Rows, p.n - t_begin * kM4Rows));
         for (int idx = threadIdx.x; idx < rows * B; idx += blockDim.x) {
             const int r = idx / B, b = idx - r * B;
-            float sum = part[(r * G) * B + b];
-            for (int gg = 1; gg < G; ++gg) sum += part[(r * G + gg) * B + b];
+            const float sum = sum_in_order(part + (r * G) * B + b, G, B);
             store_y(p, b, t_begin * kM4Rows + r, sum);
         }
     }
