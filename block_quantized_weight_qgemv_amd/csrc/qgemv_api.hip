@@ -350,8 +350,8 @@ qg_status run_mfma4(qg_format f, Params p, int32_t batch, const qg_plan *overrid
     p.part_offset = int32_t(base);
     p.norm_offset = int32_t(base + part_bytes);
     int64_t lds = base + part_bytes + norm_bytes;
-    // fused norm: gamma in LDS too where it fits (bitwise the same as reading
-    // it from memory; only the norm's prologue gets shorter)
+    // fused norm: gamma in LDS too where it fits (the same bits as reading it
+    // from memory)
     p.gamma_offset = 0;
     if (p.norm) {
         const int64_t g_off = (lds + 15) / 16 * 16;

@@ -225,9 +225,9 @@ __global__ void __launch_bounds__(512) qgemv_mfma4_kernel(const Params p) {
         }, xl);
         // One gamma unit per thread and pass, applied to that unit of every
         // batch row (each thread rewrites only the units it read; lanes past
-        // the row's end compute on its last unit and store nothing).  Gamma
-        // read from memory here, one dependent load per unit of x, cost the
-        // batch-4 fused call ~2.5 us at k = 3840 and ~10 us at k = 15360.
+        // the row's end compute on its last unit and store nothing): one
+        // gamma read per unit of a row, from LDS where it fits, instead of
+        // one load from memory per unit of x.
         for (int base = 0; base < upr; base += blockDim.x) {
             const int gu_in = base + int(threadIdx.x);
             const int gu = min(gu_in, upr - 1);
