@@ -328,7 +328,11 @@ __device__ __forceinline__ float sum_in_order(const float *src, int n, int strid
 // b's 16-byte units are cut into groups of 64 consecutive units; a wave sums a
 // group's squares over its lanes (WaveSum, whose tree does not depend on how
 // many groups it carries) and keeps the sum in LDS (gsum); after a barrier
-// every thread adds a row's group sums in group order.  So r[b] depends on
+// every wave adds a row's group sums 64 at a time with the same tree (lane l
+// holding group 64c + l) and those totals in order, taking lane 0's value, so
+// all threads hold the same r.  (Added one by one in group order, the LDS
+// reads of the chain cost the standalone norm at k = 15360 ~0.4 us and the
+// batch-4 fused call ~1.3 us.)  So r[b] depends on
 // x[b] and k alone: not on the launch shape, the kernel or the batch size.
 // Only the workgroup's first four waves load (four groups per wave at a time):
 // the waves dispatched after them would find their loads queued behind the
@@ -397,7 +401,12 @@ __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         float t = 0.0f;
-        for (int g = 0; g < gpr; ++g) t += gsum[b * gpr + g];
+        for (int g0 = 0; g0 < gpr; g0 += kWave) {
+            const float gl = gsum[b * gpr + min(g0 + lane, gpr - 1)];
+            float v[1] = {g0 + lane < gpr ? gl : 0.0f};
+            WaveSum<1>::run(v);
+            t += __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v[0])));
+        }
         r[b] = 1.0f / sqrtf(t / float(p.k) + p.eps);
     }
 }
