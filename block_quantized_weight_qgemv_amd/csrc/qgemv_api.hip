@@ -278,12 +278,19 @@ qg_status run_fp8(Params p, int32_t batch, const qg_plan *override_plan, hipStre
     return qgl::launch_fp8(p, pl, batch, lds, stream);
 }
 
+// LDS bytes of x in the fused norm's row kernel: with a 16-byte pad after
+// every 64-byte chunk for the formats whose chunks hold 32 activations
+int64_t norm_x_bytes(qg_format f, int64_t k, int32_t batch) {
+    const int64_t bytes = int64_t(batch) * k * 2;
+    return fmt_info(f).wpc == 32 ? bytes / 4 * 5 : bytes;
+}
+
 // Whether the fused norm's row kernel fits its LDS (x, gamma, the tile
 // counters, one row's split-K partials, the norm's group sums).
-bool norm_row_fits(const Params &p, int32_t batch) {
+bool norm_row_fits(qg_format f, const Params &p, int32_t batch) {
     const int64_t b = batch;
     const int64_t norm_bytes = b * ((p.k / 8 + qg::kWave - 1) / qg::kWave) * 4;
-    return (b + 1) * p.k * 2 + kCounterBytes + int64_t(p.segs) * b * 4 + norm_bytes <= kMaxLds;
+    return norm_x_bytes(f, p.k, batch) + p.k * 2 + kCounterBytes + int64_t(p.segs) * b * 4 + norm_bytes <= kMaxLds;
 }
 
 // The 4-bit formats (FP4, affine u4, the two-level format) at three or four
@@ -406,7 +413,7 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
     // norm's sums) the LDS kernel takes the call: the same bound, but its own
     // order of additions, so such a call is not bitwise the plain call on
     // the separately normalized x.
-    if (p.norm && p.segs && !norm_row_fits(p, batch)) p.segs = 0;
+    if (p.norm && p.segs && !norm_row_fits(f, p, batch)) p.segs = 0;
     Plan pl = default_plan(f, p, batch, cus);
     auto apply_override = [&](Plan &q) {
         if (!override_plan) return;
@@ -442,7 +449,7 @@ qg_status run(qg_format f, Params p, int32_t batch, const qg_plan *override_plan
         // LDS: x (staged or normalized), gamma (fused norm), the per-segment
         // tile counters (x in LDS), the split-K partials, the norm's sums
         const bool via_lds = p.x_staged || p.norm;
-        const int64_t x_bytes = via_lds ? int64_t(batch) * p.k * 2 : 0;
+        const int64_t x_bytes = !via_lds ? 0 : (p.norm ? norm_x_bytes(f, p.k, batch) : int64_t(batch) * p.k * 2);
         const int64_t g_bytes = p.norm ? int64_t(p.k) * 2 : 0;
         p.gamma_offset = int32_t(x_bytes);
         p.counter_offset = int32_t(x_bytes + g_bytes);

@@ -347,6 +347,12 @@ __device__ __forceinline__ float sum_in_order(const float *src, int n, int strid
 struct PackedRows {
     __device__ int operator()(int b, int u, int upr) const { return b * upr + u; }
 };
+// The same with one 16-byte unit of padding after every 4 (a 64-byte chunk
+// of 32 activations): a wave's lanes reading their chunks (80 bytes apart)
+// then hit distinct banks, where 64 bytes apart every fourth lane shared them.
+struct PaddedChunks {
+    __device__ int operator()(int b, int u, int upr) const { const int i = b * upr + u; return i + (i >> 2); }
+};
 
 template <int B, class Between, class XIndex = PackedRows>
 __device__ __forceinline__ void block_rms(const Params &p, float *gsum, float (&r)[B], uint4 *xdst, uint4 *gdst,
