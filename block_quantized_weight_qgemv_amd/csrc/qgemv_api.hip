@@ -718,14 +718,16 @@ qg_status qg_rmsnorm_bf16(const uint16_t *x, const uint16_t *gamma, float eps, u
     const Norm nm{gamma, eps};
     qg_status st = set_norm(p, &nm);
     if (st != QG_OK) return st;
-    // one workgroup per batch row; x and gamma stay in LDS when they fit in
-    // 64 KiB with the group sums
+    // one workgroup of 8 waves per batch row (eight loading waves take up to
+    // k = 16384 in one round of loads: k = 15360 2.89 us against 3.72 with 4
+    // waves); x and gamma stay in LDS when they fit in 64 KiB with the group
+    // sums
     const int64_t sums = qg::rmsnorm_sums_bytes(k);
     if (sums > 64 * 1024) return QG_ERR_TOO_LARGE;      // k > 2^23
     if (sums + 4 * k <= 64 * 1024)
-        return qgl::launch_kernel(qg::qg_rmsnorm_kernel<true>, dim3(batch), dim3(256), size_t(sums + 4 * k), stream,
+        return qgl::launch_kernel(qg::qg_rmsnorm_kernel<true>, dim3(batch), dim3(512), size_t(sums + 4 * k), stream,
                                   p, out);
-    return qgl::launch_kernel(qg::qg_rmsnorm_kernel<false>, dim3(batch), dim3(256), size_t(sums), stream, p, out);
+    return qgl::launch_kernel(qg::qg_rmsnorm_kernel<false>, dim3(batch), dim3(512), size_t(sums), stream, p, out);
 }
 
 qg_status qg_plan_query(qg_format format, int64_t n, int64_t k, int32_t batch, qg_plan *out) {

@@ -754,7 +754,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(const Params p) {
 inline constexpr int64_t rmsnorm_sums_bytes(int64_t k) { return ((k / 8 + kWave - 1) / kWave * 4 + 15) / 16 * 16; }
 
 template <bool kKeep>
-__global__ void __launch_bounds__(256) qg_rmsnorm_kernel(Params p, uint16_t *out) {
+__global__ void __launch_bounds__(512) qg_rmsnorm_kernel(Params p, uint16_t *out) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int upr = p.k / 8;
     p.x += int64_t(blockIdx.x) * p.k;
