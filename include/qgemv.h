@@ -264,7 +264,7 @@ const char *qg_status_string(qg_status status);
  * k, so the result is also bitwise the same for every plan and batch size.
  * x itself is not modified.  One exception to "exactly what the plain entry
  * point returns": where x and gamma do not fit in 128 KiB of LDS together
- * ((batch + 1) * k * 2 bytes for the 8-bit codes and FP8 at batch 1-2,
+ * ((batch + 1) * k * 2 bytes for the 8-bit codes, and for FP8 at batch 1-2;
  * (1.25 * batch + 1) * k * 2 for the 4-bit formats at batch 1-2, whose x is
  * kept padded; e.g. the 8-bit codes at batch 4 and k = 15360), the call runs a
  * kernel that stages x per step and adds the terms in another order; it
