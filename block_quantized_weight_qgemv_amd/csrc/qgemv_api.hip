@@ -274,6 +274,16 @@ qg_status run_fp8(Params p, int32_t batch, const qg_plan *override_plan, hipStre
     p.norm_offset = int32_t(lds);
     lds += norm_bytes;
     if (lds > kMaxLds) return QG_ERR_TOO_LARGE;
+    // fused norm: gamma in LDS too where it fits (the same bits as reading it
+    // from memory)
+    p.gamma_offset = 0;
+    if (p.norm) {
+        const int64_t g_off = (lds + 15) / 16 * 16;
+        if (g_off + int64_t(p.k) * 2 <= kMaxLds) {
+            p.gamma_offset = int32_t(g_off);
+            lds = g_off + int64_t(p.k) * 2;
+        }
+    }
     p.total_waves = pl.blocks * pl.waves_per_block;
     return qgl::launch_fp8(p, pl, batch, lds, stream);
 }

@@ -221,15 +221,27 @@ __global__ void __launch_bounds__(512) qgemv_fp8_mfma_kernel(const Params p) {
     if (shared && threadIdx.x == 0) *counter = unsigned(W);       // the next chunk to hand out
     if constexpr (kNorm) {
         float rn[B];
-        block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, nullptr, [&] {
+        // gamma is copied to LDS with the norm's loads where the host found
+        // room for it; the normalization then reads each gamma unit once and
+        // applies it to that unit of every batch row (with one load from
+        // memory per unit of x, each queued behind the first weight step, the
+        // batch-4 fused lm_head took 2.7 us more than the plain call; 2.2 now)
+        uint4 *glds = p.gamma_offset ? reinterpret_cast<uint4 *>(smem + p.gamma_offset) : nullptr;
+        block_rms<B>(p, reinterpret_cast<float *>(smem + p.norm_offset), rn, xlds, glds, [&] {
             issue(buf[0], sl[0], half_of(0));
             wait_vm_loads<kStepLoads>();
         }, xl);
-        for (int u = threadIdx.x; u < x_units; u += blockDim.x) {
-            const int b = row_of<B>(u, upr);
-            const int uu = u - b * upr;
-            const int i = xl(b, uu, upr);
-            xlds[i] = norm_unit(xlds[i], load_x_unit(p.gamma + int64_t(uu) * 8), pick_uniform(rn, b));
+        for (int base = 0; base < upr; base += blockDim.x) {
+            const int gu_in = base + int(threadIdx.x);
+            const int gu = min(gu_in, upr - 1);
+            const uint4 gv = glds ? glds[gu] : load_x_unit(p.gamma + int64_t(gu) * 8);
+            if (gu_in < upr) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int i = xl(b, gu, upr);
+                    xlds[i] = norm_unit(xlds[i], gv, rn[b]);
+                }
+            }
         }
     } else {
         constexpr int kXu = 4;
